@@ -1,0 +1,26 @@
+"""Shared test configuration: the ``gpu`` marker, import paths, and helpers
+that print the case being run before any GPU step (so a failing box still
+names it)."""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
+
+
+def announce(msg: str) -> None:
+    """Print and flush the identity of a GPU step before it runs."""
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture
+def say():
+    return announce
