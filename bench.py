@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Throughput of the SVDQuant W4A4 + low-rank path on one MI355X.
+
+One step is one pass of the whole runtime path over one batch of synthetic
+input already resident in HBM:
+    fc1  4608 x 3072 -> 12288, rank 32: quantise + low-rank down (kernel 1),
+         INT4 GEMM + low-rank up + bias + fused tanh-GELU (kernel 2)
+    fc2  4608 x 12288 -> 3072, rank 32: kernel 1, kernel 2
+    AWQ  W4A16 modulation projection 1 x 3072 -> 18432 (kernel 3)
+The offline steps (smoothing, SVD split, residual quantisation, AWQ
+quantisation) run once before timing, through the library's host code.
+
+value = 2 * (2 M N K) of the two W4A4 layers / step time, in TOPS.  Events
+recorded on the launch stream between kernels give each kernel's duration;
+the dominant kernel (the W4A4 GEMM) is reported against the int8 MFMA peak.
+Input and weight buffers rotate over several copies so the 256 MB
+Infinity Cache cannot hold a step's working set between uses.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 256 CU x 2.4 GHz x 8192 ops/clk
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "w4a4_rank_corrected_smooth_amd", "csrc", "device.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(sample_rows_fc1=3072, sample_rows_fc2=1536):
+    """The oracle as it stands, timed on the host cores over a bounded sample:
+    every token row of both layers, for a slice of each layer's output
+    channels (prepare untimed)."""
+    import numpy as np
+    import synth
+    from oracle import svdquant as O
+    from oracle import glue as OG
+    cores = len(os.sched_getaffinity(0))
+    fc1, W2, b2 = synth.mlp_cases()
+    M, K1, K2 = fc1.M, fc1.K, W2.shape[1]
+    ref1 = O.prepare(fc1.W[:sample_rows_fc1], fc1.calib_absmax(), fc1.bias[:sample_rows_fc1], 32)
+    rng = np.random.default_rng(12)
+    pre = synth.f32_to_bf16_bits(rng.standard_normal((M, K2), dtype=np.float32))
+    X2 = O.bf16_bits_of(OG.gelu_tanh_bf16(O.bf16_values(pre)))
+    ref2 = O.prepare(W2[:sample_rows_fc2], O.calibration_absmax(O.bf16_values(X2[:64])),
+                     b2[:sample_rows_fc2], 32)
+    t0 = time.perf_counter()
+    O.forward(ref1, fc1.X)
+    O.forward(ref2, X2)
+    t = time.perf_counter() - t0
+    ops = 2.0 * M * sample_rows_fc1 * K1 + 2.0 * M * sample_rows_fc2 * K2
+    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
+            "sample": (f"oracle forward (activation quantisation, low-rank down, float64 "
+                       f"group-scaled GEMM, low-rank up, bias) over all {M} tokens for "
+                       f"{sample_rows_fc1} of fc1's 12288 and {sample_rows_fc2} of fc2's 3072 "
+                       f"output channels; {t:.1f} s"),
+            "seconds": t}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sets", type=int, default=3, help="rotating copies of inputs and weights")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this library runs the layer on a single MI355X and "
+              f"has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    import w4a4_rank_corrected_smooth_amd as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    S.device_check()
+    R = max(1, args.sets)
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---------------------------------------------------------------- setup
+    log("generating the MLP pair (seed 2) and preparing fc1 on the host")
+    fc1, W2, b2 = synth.mlp_cases()
+    M, K1, N1 = fc1.M, fc1.K, fc1.N
+    K2, N2 = N1, K1
+    t0 = time.perf_counter()
+    hw1 = S.prepare_weights(fc1.W, fc1.calib_absmax(), fc1.bias, 32)
+    prep1 = time.perf_counter() - t0
+    L1 = [S.Linear(hw1, dev) for _ in range(R)]
+    X = [dev_bf16(fc1.X) for _ in range(R)]
+    ws1 = [L1[0].new_workspace(M) for _ in range(R)]
+    Y1 = [torch.empty((M, N1), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    log("calibrating fc2 on the device's own GELU(fc1) output")
+    S.linear_forward(L1[0], X[0], out=Y1[0], gelu=True, workspace=ws1[0])
+    torch.cuda.synchronize()
+    ax2 = S.calibration_absmax(Y1[0][:64].cpu().view(torch.int16).numpy().view(np.uint16))
+    t0 = time.perf_counter()
+    hw2 = S.prepare_weights(W2, ax2, b2, 32)
+    prep2 = time.perf_counter() - t0
+    L2 = [S.Linear(hw2, dev) for _ in range(R)]
+    ws2 = [L2[0].new_workspace(M) for _ in range(R)]
+    Y2 = [torch.empty((M, N2), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    log("AWQ modulation projection 18432 x 3072 (seed 4)")
+    a = synth.awq_case()
+    q, s, z = S.awq_quantize_weights(a.W)
+    A = [S.AwqLinear(q, s, z, dev) for _ in range(R)]
+    xm = [torch.from_numpy(np.ascontiguousarray(a.x[:1])).to(dev) for _ in range(R)]
+    ym = [torch.empty((1, a.N), dtype=torch.float16, device=dev) for _ in range(R)]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    NEV = 6
+
+    def step(i, ev=None):
+        k = i % R
+        if ev: ev[0].record(stream)
+        S.linear_quantize(L1[k], X[k], ws1[k])
+        if ev: ev[1].record(stream)
+        S.linear_gemm(L1[k], M, Y1[k], ws1[k], gelu=True)
+        if ev: ev[2].record(stream)
+        S.linear_quantize(L2[k], Y1[k], ws2[k])
+        if ev: ev[3].record(stream)
+        S.linear_gemm(L2[k], M, Y2[k], ws2[k])
+        if ev: ev[4].record(stream)
+        S.awq_forward(A[k], xm[k], out=ym[k])
+        if ev: ev[5].record(stream)
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(NEV)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = ["fc1_quantize", "fc1_gemm_gelu", "fc2_quantize", "fc2_gemm", "awq_m1"]
+    dur = {n: [] for n in names}
+    span = []
+    for ev in events:
+        for j, n in enumerate(names):
+            dur[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)   # us
+        span.append(ev[0].elapsed_time(ev[NEV - 1]) * 1e3)
+    avg = {n: float(np.mean(v)) for n, v in dur.items()}
+    ms_per_step = wall / args.steps * 1e3
+    ops_layer = 2.0 * M * N1 * K1            # = 2 * M * N2 * K2
+    value = 2 * ops_layer / (ms_per_step * 1e-3) / 1e12
+
+    k2_us = 0.5 * (avg["fc1_gemm_gelu"] + avg["fc2_gemm"])
+    achieved = ops_layer / (k2_us * 1e-6) / 1e12
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "k2_traffic.json")
+    if os.path.exists(tpath):
+        with open(tpath) as f:
+            tj = json.load(f)
+        if tj.get("source_hash") == source_hash():
+            traffic = tj.get("bytes_per_launch")
+    r = 32
+    k1_bytes_fc1 = M * K1 * 2 + K1 * 4 + K1 * r * 2 + M * K1 // 2 + M * (K1 // 64) * 4 + M * r * 4
+    k1_bytes_fc2 = M * K2 * 2 + K2 * 4 + K2 * r * 2 + M * K2 // 2 + M * (K2 // 64) * 4 + M * r * 4
+    awq_bytes = a.N * a.K // 2 + a.N * (a.K // 64) * 4 + a.K * 2 + a.N * 2
+    out = {
+        "metric": "W4A4+low-rank linear TOPS at Flux MLP shape; % of MI355X int8 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "flux_mlp_pair_4608x3072x12288_r32_gelu+awq_mod_1x3072x18432",
+                   "tokens": M, "d_model": K1, "d_ff": N1, "rank": 32, "group": 64,
+                   "awq_rows": 1, "rotation_sets": R},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                     "traffic": traffic, "kernel": "k2_w4a4_gemm",
+                     "ops_per_launch": ops_layer, "avg_launch_us": round(k2_us, 2)},
+        "kernels_us": {n: round(v, 2) for n, v in avg.items()},
+        "event_step_us": round(float(np.mean(span)), 2),
+        "k1_gbs": {"fc1": round(k1_bytes_fc1 / avg["fc1_quantize"] / 1e3, 1),
+                   "fc2": round(k1_bytes_fc2 / avg["fc2_quantize"] / 1e3, 1)},
+        "awq_gbs": round(awq_bytes / avg["awq_m1"] / 1e3, 1),
+        "prepare_s": {"fc1": round(prep1, 2), "fc2": round(prep2, 2)},
+        "source_hash": source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

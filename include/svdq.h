@@ -1,0 +1,230 @@
+/*
+ * svdq.h -- C ABI of libsvdq, an MI355X (gfx950) implementation of the
+ * SVDQuant W4A4 linear layer with its 16-bit low-rank branch, and of the
+ * AWQ-style W4A16 linear used for modulation layers.
+ *
+ * Method.  "Bringing Nunchaku 4-bit diffusion inference to Diffusers"
+ * (Vietnamese edition, section "Bối cảnh: SVDQuant và Nunchaku"; Korean
+ * edition, section "SVDQuant 및 Nunchaku 엔진"): activation outliers are
+ * migrated into the weights by per-channel smoothing, the hardest part of
+ * each smoothed weight is kept as a small 16-bit low-rank branch, and the
+ * remaining residual runs on 4-bit weights against 4-bit activations.  With
+ * X [M,K] bf16, W [N,K] bf16 (nn.Linear layout) and b [N]:
+ *
+ *   Y = Q4(X diag(iota)) Q4(R)^T (group scales) + (X L1s) L2 + b
+ *   R = W diag(lambda) - (diag(lambda) L1s L2)^T,   iota = 1/lambda
+ *
+ * Q4 is symmetric INT4 (codes -7..7) per group of 64 consecutive input
+ * channels with float32 scales s = a/7, a the group's max |value|.
+ * The same pages (Korean edition, same section) place the low-rank
+ * down-projection next to activation quantisation and the up-projection in
+ * the 4-bit GEMM; this library does the same with two device kernels.
+ *
+ * Conventions for every entry point
+ *   - Every function returns svdq_status_t; nothing throws across the ABI.
+ *     svdq_last_error() returns a thread-local message for the last failure.
+ *   - All validation is synchronous and happens before any HIP call.
+ *   - Ownership: the caller owns every host and device buffer.  The library
+ *     never allocates device memory; device scratch is the caller's
+ *     `workspace` (size from svdq_workspace_bytes).
+ *   - Device entry points are asynchronous: they enqueue on `hip_stream`
+ *     (a hipStream_t; NULL = the null stream) and never synchronise.  Launch
+ *     failures return SVDQ_ERR_HIP; faults surface at the caller's next sync.
+ *   - Device check: the first device call on a device checks that it is a
+ *     gfx950 part and caches the answer; any other device gets
+ *     SVDQ_ERR_UNSUPPORTED_DEVICE rather than a wrong result (the pages'
+ *     "Hỗ trợ phần cứng" section: the quantiser refuses unsupported GPUs at
+ *     load time with a clear error).
+ *   - Device pointers must be 16-byte aligned.
+ *   - Shapes: K % 64 == 0; M, N >= 1 (ragged tails are masked); rank in
+ *     [0, min(N, K)] and rank <= 256.
+ *   - bf16 / fp16 values are passed as uint16_t bit patterns on the host.
+ */
+#ifndef SVDQ_H_
+#define SVDQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SVDQ_ABI_VERSION 1
+#define SVDQ_GROUP_SIZE 64
+#define SVDQ_MAX_RANK 256
+
+typedef enum {
+  SVDQ_OK = 0,
+  SVDQ_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad enum, misaligned pointer */
+  SVDQ_ERR_UNSUPPORTED_SHAPE = 2,  /* K % 64 != 0, rank out of range, M/N/K < 1, too large */
+  SVDQ_ERR_NO_DEVICE = 3,          /* no HIP device visible */
+  SVDQ_ERR_UNSUPPORTED_DEVICE = 4, /* the current device is not gfx950 */
+  SVDQ_ERR_WORKSPACE_TOO_SMALL = 5,
+  SVDQ_ERR_NUMERICAL = 6,          /* non-finite input to an offline step */
+  SVDQ_ERR_HIP = 7                 /* a HIP runtime call or launch failed */
+} svdq_status_t;
+
+typedef enum { SVDQ_BF16 = 0, SVDQ_FP16 = 1, SVDQ_FP32 = 2 } svdq_dtype_t;
+
+/* Output epilogue of svdq_linear_forward. */
+typedef enum {
+  SVDQ_EPILOGUE_NONE = 0,
+  /* Y = gelu_tanh(linear(X)): the activation between the two projections of
+   * a diffusion-transformer MLP, fused into the store (Vietnamese edition,
+   * section "Giới thiệu Nunchaku Lite", which credits fused GELU/MLP paths
+   * for part of the original engine's speed). */
+  SVDQ_EPILOGUE_GELU_TANH = 1
+} svdq_epilogue_t;
+
+int svdq_abi_version(void);
+const char *svdq_status_string(svdq_status_t s);
+/* Thread-local description of the most recent failure on this thread. */
+const char *svdq_last_error(void);
+
+/* Checks the current HIP device once and caches the answer.  Returns
+ * SVDQ_OK on gfx950, SVDQ_ERR_NO_DEVICE or SVDQ_ERR_UNSUPPORTED_DEVICE
+ * otherwise.  Called implicitly by every device entry point. */
+svdq_status_t svdq_device_check(void);
+
+/* ======================================================== offline, host only */
+
+/* Host-side prepared weights.  Every pointer is caller-owned; sizes in bytes
+ * come from svdq_host_weights_sizes (order: inv_lambda, l1s, l2, qweight,
+ * wscales, bias). */
+typedef struct {
+  int32_t N, K, rank, group_size; /* group_size is always 64 */
+  float *inv_lambda;   /* [K]       fp32 iota_j = fl32(1/lambda_j) */
+  uint16_t *l1s;       /* [K, rank] bf16, = bf16(diag(iota) V_r S_r^(1/2)) */
+  uint16_t *l2;        /* [rank, N] bf16, = bf16(S_r^(1/2) U_r^T) */
+  uint8_t *qweight;    /* [N, K/2]  residual codes, canonical packing: byte j of a
+                          row = code 2j (low nibble) | code 2j+1 (high nibble),
+                          two's complement, codes in [-7, 7] */
+  float *wscales;      /* [N, K/64] fp32 group scales of the residual */
+  float *bias;         /* [N]       fp32 (zeros when no bias) */
+} svdq_host_weights_t;
+
+svdq_status_t svdq_host_weights_sizes(int N, int K, int rank, size_t sizes_out[6]);
+
+/* Per-channel max |x| over `rows` calibration rows of bf16 activations
+ * X_bf16 [rows, K] -> absmax_out [K] fp32.  Host only. */
+svdq_status_t svdq_calibration_absmax(const uint16_t *X_bf16, int rows, int K,
+                                      float *absmax_out);
+
+/* Offline preparation of one linear layer (host, multi-threaded):
+ *   1. smoothing factors lambda_j = fl32(sqrt(fl32(max(ax_j,1e-5)/max(aw_j,1e-5))))
+ *      from act_absmax (ax) and the weight column maxima (aw); act_absmax ==
+ *      NULL means no smoothing (lambda = 1).  Activation outliers move into
+ *      the weights (Vietnamese edition, "Bối cảnh: SVDQuant và Nunchaku").
+ *   2. W_hat = W diag(lambda) (float64), top-`rank` singular triplets of W_hat
+ *      (Gram matrix of the smaller side, Householder tridiagonalisation,
+ *      bisection and inverse iteration), split as L1 = V S^(1/2),
+ *      L2 = S^(1/2) U^T, stored bf16 with iota folded into L1.
+ *   3. residual R = W_hat - (diag(lambda) L1s L2)^T against the rounded
+ *      factors (float64, then float32), quantised per row and group of 64.
+ * W_bf16 [N, K] row-major; bias_bf16 [N] or NULL; group_size must be 64.
+ * Returns SVDQ_ERR_NUMERICAL on non-finite W, bias or act_absmax. */
+svdq_status_t svdq_prepare_weights(const uint16_t *W_bf16, int N, int K,
+                                   const float *act_absmax,
+                                   const uint16_t *bias_bf16, int rank,
+                                   int group_size, svdq_host_weights_t *out);
+
+/* Size of the device weight blob for (N, K, rank). */
+size_t svdq_device_weights_bytes(int N, int K, int rank);
+
+/* Re-tiles prepared host weights into the device blob layout (host memory,
+ * caller-allocated, `bytes` >= svdq_device_weights_bytes).  The caller
+ * uploads the blob to device memory; the layout is internal to the library
+ * and versioned with SVDQ_ABI_VERSION. */
+svdq_status_t svdq_pack_device_weights(const svdq_host_weights_t *in,
+                                       void *host_blob, size_t bytes);
+
+/* A prepared layer resident in device memory. */
+typedef struct {
+  const void *blob;   /* device pointer to the uploaded blob */
+  int32_t N, K, rank;
+} svdq_weights_t;
+
+/* =================================================== runtime, device, async */
+
+/* Device scratch needed by svdq_linear_forward for M token rows. */
+size_t svdq_workspace_bytes(int M, int N, int K, int rank);
+
+/* Y = linear(X) [+ epilogue] for X bf16 [M, K] (device, row-major) into
+ * Y [M, N] of dtype y_dtype (SVDQ_BF16 or SVDQ_FP32), row-major.
+ * Two kernels on `hip_stream`: (1) smoothing + per-group INT4 quantisation of
+ * X + low-rank down-projection D = X L1s; (2) INT4 x INT4 group GEMM with
+ * fp32 per-group scaling, + D L2 + bias (+ GELU) in the epilogue. */
+svdq_status_t svdq_linear_forward(const svdq_weights_t *w, const void *X, int M,
+                                  void *Y, svdq_dtype_t y_dtype,
+                                  svdq_epilogue_t epilogue, void *workspace,
+                                  size_t ws_bytes, void *hip_stream);
+
+/* The forward's two kernels as separate calls, for callers that time or
+ * schedule them apart.  svdq_linear_quantize runs kernel (1) on X and leaves
+ * the activation codes, scales and low-rank partials in `workspace`;
+ * svdq_linear_gemm runs kernel (2) from that workspace (same M, same weights,
+ * enqueued after the quantize call on the same stream or ordered after it).
+ * Calling both is exactly svdq_linear_forward. */
+svdq_status_t svdq_linear_quantize(const svdq_weights_t *w, const void *X, int M,
+                                   void *workspace, size_t ws_bytes, void *hip_stream);
+svdq_status_t svdq_linear_gemm(const svdq_weights_t *w, int M, void *Y, svdq_dtype_t y_dtype,
+                               svdq_epilogue_t epilogue, const void *workspace,
+                               size_t ws_bytes, void *hip_stream);
+
+/* Elementwise bf16 -> bf16 tanh-GELU (the unfused glue between the MLP's
+ * projections; same reading as SVDQ_EPILOGUE_GELU_TANH), n elements. */
+svdq_status_t svdq_gelu_tanh_bf16(const void *in, void *out, size_t n,
+                                  void *hip_stream);
+
+/* ------------------------------------------- test / inspection exports
+ * Same device kernels as the forward, writing canonical layouts. */
+
+/* qact [M, K/2] canonical packed activation codes, ascales [M, K/64] fp32,
+ * lowrank_down [M, rank] fp32 (= X L1s).  All device pointers. */
+svdq_status_t svdq_quantize_activations(const svdq_weights_t *w, const void *X,
+                                        int M, uint8_t *qact, float *ascales,
+                                        float *lowrank_down, void *workspace,
+                                        size_t ws_bytes, void *hip_stream);
+
+/* Exact int32 group sums P[i, j, g] = sum_{k in group g} qA[m0+i, k] qW[n0+j, k]
+ * for the window [m0, m0+mcount) x [n0, n0+ncount), computed by the GEMM
+ * kernel's own matrix-core path from the activation codes a preceding
+ * svdq_linear_forward / svdq_quantize_activations left in `workspace`
+ * (same M).  P is device [mcount, ncount, K/64] int32.  mcount, ncount in
+ * [1, 256]. */
+svdq_status_t svdq_debug_group_sums(const svdq_weights_t *w, int M, int m0,
+                                    int mcount, int n0, int ncount, int32_t *P,
+                                    const void *workspace, size_t ws_bytes,
+                                    void *hip_stream);
+
+/* ============================================================== AWQ W4A16
+ * "Bringing Nunchaku 4-bit diffusion inference to Diffusers" (Russian
+ * edition, technical-details section; Korean edition, "Diffusers 내
+ * Nunchaku Lite 통합"): 4-bit weights with 16-bit activations for
+ * memory-bound, precision-sensitive modulation projections. */
+
+/* Host round-to-nearest asymmetric INT4 per group of 64:
+ *   s = fp16(fl32(max(wmax - wmin, 1e-5) / 15)), z = clamp(rint(fl32(-wmin/s)), 0, 15),
+ *   q = clamp(rint(fl32(w/s)) + z, 0, 15).
+ * W_fp16 [N, K]; q [N, K/2] canonical unsigned nibbles (low = even k);
+ * scales_fp16, zeros_fp16 [N, K/64]. */
+svdq_status_t awq_quantize_weights(const uint16_t *W_fp16, int N, int K,
+                                   int group_size, uint8_t *q,
+                                   uint16_t *scales_fp16, uint16_t *zeros_fp16);
+
+size_t awq_device_weights_bytes(int N, int K);
+svdq_status_t awq_pack_device_weights(const uint8_t *q, const uint16_t *scales_fp16,
+                                      const uint16_t *zeros_fp16, int N, int K,
+                                      void *host_blob, size_t bytes);
+
+/* y [M, N] fp16 = sum_g s (sum_{k in g} x (q - z)) (+ bias) for x fp16 [M, K],
+ * M in [1, 16]; bias_fp16 [N] or NULL.  Device pointers; async. */
+svdq_status_t awq_w4a16_forward(const void *blob, int N, int K, const void *x_fp16,
+                                int M, const void *bias_fp16, void *y_fp16,
+                                void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SVDQ_H_ */

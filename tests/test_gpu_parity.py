@@ -1,0 +1,156 @@
+"""GPU parity at sizes the oracle finishes in seconds (several tiles and a
+ragged tail), plus the edge cases of the method.  Everything goes through the
+C ABI; expected values come only from the oracle on the same seeded inputs.
+
+Bars: INT4 codes, fp32 scales and int32 group sums bit-exact; Y within
+2e-3 * max|Y_ref| (fp32 output) and (2e-3 + 2^-8) * max|Y_ref| (bf16 output,
+whose own rounding is up to 2^-8 relative); the low-rank down-projection D
+within 1e-5 * max|D_ref|."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import svdquant as O
+from oracle import glue as OG
+from tests.conftest import announce
+from tests.gpu_util import bf16_to_device, layer_from_oracle, rel_max_err, to_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 2e-3
+TOL_BF16 = 2e-3 + 2.0 ** -8
+
+
+@pytest.fixture(scope="module")
+def S():
+    import w4a4_rank_corrected_smooth_amd as lib
+    lib.device_check()
+    return lib
+
+
+def run_case(S, c, smooth=True, rank=None, out_dtype=torch.float32, gelu=False, check_codes=True):
+    rank = c.rank if rank is None else rank
+    ax = c.calib_absmax() if smooth else None
+    announce(f"{c.name} M={c.M} N={c.N} K={c.K} r={rank} smooth={smooth} out={out_dtype} gelu={gelu}")
+    ref = O.prepare(c.W, ax, c.bias, rank)
+    layer = layer_from_oracle(ref)
+    X = bf16_to_device(c.X)
+    ws = layer.new_workspace(c.M)
+    Y = S.linear_forward(layer, X, out_dtype=out_dtype, gelu=gelu, workspace=ws)
+    f = O.forward(ref, c.X)
+    if check_codes:
+        q, s, d = S.quantize_activations(layer, X, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(q.cpu().numpy(), O.pack_int4(f["qA"])), "activation codes"
+        assert np.array_equal(s.cpu().numpy(), f["sA"]), "activation scales"
+        if rank > 0:
+            assert rel_max_err(to_f64(d), f["D"]) <= 1e-5, "low-rank down-projection"
+    torch.cuda.synchronize()
+    return ref, f, layer, X, ws, to_f64(Y)
+
+
+@pytest.mark.parametrize("M,N,K,rank", [(256, 512, 512, 16), (100, 200, 192, 5), (1, 64, 64, 1),
+                                        (33, 130, 320, 7), (300, 96, 128, 40), (129, 257, 256, 32)])
+def test_forward_small_shapes(S, M, N, K, rank):
+    c = synth.linear_case(f"small{M}x{N}x{K}", 200 + M, M, N, K, rank,
+                          x_outlier_n=max(1, K // 64), x_outlier_scale=40.0,
+                          w_outlier_n=max(1, K // 100), w_outlier_scale=8.0)
+    ref, f, layer, X, ws, Y = run_case(S, c)
+    assert rel_max_err(Y, f["Y"]) <= TOL_F32
+
+
+def test_tiny_config_both_output_types(S):
+    c = synth.tiny_case()
+    ref, f, layer, X, ws, Y = run_case(S, c)
+    assert rel_max_err(Y, f["Y"]) <= TOL_F32
+    Yb = to_f64(S.linear_forward(layer, X, out_dtype=torch.bfloat16, workspace=ws))
+    assert rel_max_err(Yb, f["Y"]) <= TOL_BF16
+
+
+def test_group_sums_bit_exact(S):
+    c = synth.linear_case("sums", 301, 300, 400, 256, 8, x_outlier_n=4, x_outlier_scale=40.0)
+    ref, f, layer, X, ws, Y = run_case(S, c)
+    for (m0, mc, n0, nc) in [(0, 64, 0, 64), (250, 50, 350, 50), (77, 130, 13, 200), (299, 1, 399, 1)]:
+        announce(f"group sums window m0={m0} mc={mc} n0={n0} nc={nc}")
+        P = S.debug_group_sums(layer, c.M, m0, mc, n0, nc, ws).cpu().numpy()
+        Pref = O.group_sums(f["qA"][m0:m0 + mc], ref["qW"][n0:n0 + nc])
+        assert np.array_equal(P, Pref)
+
+
+def test_rank0_without_smoothing(S):
+    c = synth.linear_case("r0", 302, 160, 192, 256, 0, x_outlier_n=3, x_outlier_scale=30.0)
+    ref, f, layer, X, ws, Y = run_case(S, c, smooth=False)
+    assert np.all(ref["iota"] == 1.0)
+    assert rel_max_err(Y, f["Y"]) <= TOL_F32
+
+
+def test_max_rank(S):
+    c = synth.linear_case("rmax", 303, 64, 256, 256, 256, x_outlier_n=4, x_outlier_scale=40.0)
+    ref, f, layer, X, ws, Y = run_case(S, c)
+    assert rel_max_err(Y, f["Y"]) <= TOL_F32
+
+
+@pytest.mark.parametrize("seed", [310, 311])
+def test_on_grid_inputs_are_exact(S, seed):
+    """Inputs on the INT4 grid with unit scales, r = 0, no smoothing, no bias:
+    every product and partial sum is an exact small integer, so the fp32
+    output must equal X W^T bit for bit."""
+    c = synth.on_grid_case(seed, 96, 160, 320, exp_lo=0, exp_hi=0)
+    ref, f, layer, X, ws, Y = run_case(S, c, smooth=False)
+    exact = O.bf16_values(c.X) @ O.bf16_values(c.W).T
+    assert np.array_equal(f["Y"], exact)
+    assert np.array_equal(Y, exact)
+
+
+def test_zero_activations_give_the_bias(S):
+    c = synth.linear_case("zero", 312, 40, 96, 128, 4)
+    c.X[:] = 0
+    ref = O.prepare(c.W, None, c.bias, 4)
+    layer = layer_from_oracle(ref)
+    Y = to_f64(S.linear_forward(layer, bf16_to_device(c.X), out_dtype=torch.float32))
+    assert np.array_equal(Y, np.broadcast_to(ref["bias"], Y.shape))
+
+
+def test_split_calls_equal_forward_and_are_deterministic(S):
+    c = synth.linear_case("split", 313, 200, 300, 384, 24, x_outlier_n=5, x_outlier_scale=50.0)
+    ref, f, layer, X, ws, Y = run_case(S, c, check_codes=False)
+    ws2 = layer.new_workspace(c.M)
+    S.linear_quantize(layer, X, ws2)
+    Y2 = torch.empty((c.M, c.N), dtype=torch.float32, device="cuda")
+    S.linear_gemm(layer, c.M, Y2, ws2)
+    Y3 = S.linear_forward(layer, X, out_dtype=torch.float32, workspace=ws2)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_f64(Y2), Y) and np.array_equal(to_f64(Y3), Y)
+
+
+def test_workspace_for_larger_M_serves_smaller_M(S):
+    c = synth.linear_case("wsre", 314, 64, 128, 192, 8, x_outlier_n=2, x_outlier_scale=30.0)
+    ref = O.prepare(c.W, c.calib_absmax(), c.bias, 8)
+    layer = layer_from_oracle(ref)
+    big = layer.new_workspace(1000)
+    Y = to_f64(S.linear_forward(layer, bf16_to_device(c.X), out_dtype=torch.float32, workspace=big))
+    assert rel_max_err(Y, O.forward(ref, c.X)["Y"]) <= TOL_F32
+
+
+def test_fused_gelu_epilogue(S):
+    c = synth.linear_case("gelu", 315, 130, 260, 256, 8, x_outlier_n=4, x_outlier_scale=40.0)
+    ref, f, layer, X, ws, _ = run_case(S, c, check_codes=False)
+    G = to_f64(S.linear_forward(layer, X, out_dtype=torch.bfloat16, gelu=True, workspace=ws))
+    Gref = OG.gelu_tanh_bf16(f["Y"])
+    # gelu is 1.13-Lipschitz: the 2e-3 bar on Y carries through, plus bf16 output rounding
+    assert np.max(np.abs(G - Gref)) <= (1.13 * TOL_F32 + 2.0 ** -8) * np.max(np.abs(f["Y"]))
+
+
+@pytest.mark.parametrize("n", [8, 1000, 4099, 1 << 16])
+def test_gelu_kernel_within_one_bf16_ulp(S, n):
+    rng = np.random.default_rng(n)
+    x = synth.f32_to_bf16_bits((rng.standard_normal(n) * 3).astype(np.float32))
+    x[:4] = synth.f32_to_bf16_bits(np.array([0.0, -0.0, 20.0, -20.0], np.float32))
+    announce(f"gelu n={n}")
+    y = S.gelu_tanh_bf16(bf16_to_device(x))
+    got = to_f64(y)
+    ref = OG.gelu_tanh_bf16(O.bf16_values(x))
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-38))) - 7)
+    assert np.all(np.abs(got - ref) <= ulp + 1e-38)
+    assert np.mean(got == ref) > 0.99

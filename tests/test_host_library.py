@@ -1,0 +1,243 @@
+"""CPU tests of libsvdq's host half: the library loads without a GPU and
+exports every symbol the header declares; offline preparation agrees with
+the oracle bit for bit where the method fixes every rounding (smoothing
+factors, residual codes and scales at rank 0, AWQ codes), and satisfies the
+SVD invariants where several results are correct (rank > 0); the device
+packer places codes where the documented layout says; every status code
+that can be forced from the host is returned.  No compute reaches a GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import synth
+from oracle import svdquant as O
+from oracle import awq as OA
+
+import w4a4_rank_corrected_smooth_amd as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+# ------------------------------------------------------------------ exports
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "svdq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:svdq|awq)_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _header_functions()
+    assert len(names) >= 18
+    lib = ctypes.CDLL(S.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(S.EXPORTS) == names
+    assert S.abi_version() == 1
+
+
+def test_status_strings():
+    lib = S._lib
+    for code in range(8):
+        assert lib.svdq_status_string(code)
+    assert b"unknown" in lib.svdq_status_string(99)
+
+
+# ----------------------------------------------------- prepare vs the oracle
+def test_smoothing_and_rank0_codes_bit_exact():
+    c = synth.tiny_case()
+    ax = c.calib_absmax()
+    hw = S.prepare_weights(c.W, ax, c.bias, 0)
+    ref = O.prepare(c.W, ax, c.bias, 0)
+    assert np.array_equal(hw.inv_lambda, ref["iota"])
+    assert np.array_equal(hw.qweight, O.pack_int4(ref["qW"]))
+    assert np.array_equal(hw.wscales, ref["sW"])
+    assert np.array_equal(hw.bias, ref["bias"].astype(np.float32))
+
+
+def test_calibration_absmax_matches():
+    c = synth.tiny_case()
+    assert np.array_equal(S.calibration_absmax(c.X[:64]), O.calibration_absmax(O.bf16_values(c.X[:64])))
+
+
+@pytest.mark.parametrize("seed,N,K", [(50, 192, 256), (51, 320, 128), (52, 128, 512)])
+def test_rank0_no_smoothing_bit_exact(seed, N, K):
+    c = synth.linear_case("r0", seed, 8, N, K, 0, w_outlier_n=5, w_outlier_scale=8.0)
+    hw = S.prepare_weights(c.W, None, None, 0)
+    ref = O.prepare(c.W, None, None, 0)
+    assert np.array_equal(hw.qweight, O.pack_int4(ref["qW"]))
+    assert np.array_equal(hw.wscales, ref["sW"])
+    assert np.all(hw.inv_lambda == 1.0) and np.all(hw.bias == 0.0)
+
+
+def _cpp_branch(hw, lam):
+    L1s = O.bf16_values(hw.l1s)
+    L2 = O.bf16_values(hw.l2)
+    return ((L1s * lam.astype(np.float64)[:, None]) @ L2).T
+
+
+@pytest.mark.parametrize("rank", [1, 8, 16, 40])
+def test_lowrank_split_invariants(rank):
+    c = synth.linear_case("svd", 60 + rank, 64, 160, 256, rank, x_outlier_n=6, x_outlier_scale=40.0,
+                          w_outlier_n=4, w_outlier_scale=8.0)
+    ax = c.calib_absmax()
+    hw = S.prepare_weights(c.W, ax, c.bias, rank)
+    ref = O.prepare(c.W, ax, c.bias, rank)
+    lam, _ = O.smoothing_factors(ax, O.bf16_values(c.W))
+    W_hat = O.smooth_weight(O.bf16_values(c.W), lam)
+    sig = scipy.linalg.svd(W_hat, compute_uv=False)
+    A = _cpp_branch(hw, lam)
+    # (1) the branch is the top-r part: residual energy matches Eckart-Young
+    #     up to the bf16 rounding of the factors
+    e_cpp = np.sum((W_hat - A) ** 2)
+    e_opt = np.sum(sig[rank:] ** 2)
+    assert e_opt <= e_cpp <= e_opt + 4 * 2.0 ** -8 * np.sqrt(e_opt) * sig[:rank].sum() + 1e-12
+    # (2) same branch as the oracle's (its own SVD, own signs) up to bf16 rounding
+    Aref = ((ref["L1s"] * lam.astype(np.float64)[:, None]) @ ref["L2b"]).T
+    assert np.linalg.norm(A - Aref) <= 2.0 ** -6 * np.linalg.norm(Aref)
+    # (3) factor structure: columns of L1 (iota folded back out) and rows of
+    #     L2 carry sigma_t: ||L1_t|| * ||L2_t|| ~ sigma_t
+    L1 = O.bf16_values(hw.l1s) * lam.astype(np.float64)[:, None]
+    L2 = O.bf16_values(hw.l2)
+    prod = np.linalg.norm(L1, axis=0) * np.linalg.norm(L2, axis=1)
+    assert np.allclose(prod, sig[:rank], rtol=2.0 ** -6)
+    # (4) residual codes reconstruct W_hat within half a quantisation step
+    deq = O.dequantize(O.unpack_int4(hw.qweight), hw.wscales)
+    step = np.repeat(hw.wscales.astype(np.float64), 64, axis=1)
+    err = np.abs(W_hat - A - deq)
+    assert np.all(err <= 0.5 * step * (1 + 2.0 ** -20) + 2.0 ** -24 * np.abs(W_hat - A) + 1e-30)
+
+
+def test_full_rank_leaves_only_factor_rounding():
+    c = synth.linear_case("fr", 70, 8, 64, 128, 64)
+    hw = S.prepare_weights(c.W, None, None, 64)
+    W = O.bf16_values(c.W)
+    A = _cpp_branch(hw, np.ones(128, np.float32))
+    # an exact SVD at r = min(N, K) leaves nothing but the factors' bf16 rounding
+    assert np.max(np.abs(W - A)) <= 2.0 ** -6 * np.max(np.abs(W))
+    assert np.max(hw.wscales) <= 2.0 ** -6 * np.max(np.abs(W)) / 7 * 8
+
+
+def test_prepare_is_deterministic():
+    c = synth.linear_case("det", 71, 8, 256, 192, 12, x_outlier_n=3, x_outlier_scale=30.0)
+    ax = c.calib_absmax()
+    a = S.prepare_weights(c.W, ax, c.bias, 12)
+    b = S.prepare_weights(c.W, ax, c.bias, 12)
+    for f in ("inv_lambda", "l1s", "l2", "qweight", "wscales", "bias"):
+        assert np.array_equal(getattr(a, f), getattr(b, f)), f
+
+
+def test_singular_values_of_a_tall_and_a_wide_matrix():
+    """Both Gram sides (N > K and N < K) give the top singular directions."""
+    for N, K in ((320, 128), (96, 384)):
+        c = synth.linear_case("tw", 72 + N, 8, N, K, 10, w_outlier_n=3, w_outlier_scale=8.0)
+        hw = S.prepare_weights(c.W, None, None, 10)
+        W = O.bf16_values(c.W)
+        sig = scipy.linalg.svd(W, compute_uv=False)
+        A = _cpp_branch(hw, np.ones(K, np.float32))
+        assert abs(np.linalg.norm(W - A) ** 2 - np.sum(sig[10:] ** 2)) <= \
+            4 * 2.0 ** -8 * np.linalg.norm(W) * sig[:10].sum()
+
+
+# ------------------------------------------------------------- device packer
+def test_device_blob_layout():
+    c = synth.linear_case("pk", 80, 8, 100, 192, 5, x_outlier_n=2, x_outlier_scale=20.0)
+    hw = S.prepare_weights(c.W, c.calib_absmax(), c.bias, 5)
+    blob = S.pack_device_weights(hw)
+    N, K, G = 100, 192, 3
+    Np = 256
+    codes = O.unpack_int4(hw.qweight)
+    qdev = blob[: Np * K].view(np.int8)
+    T = Np // 32
+    for n in range(0, N, 7):
+        for k in range(K):
+            g, kk = divmod(k, 64)
+            h = (kk % 16) // 8
+            cidx = 8 * (kk // 16) + kk % 8
+            lane = n % 32 + 32 * h
+            off = (g * T + n // 32) * 2048 + (cidx // 8) * 512 + lane * 8 + cidx % 8
+            assert qdev[off] == codes[n, k]
+    # padded rows hold zero codes
+    assert not np.any(qdev.reshape(G, T, 2048)[:, 4:, :])
+    s_off = Np * K
+    sdev = blob[s_off: s_off + G * Np * 4].view(np.float32).reshape(G, Np)
+    assert np.array_equal(sdev[:, :N].T, hw.wscales) and not np.any(sdev[:, N:])
+
+
+def test_awq_quantizer_bit_exact_and_packer():
+    a = synth.awq_case(m_max=1, N=96, K=256, seed=81)
+    q, s, z = S.awq_quantize_weights(a.W)
+    rq, rs, rz = OA.quantize(a.W)
+    assert np.array_equal(q, OA.pack(rq))
+    assert np.array_equal(s.view(np.uint16), rs.view(np.uint16))
+    assert np.array_equal(z.view(np.uint16), rz.view(np.uint16))
+
+
+# ---------------------------------------------------------------- errors
+INV, SHAPE, NODEV, WS, NUM = 1, 2, 3, 5, 6
+FAKE = 1 << 20          # aligned, never dereferenced: validation fails first
+
+
+def _dw(N=128, K=128, rank=4, blob=FAKE):
+    return S.DeviceWeights(blob, N, K, rank)
+
+
+def test_prepare_errors():
+    lib = S._lib
+    W = np.zeros((16, 64), np.uint16)
+    hw = S.PreparedHost(16, 64, 0, np.zeros(64, np.float32), np.zeros((64, 0), np.uint16),
+                        np.zeros((0, 16), np.uint16), np.zeros((16, 32), np.uint8),
+                        np.zeros((16, 1), np.float32), np.zeros(16, np.float32)).as_struct()
+    assert lib.svdq_prepare_weights(None, 16, 64, None, None, 0, 64, ctypes.byref(hw)) == INV
+    assert lib.svdq_prepare_weights(W.ctypes.data, 16, 64, None, None, 0, 32, ctypes.byref(hw)) == SHAPE
+    assert lib.svdq_prepare_weights(W.ctypes.data, 16, 60, None, None, 0, 64, ctypes.byref(hw)) == SHAPE
+    assert lib.svdq_prepare_weights(W.ctypes.data, 16, 64, None, None, 17, 64, ctypes.byref(hw)) == SHAPE
+    assert lib.svdq_prepare_weights(W.ctypes.data, 16, 64, None, None, -1, 64, ctypes.byref(hw)) == SHAPE
+    assert lib.svdq_prepare_weights(W.ctypes.data, 0, 64, None, None, 0, 64, ctypes.byref(hw)) == SHAPE
+    Wn = W.copy()
+    Wn[3, 5] = 0x7FC0                      # bf16 NaN
+    assert lib.svdq_prepare_weights(Wn.ctypes.data, 16, 64, None, None, 0, 64, ctypes.byref(hw)) == NUM
+    ax = np.ones(64, np.float32)
+    ax[2] = np.inf
+    assert lib.svdq_prepare_weights(W.ctypes.data, 16, 64, ax.ctypes.data, None, 0, 64, ctypes.byref(hw)) == NUM
+    assert b"act_absmax" in lib.svdq_last_error()
+    with pytest.raises(S.SvdqError):
+        S.prepare_weights(np.zeros((8, 100), np.uint16), None, None, 0)
+
+
+def test_forward_validation_errors():
+    lib = S._lib
+    w = _dw()
+    ws = S.workspace_bytes(64, 128, 128, 4)
+    call = lambda **kw: lib.svdq_linear_forward(
+        ctypes.byref(kw.get("w", w)), kw.get("X", FAKE), kw.get("M", 64), kw.get("Y", FAKE),
+        kw.get("dt", S.BF16), kw.get("epi", 0), kw.get("ws", FAKE), kw.get("wsb", ws), None)
+    assert call(X=None) == INV
+    assert call(X=FAKE + 4) == INV                 # misaligned
+    assert call(M=0) == SHAPE
+    assert call(dt=S.FP16) == INV
+    assert call(epi=7) == INV
+    assert call(wsb=ws - 1) == WS
+    assert call(w=_dw(K=100)) == SHAPE
+    assert call(w=_dw(rank=200)) == SHAPE
+    assert call(w=_dw(blob=0)) == INV
+    assert lib.awq_w4a16_forward(FAKE, 64, 128, FAKE, 17, None, FAKE, None) == SHAPE
+    assert lib.awq_w4a16_forward(FAKE, 64, 100, FAKE, 1, None, FAKE, None) == SHAPE
+    assert lib.awq_w4a16_forward(None, 64, 128, FAKE, 1, None, FAKE, None) == INV
+    assert lib.svdq_debug_group_sums(ctypes.byref(w), 64, 0, 300, 0, 8, FAKE, FAKE, ws, None) == SHAPE
+    assert lib.svdq_debug_group_sums(ctypes.byref(w), 64, 60, 8, 0, 8, FAKE, FAKE, ws, None) == SHAPE
+    assert lib.svdq_gelu_tanh_bf16(FAKE + 2, FAKE, 16, None) == INV
+    assert S._lib.svdq_workspace_bytes(0, 128, 128, 4) == 0
+    assert S._lib.svdq_device_weights_bytes(128, 100, 4) == 0
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="checks the no-device path")
+def test_no_device_is_reported():
+    assert S._lib.svdq_device_check() == NODEV
+    w = _dw()
+    ws = S.workspace_bytes(64, 128, 128, 4)
+    assert S._lib.svdq_linear_forward(ctypes.byref(w), FAKE, 64, FAKE, S.BF16, 0, FAKE, ws, None) == NODEV
+    assert S._lib.svdq_gelu_tanh_bf16(FAKE, FAKE, 16, None) == NODEV

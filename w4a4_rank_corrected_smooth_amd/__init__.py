@@ -1,0 +1,314 @@
+"""Python binding of libsvdq: the SVDQuant W4A4 + low-rank linear layer and
+the AWQ W4A16 linear on MI355X (gfx950).
+
+This module only marshals arguments into the C ABI declared in
+``include/svdq.h``: every step of the method runs in the library (host
+preparation in C++, the forward in HIP kernels).  PyTorch supplies device
+memory and streams.  Importing fails loudly when the library is missing;
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch  # loaded first so the library binds to the HIP runtime torch uses
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsvdq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python w4a4_rank_corrected_smooth_amd/build.py` (hipcc, gfx950)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+OK = 0
+STATUS = {0: "SVDQ_OK", 1: "SVDQ_ERR_INVALID_ARGUMENT", 2: "SVDQ_ERR_UNSUPPORTED_SHAPE",
+          3: "SVDQ_ERR_NO_DEVICE", 4: "SVDQ_ERR_UNSUPPORTED_DEVICE",
+          5: "SVDQ_ERR_WORKSPACE_TOO_SMALL", 6: "SVDQ_ERR_NUMERICAL", 7: "SVDQ_ERR_HIP"}
+BF16, FP16, FP32 = 0, 1, 2
+EPILOGUE_NONE, EPILOGUE_GELU_TANH = 0, 1
+
+EXPORTS = [
+    "svdq_abi_version", "svdq_status_string", "svdq_last_error", "svdq_device_check",
+    "svdq_host_weights_sizes", "svdq_calibration_absmax", "svdq_prepare_weights",
+    "svdq_device_weights_bytes", "svdq_pack_device_weights", "svdq_workspace_bytes",
+    "svdq_linear_forward", "svdq_linear_quantize", "svdq_linear_gemm", "svdq_gelu_tanh_bf16", "svdq_quantize_activations",
+    "svdq_debug_group_sums", "awq_quantize_weights", "awq_device_weights_bytes",
+    "awq_pack_device_weights", "awq_w4a16_forward",
+]
+
+
+class HostWeights(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("K", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("group_size", ctypes.c_int32), ("inv_lambda", _vp), ("l1s", _vp), ("l2", _vp),
+                ("qweight", _vp), ("wscales", _vp), ("bias", _vp)]
+
+
+class DeviceWeights(ctypes.Structure):
+    _fields_ = [("blob", _vp), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("rank", ctypes.c_int32)]
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+
+
+_sig("svdq_abi_version", _i, [])
+_sig("svdq_status_string", ctypes.c_char_p, [_i])
+_sig("svdq_last_error", ctypes.c_char_p, [])
+_sig("svdq_device_check", _i, [])
+_sig("svdq_host_weights_sizes", _i, [_i, _i, _i, ctypes.POINTER(_sz)])
+_sig("svdq_calibration_absmax", _i, [_vp, _i, _i, _vp])
+_sig("svdq_prepare_weights", _i, [_vp, _i, _i, _vp, _vp, _i, _i, ctypes.POINTER(HostWeights)])
+_sig("svdq_device_weights_bytes", _sz, [_i, _i, _i])
+_sig("svdq_pack_device_weights", _i, [ctypes.POINTER(HostWeights), _vp, _sz])
+_sig("svdq_workspace_bytes", _sz, [_i, _i, _i, _i])
+_sig("svdq_linear_forward", _i, [ctypes.POINTER(DeviceWeights), _vp, _i, _vp, _i, _i, _vp, _sz, _vp])
+_sig("svdq_linear_quantize", _i, [ctypes.POINTER(DeviceWeights), _vp, _i, _vp, _sz, _vp])
+_sig("svdq_linear_gemm", _i, [ctypes.POINTER(DeviceWeights), _i, _vp, _i, _i, _vp, _sz, _vp])
+_sig("svdq_gelu_tanh_bf16", _i, [_vp, _vp, _sz, _vp])
+_sig("svdq_quantize_activations", _i, [ctypes.POINTER(DeviceWeights), _vp, _i, _vp, _vp, _vp,
+                                       _vp, _sz, _vp])
+_sig("svdq_debug_group_sums", _i, [ctypes.POINTER(DeviceWeights), _i, _i, _i, _i, _i, _vp, _vp,
+                                   _sz, _vp])
+_sig("awq_quantize_weights", _i, [_vp, _i, _i, _i, _vp, _vp, _vp])
+_sig("awq_device_weights_bytes", _sz, [_i, _i])
+_sig("awq_pack_device_weights", _i, [_vp, _vp, _vp, _i, _i, _vp, _sz])
+_sig("awq_w4a16_forward", _i, [_vp, _i, _i, _vp, _i, _vp, _vp, _vp])
+
+
+class SvdqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.svdq_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {msg}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise SvdqError(status, where)
+
+
+def _ptr(a) -> Optional[int]:
+    if a is None:
+        return None
+    if isinstance(a, torch.Tensor):
+        return a.data_ptr()
+    return a.ctypes.data
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def abi_version() -> int:
+    return _lib.svdq_abi_version()
+
+
+def device_check() -> None:
+    _check(_lib.svdq_device_check(), "svdq_device_check")
+
+
+# ------------------------------------------------------------ offline, host
+@dataclass
+class PreparedHost:
+    """Output of svdq_prepare_weights (host numpy arrays, canonical layouts)."""
+    N: int
+    K: int
+    rank: int
+    inv_lambda: np.ndarray   # float32 [K]
+    l1s: np.ndarray          # uint16 (bf16) [K, rank]
+    l2: np.ndarray           # uint16 (bf16) [rank, N]
+    qweight: np.ndarray      # uint8 [N, K/2]
+    wscales: np.ndarray      # float32 [N, K/64]
+    bias: np.ndarray         # float32 [N]
+
+    def as_struct(self) -> HostWeights:
+        return HostWeights(self.N, self.K, self.rank, 64, _ptr(self.inv_lambda),
+                           _ptr(self.l1s) if self.rank else None,
+                           _ptr(self.l2) if self.rank else None, _ptr(self.qweight),
+                           _ptr(self.wscales), _ptr(self.bias))
+
+
+def calibration_absmax(X_bits: np.ndarray) -> np.ndarray:
+    X_bits = np.ascontiguousarray(X_bits, dtype=np.uint16)
+    rows, K = X_bits.shape
+    out = np.empty(K, np.float32)
+    _check(_lib.svdq_calibration_absmax(_ptr(X_bits), rows, K, _ptr(out)), "svdq_calibration_absmax")
+    return out
+
+
+def prepare_weights(W_bits: np.ndarray, act_absmax: Optional[np.ndarray],
+                    bias_bits: Optional[np.ndarray], rank: int) -> PreparedHost:
+    """Host preparation (smoothing, top-r SVD split, residual INT4 quantisation)."""
+    W_bits = np.ascontiguousarray(W_bits, dtype=np.uint16)
+    N, K = W_bits.shape
+    ax = None if act_absmax is None else np.ascontiguousarray(act_absmax, dtype=np.float32)
+    b = None if bias_bits is None else np.ascontiguousarray(bias_bits, dtype=np.uint16)
+    G = max(K // 64, 1)
+    out = PreparedHost(N, K, rank, np.empty(K, np.float32), np.empty((K, rank), np.uint16),
+                       np.empty((rank, N), np.uint16), np.empty((N, max(K // 2, 1)), np.uint8),
+                       np.empty((N, G), np.float32), np.empty(N, np.float32))
+    hw = out.as_struct()
+    _check(_lib.svdq_prepare_weights(_ptr(W_bits), N, K, _ptr(ax), _ptr(b), rank, 64,
+                                     ctypes.byref(hw)), "svdq_prepare_weights")
+    return out
+
+
+def device_weights_bytes(N: int, K: int, rank: int) -> int:
+    return _lib.svdq_device_weights_bytes(N, K, rank)
+
+
+def pack_device_weights(hw: PreparedHost) -> np.ndarray:
+    n = device_weights_bytes(hw.N, hw.K, hw.rank)
+    if n == 0:
+        raise SvdqError(2, "svdq_device_weights_bytes")
+    blob = np.empty(n, np.uint8)
+    s = hw.as_struct()
+    _check(_lib.svdq_pack_device_weights(ctypes.byref(s), _ptr(blob), n), "svdq_pack_device_weights")
+    return blob
+
+
+class Linear:
+    """A prepared SVDQuant layer resident on one device."""
+
+    def __init__(self, hw: PreparedHost, device="cuda"):
+        self.N, self.K, self.rank = hw.N, hw.K, hw.rank
+        self.blob = torch.from_numpy(pack_device_weights(hw)).to(device)
+        self.device = self.blob.device
+        self._w = DeviceWeights(self.blob.data_ptr(), self.N, self.K, self.rank)
+
+    def workspace_bytes(self, M: int) -> int:
+        return workspace_bytes(M, self.N, self.K, self.rank)
+
+    def new_workspace(self, M: int) -> torch.Tensor:
+        return torch.empty(self.workspace_bytes(M), dtype=torch.uint8, device=self.device)
+
+
+def workspace_bytes(M: int, N: int, K: int, rank: int) -> int:
+    n = _lib.svdq_workspace_bytes(M, N, K, rank)
+    if n == 0:
+        raise SvdqError(2, "svdq_workspace_bytes")
+    return n
+
+
+# ------------------------------------------------------------- device calls
+def linear_forward(layer: Linear, X: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   out_dtype=torch.bfloat16, gelu: bool = False,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X W^T + b through the SVDQuant path (optionally gelu_tanh(Y))."""
+    assert X.dtype == torch.bfloat16 and X.is_contiguous() and X.shape[1] == layer.K
+    M = X.shape[0]
+    if out is None:
+        out = torch.empty((M, layer.N), dtype=out_dtype, device=X.device)
+    if workspace is None:
+        workspace = layer.new_workspace(M)
+    dt = FP32 if out.dtype == torch.float32 else BF16
+    _check(_lib.svdq_linear_forward(ctypes.byref(layer._w), X.data_ptr(), M, out.data_ptr(), dt,
+                                    EPILOGUE_GELU_TANH if gelu else EPILOGUE_NONE,
+                                    workspace.data_ptr(), workspace.numel(), _stream(X.device)),
+           "svdq_linear_forward")
+    return out
+
+
+def linear_quantize(layer: Linear, X: torch.Tensor, workspace: torch.Tensor) -> None:
+    """Kernel (1) of the forward alone: fills `workspace` from X."""
+    assert X.dtype == torch.bfloat16 and X.is_contiguous() and X.shape[1] == layer.K
+    _check(_lib.svdq_linear_quantize(ctypes.byref(layer._w), X.data_ptr(), X.shape[0],
+                                     workspace.data_ptr(), workspace.numel(), _stream(X.device)),
+           "svdq_linear_quantize")
+
+
+def linear_gemm(layer: Linear, M: int, out: torch.Tensor, workspace: torch.Tensor,
+                gelu: bool = False) -> torch.Tensor:
+    """Kernel (2) of the forward alone, from a workspace filled by linear_quantize."""
+    dt = FP32 if out.dtype == torch.float32 else BF16
+    _check(_lib.svdq_linear_gemm(ctypes.byref(layer._w), M, out.data_ptr(), dt,
+                                 EPILOGUE_GELU_TANH if gelu else EPILOGUE_NONE,
+                                 workspace.data_ptr(), workspace.numel(), _stream(out.device)),
+           "svdq_linear_gemm")
+    return out
+
+
+def gelu_tanh_bf16(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    assert x.dtype == torch.bfloat16 and x.is_contiguous()
+    if out is None:
+        out = torch.empty_like(x)
+    _check(_lib.svdq_gelu_tanh_bf16(x.data_ptr(), out.data_ptr(), x.numel(), _stream(x.device)),
+           "svdq_gelu_tanh_bf16")
+    return out
+
+
+def quantize_activations(layer: Linear, X: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+    """Canonical-layout export of the quantiser kernel: (codes uint8 [M, K/2],
+    scales float32 [M, K/64], low-rank down float32 [M, rank])."""
+    M = X.shape[0]
+    dev = X.device
+    q = torch.empty((M, layer.K // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((M, layer.K // 64), dtype=torch.float32, device=dev)
+    d = torch.empty((M, max(layer.rank, 1)), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = layer.new_workspace(M)
+    _check(_lib.svdq_quantize_activations(ctypes.byref(layer._w), X.data_ptr(), M, q.data_ptr(),
+                                          s.data_ptr(), d.data_ptr(), workspace.data_ptr(),
+                                          workspace.numel(), _stream(dev)),
+           "svdq_quantize_activations")
+    return q, s, d[:, :layer.rank]
+
+
+def debug_group_sums(layer: Linear, M: int, m0: int, mcount: int, n0: int, ncount: int,
+                     workspace: torch.Tensor) -> torch.Tensor:
+    P = torch.empty((mcount, ncount, layer.K // 64), dtype=torch.int32, device=workspace.device)
+    _check(_lib.svdq_debug_group_sums(ctypes.byref(layer._w), M, m0, mcount, n0, ncount,
+                                      P.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                      _stream(workspace.device)), "svdq_debug_group_sums")
+    return P
+
+
+# ------------------------------------------------------------------- AWQ
+def awq_quantize_weights(W_fp16: np.ndarray):
+    W = np.ascontiguousarray(W_fp16, dtype=np.float16)
+    N, K = W.shape
+    q = np.empty((N, K // 2), np.uint8)
+    s = np.empty((N, K // 64), np.uint16)
+    z = np.empty((N, K // 64), np.uint16)
+    _check(_lib.awq_quantize_weights(_ptr(W.view(np.uint16)), N, K, 64, _ptr(q), _ptr(s), _ptr(z)),
+           "awq_quantize_weights")
+    return q, s.view(np.float16), z.view(np.float16)
+
+
+class AwqLinear:
+    def __init__(self, q: np.ndarray, s: np.ndarray, z: np.ndarray, device="cuda"):
+        self.N, self.K = q.shape[0], q.shape[1] * 2
+        n = _lib.awq_device_weights_bytes(self.N, self.K)
+        if n == 0:
+            raise SvdqError(2, "awq_device_weights_bytes")
+        blob = np.empty(n, np.uint8)
+        q = np.ascontiguousarray(q, np.uint8)
+        s = np.ascontiguousarray(s, np.float16).view(np.uint16)
+        z = np.ascontiguousarray(z, np.float16).view(np.uint16)
+        _check(_lib.awq_pack_device_weights(_ptr(q), _ptr(s), _ptr(z), self.N, self.K, _ptr(blob), n),
+               "awq_pack_device_weights")
+        self.blob = torch.from_numpy(blob).to(device)
+
+
+def awq_forward(layer: AwqLinear, x: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    assert x.dtype == torch.float16 and x.is_contiguous() and x.shape[1] == layer.K
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, layer.N), dtype=torch.float16, device=x.device)
+    _check(_lib.awq_w4a16_forward(layer.blob.data_ptr(), layer.N, layer.K, x.data_ptr(), M,
+                                  None if bias is None else bias.data_ptr(), out.data_ptr(),
+                                  _stream(x.device)), "awq_w4a16_forward")
+    return out

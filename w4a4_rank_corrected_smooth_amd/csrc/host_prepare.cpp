@@ -1,0 +1,259 @@
+// Offline preparation (host): smoothing factors, top-r low-rank split,
+// residual quantisation, device packing; AWQ round-to-nearest quantiser.
+//
+// This file is compiled with -ffp-contract=off: every float32 step below is
+// one IEEE operation, so the scales and codes are reproducible bit for bit.
+#include "host_prepare.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "common.h"
+#include "host_linalg.h"
+#include "host_threads.h"
+#include "layout.h"
+
+namespace svdq {
+
+// ------------------------------------------------------------ conversions
+float f16_to_f32(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h & 0x8000) << 16;
+  const uint32_t e = (h >> 10) & 0x1F, m = h & 0x3FF;
+  if (e == 0) {
+    float f = (float)m * (1.0f / 16777216.0f);   // m * 2^-24, exact
+    return sign ? -f : f;
+  }
+  if (e == 31) return f32_from_bits(sign | 0x7F800000u | (m << 13));
+  return f32_from_bits(sign | ((e - 15 + 127) << 23) | (m << 13));
+}
+
+uint16_t f32_to_f16(float f) {
+  const uint32_t x = f32_bits(f);
+  const uint16_t sign = (uint16_t)((x >> 16) & 0x8000);
+  const uint32_t ax = x & 0x7FFFFFFFu;
+  if (ax >= 0x7F800000u) return sign | 0x7C00 | (ax > 0x7F800000u ? 0x200 : 0);
+  if (ax >= 0x477FF000u) return sign | 0x7C00;                 // rounds past 65504
+  if (ax < 0x38800000u) {                                      // below 2^-14: subnormal
+    const float a = f32_from_bits(ax) * 16777216.0f;           // * 2^24, exact
+    return sign | (uint16_t)std::nearbyint(a);                 // 1024 encodes 2^-14
+  }
+  uint32_t h = (((ax >> 23) - 127 + 15) << 10) | ((ax & 0x7FFFFFu) >> 13);
+  const uint32_t rem = ax & 0x1FFFu;
+  if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) ++h;
+  return sign | (uint16_t)h;
+}
+
+uint16_t f64_to_bf16(double x) {
+  if (x == 0.0) return std::signbit(x) ? 0x8000 : 0;
+  int e;
+  std::frexp(x, &e);                                  // x = m 2^e, 0.5 <= |m| < 1
+  const double q = std::ldexp(1.0, std::max(e - 8, -133));
+  const double r = std::nearbyint(x / q) * q;         // x / q exact; ties to even
+  return (uint16_t)(f32_bits((float)r) >> 16);        // r is a bf16 value
+}
+
+// --------------------------------------------------------- group quantiser
+void quantize_group64(const float *v, int8_t *q, float *s) {
+  float a = 0.0f;
+  for (int i = 0; i < kGroup; ++i) a = std::max(a, std::fabs(v[i]));
+  if (!(a >= 0x1p-100f)) {
+    *s = 0.0f;
+    std::memset(q, 0, kGroup);
+    return;
+  }
+  *s = a / 7.0f;
+  const float inv = 7.0f / a;
+  for (int i = 0; i < kGroup; ++i) {
+    float t = std::rint(v[i] * inv);
+    t = std::min(7.0f, std::max(-7.0f, t));
+    q[i] = (int8_t)t;
+  }
+}
+
+// ---------------------------------------------------------------- prepare
+svdq_status_t prepare_weights(const uint16_t *W_bf16, int N, int K, const float *act_absmax,
+                              const uint16_t *bias_bf16, int rank, svdq_host_weights_t *out) {
+  const int64_t NK = (int64_t)N * K;
+  const int G = K / kGroup;
+  std::vector<float> W((size_t)NK);
+  bool finite = true;
+  for (int64_t i = 0; i < NK; ++i) {
+    W[i] = bf16_to_f32(W_bf16[i]);
+    if (!std::isfinite(W[i])) finite = false;
+  }
+  if (!finite) return fail(SVDQ_ERR_NUMERICAL, "non-finite value in W");
+  if (act_absmax)
+    for (int k = 0; k < K; ++k)
+      if (!std::isfinite(act_absmax[k]) || act_absmax[k] < 0.0f)
+        return fail(SVDQ_ERR_NUMERICAL, "act_absmax[%d] is negative or non-finite", k);
+  if (bias_bf16)
+    for (int n = 0; n < N; ++n)
+      if (!std::isfinite(bf16_to_f32(bias_bf16[n])))
+        return fail(SVDQ_ERR_NUMERICAL, "non-finite bias[%d]", n);
+
+  // 1. smoothing factors (float32)
+  std::vector<float> lam(K, 1.0f), iota(K, 1.0f);
+  if (act_absmax) {
+    std::vector<float> aw(K, 0.0f);
+    for (int64_t n = 0; n < N; ++n)
+      for (int k = 0; k < K; ++k) aw[k] = std::max(aw[k], std::fabs(W[n * K + k]));
+    const float floor_ = 1e-5f;
+    for (int k = 0; k < K; ++k) {
+      const float ratio = std::max(act_absmax[k], floor_) / std::max(aw[k], floor_);
+      lam[k] = std::sqrt(ratio);
+      iota[k] = 1.0f / lam[k];
+    }
+  }
+  std::memcpy(out->inv_lambda, iota.data(), sizeof(float) * K);
+
+  // 2. smoothed weight (float64, exact) and its top-r SVD
+  std::vector<double> What((size_t)NK);
+  parallel_for(N, 64, [&](int64_t n0, int64_t n1) {
+    for (int64_t n = n0; n < n1; ++n)
+      for (int k = 0; k < K; ++k) What[n * K + k] = (double)W[n * K + k] * (double)lam[k];
+  });
+  std::vector<double> L1s((size_t)K * std::max(rank, 1), 0.0), L2((size_t)rank * N, 0.0);
+  if (rank > 0) {
+    std::vector<double> U((size_t)N * rank), sig(rank), V((size_t)K * rank);
+    if (svd_top(What.data(), N, K, rank, U.data(), sig.data(), V.data()) != 0)
+      return fail(SVDQ_ERR_NUMERICAL, "eigensolver produced a non-finite value");
+    for (int t = 0; t < rank; ++t) {
+      const double root = std::sqrt(sig[t]);
+      for (int k = 0; k < K; ++k) {
+        const double l1 = V[(int64_t)k * rank + t] * root;
+        const uint16_t b = f64_to_bf16((double)iota[k] * l1);
+        out->l1s[(int64_t)k * rank + t] = b;
+        L1s[(int64_t)k * rank + t] = (double)bf16_to_f32(b);
+      }
+      for (int n = 0; n < N; ++n) {
+        const uint16_t b = f64_to_bf16(root * U[(int64_t)n * rank + t]);
+        out->l2[(int64_t)t * N + n] = b;
+        L2[(int64_t)t * N + n] = (double)bf16_to_f32(b);
+      }
+    }
+  }
+
+  // 3. residual against the rounded factors, float64 -> float32, quantised
+  //    per row and group of 64
+  parallel_for(N, 16, [&](int64_t n0, int64_t n1) {
+    std::vector<float> row(K);
+    std::vector<double> l2n(std::max(rank, 1));
+    std::vector<int8_t> q(kGroup);
+    for (int64_t n = n0; n < n1; ++n) {
+      for (int t = 0; t < rank; ++t) l2n[t] = L2[(int64_t)t * N + n];
+      for (int k = 0; k < K; ++k) {
+        double s = 0.0;
+        const double *l1 = &L1s[(int64_t)k * rank];
+        for (int t = 0; t < rank; ++t) s += l1[t] * l2n[t];
+        const double branch = s * (double)lam[k];
+        row[k] = (float)(What[n * K + k] - branch);
+      }
+      for (int g = 0; g < G; ++g) {
+        float sc;
+        quantize_group64(&row[g * kGroup], q.data(), &sc);
+        out->wscales[n * G + g] = sc;
+        uint8_t *dst = out->qweight + n * (K / 2) + g * (kGroup / 2);
+        for (int j = 0; j < kGroup / 2; ++j)
+          dst[j] = (uint8_t)(((uint8_t)q[2 * j] & 0x0F) | (((uint8_t)q[2 * j + 1] & 0x0F) << 4));
+      }
+    }
+  });
+  for (int n = 0; n < N; ++n) out->bias[n] = bias_bf16 ? bf16_to_f32(bias_bf16[n]) : 0.0f;
+  out->N = N;
+  out->K = K;
+  out->rank = rank;
+  out->group_size = kGroup;
+  return SVDQ_OK;
+}
+
+// ------------------------------------------------------------ device pack
+svdq_status_t pack_device_weights(const svdq_host_weights_t *in, void *host_blob, size_t bytes) {
+  const WeightLayout L(in->N, in->K, in->rank);
+  if ((int64_t)bytes < L.total)
+    return fail(SVDQ_ERR_WORKSPACE_TOO_SMALL, "blob needs %lld bytes, got %zu",
+                (long long)L.total, bytes);
+  uint8_t *b = static_cast<uint8_t *>(host_blob);
+  std::memset(b, 0, (size_t)L.total);
+  const int64_t N = in->N, K = in->K, r = in->rank, T = L.Np / kTile;
+  int8_t *q = reinterpret_cast<int8_t *>(b + L.q);
+  parallel_for(N, 64, [&](int64_t n0, int64_t n1) {
+    for (int64_t n = n0; n < n1; ++n)
+      for (int64_t k = 0; k < K; k += 2) {
+        const uint8_t byte = in->qweight[n * (K / 2) + k / 2];
+        q[code_offset_rk(n, k, T)] = (int8_t)((int8_t)(byte << 4) >> 4);
+        q[code_offset_rk(n, k + 1, T)] = (int8_t)((int8_t)byte >> 4);
+      }
+  });
+  float *s = reinterpret_cast<float *>(b + L.s);
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t g = 0; g < L.G; ++g) s[g * L.Np + n] = in->wscales[n * L.G + g];
+  uint16_t *l2t = reinterpret_cast<uint16_t *>(b + L.l2t);
+  uint16_t *l1t = reinterpret_cast<uint16_t *>(b + L.l1t);
+  for (int64_t t = 0; t < r; ++t) {
+    for (int64_t n = 0; n < N; ++n) l2t[n * L.rp + t] = in->l2[t * N + n];
+    for (int64_t k = 0; k < K; ++k) l1t[t * K + k] = in->l1s[k * r + t];
+  }
+  std::memcpy(b + L.iota, in->inv_lambda, sizeof(float) * K);
+  std::memcpy(b + L.bias, in->bias, sizeof(float) * N);
+  return SVDQ_OK;
+}
+
+// ------------------------------------------------------------------- AWQ
+svdq_status_t awq_quantize(const uint16_t *W_fp16, int N, int K, uint8_t *q, uint16_t *s,
+                           uint16_t *z) {
+  const int G = K / kGroup;
+  for (int64_t i = 0; i < (int64_t)N * K; ++i)
+    if (!std::isfinite(f16_to_f32(W_fp16[i])))
+      return fail(SVDQ_ERR_NUMERICAL, "non-finite weight at %lld", (long long)i);
+  parallel_for(N, 64, [&](int64_t n0, int64_t n1) {
+    float w[kGroup];
+    for (int64_t n = n0; n < n1; ++n)
+      for (int g = 0; g < G; ++g) {
+        float wmax = -INFINITY, wmin = INFINITY;
+        for (int i = 0; i < kGroup; ++i) {
+          w[i] = f16_to_f32(W_fp16[n * K + g * kGroup + i]);
+          wmax = std::max(wmax, w[i]);
+          wmin = std::min(wmin, w[i]);
+        }
+        const float range = std::max(wmax - wmin, 1e-5f);
+        const uint16_t s16 = f32_to_f16(range / 15.0f);
+        const float sc = f16_to_f32(s16);
+        const float zf = std::min(15.0f, std::max(0.0f, std::rint(-wmin / sc)));
+        s[n * G + g] = s16;
+        z[n * G + g] = f32_to_f16(zf);
+        uint8_t *dst = q + n * (K / 2) + g * (kGroup / 2);
+        for (int j = 0; j < kGroup / 2; ++j) {
+          const float a = std::min(15.0f, std::max(0.0f, std::rint(w[2 * j] / sc) + zf));
+          const float c = std::min(15.0f, std::max(0.0f, std::rint(w[2 * j + 1] / sc) + zf));
+          dst[j] = (uint8_t)((uint8_t)a | ((uint8_t)c << 4));
+        }
+      }
+  });
+  return SVDQ_OK;
+}
+
+svdq_status_t awq_pack(const uint8_t *q, const uint16_t *s, const uint16_t *z, int N, int K,
+                       void *host_blob, size_t bytes) {
+  const AwqLayout L(N, K);
+  if ((int64_t)bytes < L.total)
+    return fail(SVDQ_ERR_WORKSPACE_TOO_SMALL, "blob needs %lld bytes, got %zu",
+                (long long)L.total, bytes);
+  uint8_t *b = static_cast<uint8_t *>(host_blob);
+  std::memset(b, 0, (size_t)L.total);
+  uint8_t *qd = b + L.q;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      const uint8_t byte = q[n * (K / 2) + k / 2];
+      const uint8_t code = (k & 1) ? (byte >> 4) : (byte & 0x0F);
+      qd[awq_code_byte(n, k, L.G)] |= (uint8_t)(code << awq_code_shift(k));
+    }
+  uint32_t *sz = reinterpret_cast<uint32_t *>(b + L.sz);
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t g = 0; g < L.G; ++g)
+      sz[g * L.Np + n] = (uint32_t)s[n * L.G + g] | ((uint32_t)z[n * L.G + g] << 16);
+  return SVDQ_OK;
+}
+
+}  // namespace svdq

@@ -1,0 +1,25 @@
+// Offline (host) preparation of an SVDQuant layer and of AWQ weights.
+#pragma once
+
+#include <cstdint>
+
+#include "svdq.h"
+
+namespace svdq {
+
+// Symmetric INT4 quantiser of one group of 64 float32 values (see the
+// definition in svdq_prepare_weights): codes in [-7, 7] and the fp32 scale.
+void quantize_group64(const float *v, int8_t *q, float *s);
+
+svdq_status_t prepare_weights(const uint16_t *W_bf16, int N, int K, const float *act_absmax,
+                              const uint16_t *bias_bf16, int rank, svdq_host_weights_t *out);
+
+svdq_status_t pack_device_weights(const svdq_host_weights_t *in, void *host_blob, size_t bytes);
+
+svdq_status_t awq_quantize(const uint16_t *W_fp16, int N, int K, uint8_t *q, uint16_t *s,
+                           uint16_t *z);
+
+svdq_status_t awq_pack(const uint8_t *q, const uint16_t *s, const uint16_t *z, int N, int K,
+                       void *host_blob, size_t bytes);
+
+}  // namespace svdq

@@ -1,0 +1,124 @@
+// Device data layouts shared by the host packer and the device kernels.
+// Everything here is constexpr so the same definitions serve both sides.
+//
+// INT4 codes live on the device one byte per code ("int8 containers") in a
+// matrix-core friendly tiling: rows (tokens for activations, output channels
+// for weights) are cut into tiles of 32; for every (group g of 64 input
+// channels, tile t) there is one 2048-byte block holding 32 codes for each of
+// the 64 lanes of a wavefront.  Lane l covers row l % 32 of the tile and half
+// h = l / 32 of the group; its code c (0..31) is input channel
+//     k = 64 g + 16 (c / 8) + 8 h + (c % 8).
+// Inside the block, code c of lane l sits at byte (c / 8) * 512 + l * 8 + c % 8,
+// so each 8-code chunk is one coalesced 512-byte line per wavefront.
+// Activations and weights use the identical assignment, which is all the
+// integer dot products need: a group's sum does not depend on how its 64
+// channels are ordered as long as both operands agree.
+#pragma once
+
+#include <stdint.h>
+
+namespace svdq {
+
+constexpr int kGroup = 64;
+constexpr int kTile = 32;
+constexpr int kPad = 256;                // M and N are padded to multiples of this
+constexpr int kLaneBytes = 32;           // one int8 per code, 32 codes per lane
+constexpr int kBlockBytes = 64 * kLaneBytes;
+constexpr int64_t kAlign = 256;
+
+constexpr int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+constexpr int rank_pad(int rank) { return rank <= 0 ? 0 : (int)round_up(rank, 32); }
+
+// input channel (within the group) of code c held by half h
+constexpr int lane_code_k(int h, int c) { return 16 * (c >> 3) + 8 * h + (c & 7); }
+
+// byte offset of code c of lane `lane` in block (g, t) of a code array with T tiles
+constexpr int64_t code_offset(int64_t g, int64_t t, int64_t T, int lane, int c) {
+  return (g * T + t) * kBlockBytes + (int64_t)(c >> 3) * 512 + (int64_t)lane * 8 + (c & 7);
+}
+
+// byte offset of the code for (row, k) in a code array with T tiles
+constexpr int64_t code_offset_rk(int64_t row, int64_t k, int64_t T) {
+  return code_offset(k / kGroup, row / kTile, T,
+                     (int)(row % kTile) + 32 * (int)((k % 16) / 8),
+                     8 * (int)((k % kGroup) / 16) + (int)(k % 8));
+}
+
+// Device weight blob of one prepared layer.
+struct WeightLayout {
+  int64_t N = 0, K = 0, rank = 0, Np = 0, rp = 0, G = 0;
+  int64_t q = 0, s = 0, l2t = 0, l1t = 0, iota = 0, bias = 0, total = 0;
+  constexpr WeightLayout(int64_t N_, int64_t K_, int64_t rank_)
+      : N(N_), K(K_), rank(rank_), Np(round_up(N_, kPad)), rp(rank_pad((int)rank_)),
+        G(K_ / kGroup) {
+    int64_t o = 0;
+    q = o;    o = round_up(o + Np * K, kAlign);          // int8 codes, tiled
+    s = o;    o = round_up(o + G * Np * 4, kAlign);      // fp32 scales [G][Np]
+    l2t = o;  o = round_up(o + Np * rp * 2, kAlign);     // bf16 L2^T [Np][rp]
+    l1t = o;  o = round_up(o + rp * K * 2, kAlign);      // bf16 L1s^T [rp][K]
+    iota = o; o = round_up(o + K * 4, kAlign);           // fp32 1/lambda [K]
+    bias = o; o = round_up(o + Np * 4, kAlign);          // fp32 [Np]
+    total = o;
+  }
+};
+
+// Groups of 64 handled by one quantiser workgroup: the K range is split
+// S ways so that enough workgroups exist to keep every CU streaming.
+constexpr int64_t k1_splits(int64_t Mp, int64_t G) {
+  const int64_t T = Mp / kTile;
+  int64_t best = 1;
+  for (int64_t s = 1; s <= G; ++s) {
+    if (G % s != 0 || G / s < 4) continue;
+    best = s;
+    if (T * s >= 512) return s;
+  }
+  return best;
+}
+
+// Device workspace of one forward call.
+struct WorkLayout {
+  int64_t M = 0, Mp = 0, K = 0, G = 0, rp = 0, S = 0;
+  int64_t qa = 0, sa = 0, d = 0, total = 0;
+  constexpr WorkLayout(int64_t M_, int64_t K_, int64_t rank_)
+      : M(M_), Mp(round_up(M_, kPad)), K(K_), G(K_ / kGroup), rp(rank_pad((int)rank_)),
+        S(k1_splits(round_up(M_, kPad), K_ / kGroup)) {
+    int64_t o = 0;
+    qa = o; o = round_up(o + Mp * K, kAlign);            // int8 codes, tiled
+    sa = o; o = round_up(o + G * Mp * 4, kAlign);        // fp32 scales [G][Mp]
+    d = o;  o = round_up(o + S * Mp * rp * 4, kAlign);   // fp32 partial X L1s [S][Mp][rp]
+    total = o;
+  }
+};
+
+// AWQ W4A16 device blob.  Output channels are cut into tiles of 16; for each
+// (tile, group of 64) there is a 512-byte block: lane l (column l % 16 of the
+// tile, quarter q = l / 16 of the group) holds the 16 codes of input channels
+// 64 g + 16 q + [0, 16) in 8 bytes.  Within each 4-byte word the low 16 bits
+// hold the codes of the even channels (nibble j = channel 2j) and the high
+// 16 bits those of the odd channels, so one shift and one mask turn a word
+// into pairs of fp16 operands.  Scales and zero points follow as one
+// 32-bit word per (group, column): fp16 scale | fp16 zero << 16, [G][N16].
+constexpr int kAwqTile = 16;
+constexpr int kAwqBlockBytes = 512;
+
+// byte offset and nibble shift of the code for (n, k)
+constexpr int64_t awq_code_byte(int64_t n, int64_t k, int64_t G) {
+  return ((n / kAwqTile) * G + k / kGroup) * kAwqBlockBytes +
+         ((n % kAwqTile) + 16 * ((k % kGroup) / 16)) * 8 + 4 * ((k % 16) / 8) +
+         (((k % 8) / 2) / 2) + 2 * (k % 2);
+}
+constexpr int awq_code_shift(int64_t k) { return 4 * (((k % 8) / 2) % 2); }
+
+struct AwqLayout {
+  int64_t N = 0, K = 0, G = 0, Np = 0;
+  int64_t q = 0, sz = 0, total = 0;
+  constexpr AwqLayout(int64_t N_, int64_t K_)
+      : N(N_), K(K_), G(K_ / kGroup), Np(round_up(N_, kAwqTile)) {
+    int64_t o = 0;
+    q = o;  o = round_up(o + Np * K / 2, kAlign);
+    sz = o; o = round_up(o + G * Np * 4, kAlign);
+    total = o;
+  }
+};
+
+}  // namespace svdq
