@@ -241,3 +241,24 @@ def test_no_device_is_reported():
     ws = S.workspace_bytes(64, 128, 128, 4)
     assert S._lib.svdq_linear_forward(ctypes.byref(w), FAKE, 64, FAKE, S.BF16, 0, FAKE, ws, None) == NODEV
     assert S._lib.svdq_gelu_tanh_bf16(FAKE, FAKE, 16, None) == NODEV
+
+
+def test_host_weights_accept_fortran_ordered_arrays():
+    """Arrays handed to the C side are made row-major first (an oracle SVD
+    factor is a transposed view, i.e. Fortran-ordered)."""
+    c = synth.linear_case("fo", 90, 8, 96, 128, 6, x_outlier_n=2, x_outlier_scale=20.0)
+    ref = O.prepare(c.W, c.calib_absmax(), c.bias, 6)
+    assert not ref["L1s"].flags.c_contiguous
+    from tests.gpu_util import host_from_oracle
+    hw = host_from_oracle(ref)
+    assert hw.l1s.flags.c_contiguous and hw.l2.flags.c_contiguous
+    blob = S.pack_device_weights(hw)
+    L = S.device_weights_bytes(96, 128, 6)
+    Np, rp, K = 256, 32, 128
+    off_l2t = Np * K + 2 * Np * 4
+    off_l1t = off_l2t + Np * rp * 2
+    l1t = blob[off_l1t: off_l1t + rp * K * 2].view(np.uint16).reshape(rp, K)
+    assert np.array_equal(l1t[:6].T, O.bf16_bits_of(ref["L1s"]))
+    l2t = blob[off_l2t: off_l2t + Np * rp * 2].view(np.uint16).reshape(Np, rp)
+    assert np.array_equal(l2t[:96, :6].T, O.bf16_bits_of(ref["L2b"]))
+    assert L == len(blob)

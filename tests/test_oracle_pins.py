@@ -456,6 +456,15 @@ def test_gelu_identities_and_library():
     assert OG.gelu_tanh(np.array([0.0]))[0] == 0.0
     ref = torch.nn.functional.gelu(torch.from_numpy(y), approximate="tanh").numpy()
     assert np.allclose(g, ref, rtol=1e-14, atol=1e-15)
+    # far negative tail: the printed form cancels, the logistic form keeps
+    # relative accuracy; check against a 50-digit evaluation
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    for yv in (-6.0, -8.5, -10.0):
+        yd = Decimal(yv)
+        u = Decimal(2).sqrt() / Decimal(math.pi).sqrt() * (yd + Decimal("0.044715") * yd ** 3)
+        exact = float(yd / (1 + (-2 * u).exp()))
+        assert math.isclose(OG.gelu_tanh(np.array([yv]))[0], exact, rel_tol=1e-12)
     erf_form = 0.5 * y * (1.0 + scipy.special.erf(y / math.sqrt(2.0)))
     assert np.max(np.abs(g - erf_form)) < 1e-3
     gb = OG.gelu_tanh_bf16(y)

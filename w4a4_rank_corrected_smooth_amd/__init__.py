@@ -133,6 +133,15 @@ class PreparedHost:
     wscales: np.ndarray      # float32 [N, K/64]
     bias: np.ndarray         # float32 [N]
 
+    def __post_init__(self):
+        # the C side reads row-major buffers of exactly these types
+        self.inv_lambda = np.ascontiguousarray(self.inv_lambda, dtype=np.float32)
+        self.l1s = np.ascontiguousarray(self.l1s, dtype=np.uint16)
+        self.l2 = np.ascontiguousarray(self.l2, dtype=np.uint16)
+        self.qweight = np.ascontiguousarray(self.qweight, dtype=np.uint8)
+        self.wscales = np.ascontiguousarray(self.wscales, dtype=np.float32)
+        self.bias = np.ascontiguousarray(self.bias, dtype=np.float32)
+
     def as_struct(self) -> HostWeights:
         return HostWeights(self.N, self.K, self.rank, 64, _ptr(self.inv_lambda),
                            _ptr(self.l1s) if self.rank else None,

@@ -43,11 +43,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ v8bf as_v8bf(uint4 u) { return __builtin_bit_cast(v8bf, u); }
 
+// tanh-form GELU, 0.5 y (1 + tanh u) with u = sqrt(2/pi) (y + 0.044715 y^3),
+// evaluated as y / (1 + exp(-2u)) (the same function) so that large negative
+// y keep their relative accuracy instead of cancelling in 1 + tanh(u).  The
+// hardware exp2 and reciprocal (about 1 ulp of fp32 each) are far inside the
+// half-ulp of the bf16 result; exp overflow gives 1/inf = 0, the right limit.
 __device__ __forceinline__ float gelu_tanh_f32(float y) {
   const float k0 = 0.7978845608028654f;   // sqrt(2/pi)
   const float k1 = 0.044715f;
   const float u = k0 * (y + k1 * y * y * y);
-  return 0.5f * y * (1.0f + tanhf(u));
+  return y * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
 }
 
 // ======================================================================= K1
