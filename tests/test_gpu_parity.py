@@ -146,12 +146,14 @@ def test_fused_gelu_epilogue(S):
 def test_gelu_kernel_within_one_bf16_ulp(S, n):
     rng = np.random.default_rng(n)
     x = synth.f32_to_bf16_bits((rng.standard_normal(n) * 3).astype(np.float32))
-    x[:6] = synth.f32_to_bf16_bits(np.array([0.0, -0.0, 20.0, -20.0, -7.5, -9.75], np.float32))
+    x[:7] = synth.f32_to_bf16_bits(np.array([0.0, -0.0, 20.0, -20.0, -7.5, -9.75, -10.0], np.float32))
     announce(f"gelu n={n}")
     y = S.gelu_tanh_bf16(bf16_to_device(x))
     got = to_f64(y)
     ref = OG.gelu_tanh_bf16(O.bf16_values(x))
-    # one bf16 ulp of the reference (the subnormal quantum is 2^-133)
+    # one bf16 ulp of the reference; results smaller than 2^-100 in magnitude
+    # (inputs below about -9.8) may flush to zero in the fp32 exp/reciprocal
     ulp = np.exp2(np.maximum(np.floor(np.log2(np.maximum(np.abs(ref), 1e-300))) - 7, -133))
-    assert np.all(np.abs(got - ref) <= ulp)
+    tiny = (np.abs(ref) < 2.0 ** -100) & (np.abs(got) < 2.0 ** -100)
+    assert np.all((np.abs(got - ref) <= ulp) | tiny)
     assert np.mean(got == ref) > 0.99
