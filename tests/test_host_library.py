@@ -143,26 +143,40 @@ def test_singular_values_of_a_tall_and_a_wide_matrix():
 
 
 # ------------------------------------------------------------- device packer
+E2M3_INT = {0: 0, 8: 1, 16: 2, 20: 3, 24: 4, 26: 5, 28: 6, 30: 7}
+
+
+def _e2m3_to_int(v):
+    return -E2M3_INT[v & 31] if v & 32 else E2M3_INT[v & 31]
+
+
 def test_device_blob_layout():
+    """Weight codes sit where the documented tiling says, as FP6 E2M3 fields:
+    block (g, tile) of 1536 bytes; lane = row % 32 + 32 * half; code c at
+    bits 6c of the lane's 192-bit string, stored as three 8-byte pairs at
+    512 j + 8 lane."""
     c = synth.linear_case("pk", 80, 8, 100, 192, 5, x_outlier_n=2, x_outlier_scale=20.0)
     hw = S.prepare_weights(c.W, c.calib_absmax(), c.bias, 5)
     blob = S.pack_device_weights(hw)
     N, K, G = 100, 192, 3
     Np = 256
-    codes = O.unpack_int4(hw.qweight)
-    qdev = blob[: Np * K].view(np.int8)
     T = Np // 32
+    codes = O.unpack_int4(hw.qweight)
+    qbytes = Np * K * 3 // 4
+    qdev = blob[:qbytes]
     for n in range(0, N, 7):
         for k in range(K):
             g, kk = divmod(k, 64)
             h = (kk % 16) // 8
             cidx = 8 * (kk // 16) + kk % 8
             lane = n % 32 + 32 * h
-            off = (g * T + n // 32) * 2048 + (cidx // 8) * 512 + lane * 8 + cidx % 8
-            assert qdev[off] == codes[n, k]
+            base = (g * T + n // 32) * 1536 + lane * 8
+            words = b"".join(bytes(qdev[base + 512 * j: base + 512 * j + 8]) for j in range(3))
+            bits = int.from_bytes(words, "little")
+            assert _e2m3_to_int((bits >> (6 * cidx)) & 63) == codes[n, k]
     # padded rows hold zero codes
-    assert not np.any(qdev.reshape(G, T, 2048)[:, 4:, :])
-    s_off = Np * K
+    assert not np.any(qdev.reshape(G, T, 1536)[:, 4:, :])
+    s_off = (qbytes + 255) // 256 * 256
     sdev = blob[s_off: s_off + G * Np * 4].view(np.float32).reshape(G, Np)
     assert np.array_equal(sdev[:, :N].T, hw.wscales) and not np.any(sdev[:, N:])
 
@@ -255,7 +269,7 @@ def test_host_weights_accept_fortran_ordered_arrays():
     blob = S.pack_device_weights(hw)
     L = S.device_weights_bytes(96, 128, 6)
     Np, rp, K = 256, 32, 128
-    off_l2t = Np * K + 2 * Np * 4
+    off_l2t = Np * K * 3 // 4 + 2 * Np * 4
     off_l1t = off_l2t + Np * rp * 2
     l1t = blob[off_l1t: off_l1t + rp * K * 2].view(np.uint16).reshape(rp, K)
     assert np.array_equal(l1t[:6].T, O.bf16_bits_of(ref["L1s"]))

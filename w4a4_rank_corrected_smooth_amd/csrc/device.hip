@@ -29,6 +29,9 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef unsigned v6u __attribute__((ext_vector_type(6)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v32f __attribute__((ext_vector_type(32)));
 
 // ------------------------------------------------------------ small helpers
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -60,7 +63,8 @@ __device__ __forceinline__ float gelu_tanh_f32(float y) {
 // of a wavefront owns row l % 32 and half h = l / 32 of each group: 32 bf16
 // values read as four 16-byte loads.  The four wavefronts interleave groups.
 // Per group:  x_hat = fl32(x * iota);  a = max |x_hat| over 64 (two lanes);
-// s = a / 7, inv = 7 / a (correctly rounded), q = clamp(rint(x_hat inv), +-7).
+// s = a / 7, inv = 7 / a (correctly rounded), q = clamp(rint(x_hat inv), +-7),
+// stored as fp6 E2M3 (exact for these integers).
 // The raw bf16 values also feed a 32x32x16 bf16 MFMA against L1s^T, giving
 // the low-rank down-projection; the four wavefronts' partial products are
 // summed through LDS and written as this split's partial D.
@@ -68,7 +72,7 @@ template <int TB>   // rank_pad / 32
 __global__ __launch_bounds__(256) void k1_quantize_lowrank_down(
     const uint16_t *__restrict__ X, int M, int K, int Mp, int S,
     const float *__restrict__ iota, const uint16_t *__restrict__ l1t,
-    int8_t *__restrict__ qa, float *__restrict__ sa, float *__restrict__ dpart) {
+    uint8_t *__restrict__ qa, float *__restrict__ sa, float *__restrict__ dpart) {
   const int t = blockIdx.x, s = blockIdx.y;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int G = K / kGroup, Gs = G / S, T = Mp / kTile;
@@ -108,20 +112,22 @@ __global__ __launch_bounds__(256) void k1_quantize_lowrank_down(
       sc = a / 7.0f;
       inv = 7.0f / a;
     }
-    int8_t *qp = qa + code_offset(g, t, T, lane, 0);
+    // codes as fp6 E2M3: the hardware packer interleaves its two 16-value
+    // inputs (field 2i from the first, 2i+1 from the second), so even and odd
+    // elements go in to get element order 0..31 at bits 6c.
+    v16f ev, od;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float qf = rintf(__fmul_rn(xh[8 * j + e], inv));
-        qf = fminf(7.0f, fmaxf(-7.0f, qf));
-        const uint32_t byte = (uint32_t)(int32_t)qf & 0xFFu;
-        if (e < 4) lo |= byte << (8 * e);
-        else hi |= byte << (8 * (e - 4));
-      }
-      *reinterpret_cast<uint2 *>(qp + 512 * j) = make_uint2(lo, hi);
+    for (int c = 0; c < 16; ++c) {
+      float q0 = rintf(__fmul_rn(xh[2 * c], inv));
+      float q1 = rintf(__fmul_rn(xh[2 * c + 1], inv));
+      ev[c] = fminf(7.0f, fmaxf(-7.0f, q0));
+      od[c] = fminf(7.0f, fmaxf(-7.0f, q1));
     }
+    const v6u packed = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+    uint8_t *qp = qa + pair_offset(g, t, T, lane, 0);
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      *reinterpret_cast<uint2 *>(qp + 512 * j) = make_uint2(packed[2 * j], packed[2 * j + 1]);
     if (h == 0) sa[(int64_t)g * Mp + row] = sc;
     if constexpr (TB > 0) {
 #pragma unroll
@@ -155,94 +161,248 @@ __global__ __launch_bounds__(256) void k1_quantize_lowrank_down(
   }
 }
 
+// Global -> LDS copy of 16 bytes per lane by the load unit
+// (global_load_lds_dwordx4): lane i writes LDS address lds_base + 16 i.
+// lds_base must be uniform across the wavefront.  Written as inline asm so
+// that the copy's completion is tracked by the caller's own vmcnt waits
+// (the compiler would otherwise wait for every copy before any LDS read).
+// The asm has no register outputs; M0 is set and used inside the block.
+__device__ __forceinline__ void lds_dma16(const void *gsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gsrc), "s"(lds_base) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void vmcnt_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ void vmcnt_wait0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ======================================================================= K2
-// Output tile 128 x 128 per workgroup, 64 x 64 per wavefront (2 x 2 MFMA tiles
-// of 32 x 32).  For each group g: the int32 group sums P of every 32 x 32 tile
-// come from two v_mfma_i32_32x32x32_i8 (K = 32 each) on the int8 codes; then
-// acc += (sA[m,g] * sW[n,g]) * float(P) in fp32.  The epilogue adds the
-// low-rank up-projection D L2 on bf16 MFMA (D split into a bf16 high part and
-// a bf16 remainder, so the product keeps ~16 bits of D), the bias, the
-// optional GELU, and stores bf16 or fp32.
-// MODE_SUMS stores the raw int32 P of each group for a window instead.
+// INT4 x INT4 group GEMM with per-group fp32 scaling.
+//
+// Workgroup: 8 wavefronts, output tile 256 x 128; wavefront tile 64 x 64
+// (2 x 2 MFMA tiles of 32 x 32).  One pipeline stage holds two groups of 64
+// input channels (A codes, B codes, their fp32 scales) in LDS, double
+// buffered: the next stage's global loads are issued before the current
+// stage is consumed and written to LDS after it.
+//
+// Per 32 x 32 tile and group:
+//   P  = v_mfma_scale_f32_32x32x64_f8f6f4 on fp6 codes (unit block scales):
+//        the exact int32 group sums, delivered as fp32 (|P| <= 3136)
+//   S  = v_mfma_f32_32x32x1_2b_f32: the outer product sA[m,g] sW[n,g] for
+//        two groups at once (one IEEE fp32 product per element)
+//   acc = fma(P, S, acc)                  (the only VALU work per element)
+// The epilogue adds the low-rank up-projection D L2 on bf16 MFMA (D split
+// into a bf16 high part and a bf16 remainder), the bias, the optional GELU,
+// and stores bf16 or fp32.  MODE_SUMS stores P for a window instead.
+//
+// Tile order: workgroups are dealt round-robin to the 8 XCDs, so block id b
+// runs on XCD b % 8; each XCD is given a contiguous range of tiles, walked
+// four tile-rows at a time, so the A and B panels its CUs share stay in its
+// L2.
 enum { MODE_FWD = 0, MODE_SUMS = 1 };
 
 struct K2Args {
-  const int8_t *qa; const float *sa; const float *dpart; int S, M, Mp;
-  const int8_t *qw; const float *sw; const uint16_t *l2t; const float *bias;
+  const uint8_t *qa; const float *sa; const float *dpart; int S, M, Mp;
+  const uint8_t *qw; const float *sw; const uint16_t *l2t; const float *bias;
   int N, Np, K, rp;
   void *Y;
-  int32_t *P; int m0, mcount, n0, ncount, tile_m0, tile_n0;
+  int32_t *P; int m0, mcount, n0, ncount;
+  int tile_m0, tile_n0, TM, TN;     // tile grid (units of 256 x 128)
 };
 
-__device__ __forceinline__ v4i load_frag(const int8_t *blk, int lane, int half) {
-  const uint2 c0 = *reinterpret_cast<const uint2 *>(blk + 1024 * half + lane * 8);
-  const uint2 c1 = *reinterpret_cast<const uint2 *>(blk + 1024 * half + 512 + lane * 8);
-  return v4i{(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y};
+namespace k2c {
+constexpr int BM = 256, BN = 128, THREADS = 512;
+constexpr int A_BLK = BM / kTile, B_BLK = BN / kTile;
+constexpr int A_BYTES = A_BLK * kBlockBytes;     // one group per stage
+constexpr int B_BYTES = B_BLK * kBlockBytes;
+constexpr int SA_BYTES = BM * 4, SW_BYTES = BN * 4;
+constexpr int STAGE_USED = A_BYTES + B_BYTES + SA_BYTES + SW_BYTES;   // 19968
+constexpr int UNITS = STAGE_USED / 16;                                 // 1248
+constexpr int WAVE_LOADS = (UNITS + 63) / 64;                          // 20
+constexpr int STAGE = WAVE_LOADS * 64 * 16;                            // 20480, padded
+constexpr int NBUF = 4;                                                // stages in LDS
+constexpr int GM = 4;             // tile-rows walked together on one XCD
+static_assert(STAGE_USED % 16 == 0, "stage must be whole 16-byte units");
+static_assert(WAVE_LOADS > 16 && WAVE_LOADS <= 24, "copy schedule below: 3 loads for waves 0-3, 2 for 4-7");
+}  // namespace k2c
+
+// Stage layout in LDS (one group of 64 input channels):
+//   A codes [8 blocks][1536] | B codes [4 blocks][1536] | sA [256] | sW [128]
+// Unit u (16 bytes) of the stage sits at LDS byte 16 u; its global source:
+__device__ __forceinline__ const uint4 *k2_unit_src(const K2Args &p, int g, int u, int bm, int bn,
+                                                   int Ta, int Tw) {
+  using namespace k2c;
+  int off = u * 16;
+  if (off < A_BYTES)
+    return reinterpret_cast<const uint4 *>(p.qa + ((int64_t)g * Ta + bm / kTile) * kBlockBytes + off);
+  off -= A_BYTES;
+  if (off < B_BYTES)
+    return reinterpret_cast<const uint4 *>(p.qw + ((int64_t)g * Tw + bn / kTile) * kBlockBytes + off);
+  off -= B_BYTES;
+  if (off < SA_BYTES)
+    return reinterpret_cast<const uint4 *>(p.sa + (int64_t)g * p.Mp + bm + off / 4);
+  off -= SA_BYTES;
+  return reinterpret_cast<const uint4 *>(p.sw + (int64_t)g * p.Np + bn + off / 4);
+}
+
+__device__ __forceinline__ v8i k2_frag(const uint8_t *blk, int lane) {
+  const uint2 w0 = *reinterpret_cast<const uint2 *>(blk + lane * 8);
+  const uint2 w1 = *reinterpret_cast<const uint2 *>(blk + 512 + lane * 8);
+  const uint2 w2 = *reinterpret_cast<const uint2 *>(blk + 1024 + lane * 8);
+  return v8i{(int)w0.x, (int)w0.y, (int)w1.x, (int)w1.y, (int)w2.x, (int)w2.y, 0, 0};
 }
 
 template <int MODE, int EPI, bool OUT_F32>
-__global__ __launch_bounds__(256) void k2_w4a4_gemm(K2Args p) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int bm = p.tile_m0 + blockIdx.y * 128, bn = p.tile_n0 + blockIdx.x * 128;
-  const int wm = bm + (w >> 1) * 64, wn = bn + (w & 1) * 64;
-  const int G = p.K / kGroup, Ta = p.Mp / kTile, Tw = p.Np / kTile;
+__global__ __launch_bounds__(512) void k2_w4a4_gemm(K2Args p) {
+  using namespace k2c;
+  // ---- tile of this workgroup (XCD-aware, grouped)
+  const int T = p.TM * p.TN;
+  const int per_xcd = (T + 7) / 8;
+  const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (L >= T) return;
+  const int band = L / (GM * p.TN);
+  const int first_m = band * GM;
+  const int gm = min(GM, p.TM - first_m);
+  const int within = L - band * GM * p.TN;
+  const int tm = first_m + within % gm, tn = within / gm;
+  const int bm = p.tile_m0 + tm * BM, bn = p.tile_n0 + tn * BN;
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * STAGE];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int wmi = w >> 1, wni = w & 1;
+  const int wm = bm + 64 * wmi, wn = bn + 64 * wni;
+  const int G = p.K / kGroup;
+  const int Ta = p.Mp / kTile, Tw = p.Np / kTile;
   const int hl = lane >> 5, ln = lane & 31;
+
   v16f acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
 
-  for (int g = 0; g < G; ++g) {
-    v4i a[2][2], b[2][2];
+  // Copy schedule: a stage is 20 wavefront-loads of 64 x 16 bytes; wave w
+  // issues loads w, w + 8 and (waves 0-3 only) w + 16, every lane active,
+  // so each wavefront issues the same number of copies per stage and the
+  // vmcnt waits below count exactly.  The last 32 units are padding
+  // (source: the first codes of this panel, destination: the pad).
+  const int wu = __builtin_amdgcn_readfirstlane(w);      // wavefront index, scalar
+  const int nload = wu < WAVE_LOADS - 16 ? 3 : 2;
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
+  // per copy slot: source of group 0 and the byte stride from one group to
+  // the next (A and B panels advance by a row of blocks, the scales by a row
+  // of the [G][Mp] / [G][Np] arrays); padding lanes re-read the A panel
+  const uint8_t *src0[3];
+  int64_t sstride[3];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int8_t *blk = p.qa + ((int64_t)g * Ta + wm / kTile + i) * kBlockBytes;
-      a[i][0] = load_frag(blk, lane, 0);
-      a[i][1] = load_frag(blk, lane, 1);
+  for (int r = 0; r < 3; ++r) {
+    const int u = 64 * (wu + 8 * r) + lane;
+    const int off = u * 16;
+    if (u >= UNITS || off < A_BYTES) {
+      src0[r] = p.qa + (int64_t)(bm / kTile) * kBlockBytes + (u < UNITS ? off : 0);
+      sstride[r] = (int64_t)Ta * kBlockBytes;
+    } else if (off < A_BYTES + B_BYTES) {
+      src0[r] = p.qw + (int64_t)(bn / kTile) * kBlockBytes + (off - A_BYTES);
+      sstride[r] = (int64_t)Tw * kBlockBytes;
+    } else if (off < A_BYTES + B_BYTES + SA_BYTES) {
+      src0[r] = reinterpret_cast<const uint8_t *>(p.sa + bm) + (off - A_BYTES - B_BYTES);
+      sstride[r] = (int64_t)p.Mp * 4;
+    } else {
+      src0[r] = reinterpret_cast<const uint8_t *>(p.sw + bn) + (off - A_BYTES - B_BYTES - SA_BYTES);
+      sstride[r] = (int64_t)p.Np * 4;
     }
+  }
+  auto fetch = [&](int g) {
+    const uint32_t buf = smem_lds + (uint32_t)((g % NBUF) * STAGE) + (uint32_t)(wu * 64 * 16);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int8_t *blk = p.qw + ((int64_t)g * Tw + wn / kTile + j) * kBlockBytes;
-      b[j][0] = load_frag(blk, lane, 0);
-      b[j][1] = load_frag(blk, lane, 1);
+    for (int r = 0; r < 3; ++r)
+      if (r < nload) lds_dma16(src0[r] + g * sstride[r], buf + (uint32_t)(r * 8 * 64 * 16));
+  };
+  // wait until at most `later` stages issued after the one needed are in flight
+  auto wait_stage = [&](int later) {
+    if (MODE == MODE_SUMS) { vmcnt_wait0(); return; }   // P stores also count
+    if (nload == 3) {
+      if (later >= 2) vmcnt_wait<6>(); else if (later == 1) vmcnt_wait<3>(); else vmcnt_wait0();
+    } else {
+      if (later >= 2) vmcnt_wait<4>(); else if (later == 1) vmcnt_wait<2>(); else vmcnt_wait0();
     }
-    float sw[2];
-    float4 sa[2][4];
-    if constexpr (MODE == MODE_FWD) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) sw[j] = p.sw[(int64_t)g * p.Np + wn + 32 * j + ln];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          sa[i][q] = *reinterpret_cast<const float4 *>(p.sa + (int64_t)g * p.Mp + wm + 32 * i +
-                                                       8 * q + 4 * hl);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
+  };
+
+  // Operands of one group as a wavefront holds them in registers.
+  struct Frags { v8i a0, a1, b0, b1; float sa0, sa1, sw; };
+  auto read_stage = [&](int g) {
+    const uint8_t *st = smem + (g % NBUF) * STAGE;
+    const float *lsa = reinterpret_cast<const float *>(st + A_BYTES + B_BYTES);
+    const float *lsw = reinterpret_cast<const float *>(st + A_BYTES + B_BYTES + SA_BYTES);
+    Frags f;
+    f.b0 = k2_frag(st + A_BYTES + (2 * wni) * kBlockBytes, lane);
+    f.b1 = k2_frag(st + A_BYTES + (2 * wni + 1) * kBlockBytes, lane);
+    f.a0 = k2_frag(st + (2 * wmi) * kBlockBytes, lane);
+    f.a1 = k2_frag(st + (2 * wmi + 1) * kBlockBytes, lane);
+    // outer-product operands: block 0 (lanes 0-31) pairs a row tile with
+    // column tile 0, block 1 (lanes 32-63) with column tile 1
+    f.sw = lsw[64 * wni + 32 * hl + ln];
+    f.sa0 = lsa[64 * wmi + ln];
+    f.sa1 = lsa[64 * wmi + 32 + ln];
+    return f;
+  };
+  Frags f;
+
+  // Software pipeline over (group, row tile).  Each wavefront keeps the
+  // products of one row tile in flight while it applies the scales of the
+  // other, so its own matrix and FMA work overlap:
+  //   A. matrix work of row tile 1, group g   |  FMAs of row tile 0, group g
+  //   B. wait for stage g+1, barrier (buffer (g-1) % NBUF is then free),
+  //      read stage g+1 into f, request stage g+NBUF-1
+  //   C. matrix work of row tile 0, group g+1 |  FMAs of row tile 1, group g
+  auto mm_row = [&](const v8i &a, float sa, v16f &P0, v16f &P1, v32f &Sc) {
+    P0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, f.b0, v16f{}, 2, 2, 0, 127, 0, 127);
+    P1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, f.b1, v16f{}, 2, 2, 0, 127, 0, 127);
+    if constexpr (MODE == MODE_FWD) Sc = __builtin_amdgcn_mfma_f32_32x32x1f32(sa, f.sw, v32f{}, 0, 0, 0);
+  };
+  auto apply_row = [&](int i, int g, const v16f &P0, const v16f &P1, const v32f &Sc) {
+    if constexpr (MODE == MODE_SUMS) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        v16i P = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i][0], b[j][0], v16i{}, 0, 0, 0);
-        P = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i][1], b[j][1], P, 0, 0, 0);
-        if constexpr (MODE == MODE_SUMS) {
-          const int n = wn + 32 * j + ln;
+        const int n = wn + 32 * j + ln;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int m = wm + 32 * i + 8 * (e >> 2) + 4 * hl + (e & 3);
-            if (m >= p.m0 && m < p.m0 + p.mcount && n >= p.n0 && n < p.n0 + p.ncount)
-              p.P[((int64_t)(m - p.m0) * p.ncount + (n - p.n0)) * G + g] = P[e];
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float4 s4 = sa[i][e >> 2];
-            const float sae = (e & 3) == 0 ? s4.x : (e & 3) == 1 ? s4.y : (e & 3) == 2 ? s4.z : s4.w;
-            acc[i][j][e] = __builtin_fmaf((float)P[e], __fmul_rn(sae, sw[j]), acc[i][j][e]);
-          }
+        for (int e = 0; e < 16; ++e) {
+          const int m = wm + 32 * i + 8 * (e >> 2) + 4 * hl + (e & 3);
+          const float v = j ? P1[e] : P0[e];
+          if (m >= p.m0 && m < p.m0 + p.mcount && n >= p.n0 && n < p.n0 + p.ncount)
+            p.P[((int64_t)(m - p.m0) * p.ncount + (n - p.n0)) * G + g] = (int32_t)v;
         }
       }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        acc[i][0][e] = __builtin_fmaf(P0[e], Sc[e], acc[i][0][e]);
+        acc[i][1][e] = __builtin_fmaf(P1[e], Sc[16 + e], acc[i][1][e]);
+      }
+    }
+  };
+
+  for (int g = 0; g < NBUF - 1 && g < G; ++g) fetch(g);
+  wait_stage(min(NBUF - 2, G - 1));
+  __syncthreads();
+  f = read_stage(0);
+  v16f P00, P01, P10, P11;
+  v32f S0, S1;
+  mm_row(f.a0, f.sa0, P00, P01, S0);
+  for (int g = 0; g < G; ++g) {
+    mm_row(f.a1, f.sa1, P10, P11, S1);                      // A
+    apply_row(0, g, P00, P01, S0);
+    if (g + 1 < G) {                                        // B
+      wait_stage(min(NBUF - 3, G - 2 - g));
+      __syncthreads();
+      f = read_stage(g + 1);
+      if (g + NBUF - 1 < G) fetch(g + NBUF - 1);
+    }
+    mm_row(f.a0, f.sa0, P00, P01, S0);                      // C (unused after the last group)
+    apply_row(1, g, P10, P11, S1);
   }
+
   if constexpr (MODE == MODE_FWD) {
     // low-rank up-projection: acc += D L2, D summed over the K1 splits
     for (int c = 0; c < p.rp / 16; ++c) {
@@ -277,24 +437,60 @@ __global__ __launch_bounds__(256) void k2_w4a4_gemm(K2Args p) {
         }
       }
     }
+    // Bias (+ GELU), then the wavefront's 64 x 64 tile goes out through its
+    // own 8 KB of LDS one 32-row half at a time, so global stores are whole
+    // 16-byte vectors along a row instead of 2- or 4-byte scattered stores.
+    __syncthreads();                    // every wavefront is done with the stages
+    uint8_t *wbuf = smem + w * 8192;
+    constexpr int ES = OUT_F32 ? 4 : 2;          // bytes per output element
+    constexpr int VE = 16 / ES;                  // elements per 16-byte vector
+    constexpr int LPR = 64 / VE;                 // lanes per 64-wide row
+    const bool vec_ok = (p.N % VE) == 0;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = wn + 32 * j + ln;
-      const float bj = p.bias[n];
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j) {
+        const float bj = p.bias[wn + 32 * j + ln];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int m = wm + 32 * i + 8 * (e >> 2) + 4 * hl + (e & 3);
+          const int r = 8 * (e >> 2) + 4 * hl + (e & 3);
           float y = acc[i][j][e] + bj;
           if constexpr (EPI == SVDQ_EPILOGUE_GELU_TANH) y = gelu_tanh_f32(y);
-          if (m < p.M && n < p.N) {
-            if constexpr (OUT_F32)
-              reinterpret_cast<float *>(p.Y)[(int64_t)m * p.N + n] = y;
-            else
-              reinterpret_cast<uint16_t *>(p.Y)[(int64_t)m * p.N + n] = (uint16_t)f32_to_bf16_rne(y);
+          if constexpr (OUT_F32)
+            reinterpret_cast<float *>(wbuf)[r * 64 + 32 * j + ln] = y;
+          else
+            reinterpret_cast<uint16_t *>(wbuf)[r * 64 + 32 * j + ln] = (uint16_t)f32_to_bf16_rne(y);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int q = 0; q < 32 * LPR / 64; ++q) {
+        const int r = q * (64 / LPR) + lane / LPR;
+        const int c = (lane % LPR) * VE;
+        const int m = wm + 32 * i + r, n = wn + c;
+        const uint4 v = *reinterpret_cast<const uint4 *>(wbuf + (r * 64 + c) * ES);
+        if (m < p.M) {
+          uint8_t *dst = reinterpret_cast<uint8_t *>(p.Y) + ((int64_t)m * p.N + n) * ES;
+          if (vec_ok && n + VE <= p.N) {
+            *reinterpret_cast<uint4 *>(dst) = v;
+          } else {
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int t = 0; t < VE; ++t)
+              if (n + t < p.N) {
+                if constexpr (OUT_F32)
+                  reinterpret_cast<float *>(dst)[t] = __uint_as_float(wv[t]);
+                else
+                  reinterpret_cast<uint16_t *>(dst)[t] = (uint16_t)(wv[t >> 1] >> (16 * (t & 1)));
+              }
           }
         }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
 }
@@ -390,15 +586,28 @@ __global__ __launch_bounds__(256) void gelu_tanh_bf16_kernel(const uint16_t *__r
 }
 
 // ============================================================ inspection
-__global__ void canon_codes_kernel(const int8_t *__restrict__ qa, int M, int K, int T,
+__global__ void canon_codes_kernel(const uint8_t *__restrict__ qa, int M, int K, int T,
                                    uint8_t *__restrict__ out) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nb = (int64_t)M * (K / 2);
   if (idx >= nb) return;
   const int64_t m = idx / (K / 2), kb = idx % (K / 2);
-  const int8_t c0 = qa[code_offset_rk(m, 2 * kb, T)];
-  const int8_t c1 = qa[code_offset_rk(m, 2 * kb + 1, T)];
-  out[idx] = (uint8_t)(((uint8_t)c0 & 0x0F) | (((uint8_t)c1 & 0x0F) << 4));
+  int code[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const CodePos cp = code_pos(m, 2 * kb + u);
+    const uint32_t *wp = reinterpret_cast<const uint32_t *>(qa + pair_offset(cp.g, cp.t, T, cp.lane, 0));
+    // the lane's words 0..5 live as pairs 512 bytes apart
+    const int bit = 6 * cp.c, wi = bit / 32, sh = bit % 32;
+    const uint32_t w0 = wp[(wi / 2) * 128 + (wi & 1)];
+    uint32_t v = w0 >> sh;
+    if (sh > 26) {
+      const int wj = wi + 1;
+      v |= wp[(wj / 2) * 128 + (wj & 1)] << (32 - sh);
+    }
+    code[u] = int_of_e2m3(v & 63u);
+  }
+  out[idx] = (uint8_t)(((uint32_t)code[0] & 0x0Fu) | (((uint32_t)code[1] & 0x0Fu) << 4));
 }
 
 __global__ void canon_scales_kernel(const float *__restrict__ sa, int M, int Mp, int G,
@@ -476,7 +685,7 @@ svdq_status_t launch_k1(const WeightLayout &L, const WorkLayout &Wl, const svdq_
   const uint16_t *x = static_cast<const uint16_t *>(X);
   const float *iota = reinterpret_cast<const float *>(blob + L.iota);
   const uint16_t *l1t = reinterpret_cast<const uint16_t *>(blob + L.l1t);
-  int8_t *qa = reinterpret_cast<int8_t *>(ws + Wl.qa);
+  uint8_t *qa = ws + Wl.qa;
   float *sa = reinterpret_cast<float *>(ws + Wl.sa);
   float *dp = reinterpret_cast<float *>(ws + Wl.d);
   const int K = w->K, Mp = (int)Wl.Mp, S = (int)Wl.S;
@@ -498,13 +707,13 @@ K2Args make_k2_args(const WeightLayout &L, const WorkLayout &Wl, const svdq_weig
                     const uint8_t *ws) {
   const uint8_t *blob = static_cast<const uint8_t *>(w->blob);
   K2Args a{};
-  a.qa = reinterpret_cast<const int8_t *>(ws + Wl.qa);
+  a.qa = ws + Wl.qa;
   a.sa = reinterpret_cast<const float *>(ws + Wl.sa);
   a.dpart = reinterpret_cast<const float *>(ws + Wl.d);
   a.S = (int)Wl.S;
   a.M = M;
   a.Mp = (int)Wl.Mp;
-  a.qw = reinterpret_cast<const int8_t *>(blob + L.q);
+  a.qw = blob + L.q;
   a.sw = reinterpret_cast<const float *>(blob + L.s);
   a.l2t = reinterpret_cast<const uint16_t *>(blob + L.l2t);
   a.bias = reinterpret_cast<const float *>(blob + L.bias);
@@ -527,8 +736,7 @@ static svdq_status_t validate_forward(const svdq_weights_t *w, int M, size_t ws_
   if (st != SVDQ_OK) return st;
   if (!workspace) return fail(SVDQ_ERR_INVALID_ARGUMENT, "%s: NULL workspace", who);
   if (!aligned16(workspace)) return fail(SVDQ_ERR_INVALID_ARGUMENT, "%s: misaligned workspace", who);
-  // grid.y of the GEMM counts 128-row tiles and is limited to 65535
-  if (M < 1 || M > 65535 * 128 || (int64_t)M * w->K > ((int64_t)1 << 31))
+  if (M < 1 || (int64_t)M * w->K > ((int64_t)1 << 31))
     return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "%s: M=%d", who, M);
   const WorkLayout Wl(M, w->K, w->rank);
   if ((int64_t)ws_bytes < Wl.total)
@@ -554,17 +762,20 @@ static svdq_status_t launch_k2(const svdq_weights_t *w, int M, void *Y, svdq_dty
   const WorkLayout Wl(M, w->K, w->rank);
   K2Args a = make_k2_args(L, Wl, w, M, static_cast<const uint8_t *>(workspace));
   a.Y = Y;
-  const dim3 grid((unsigned)((w->N + 127) / 128), (unsigned)((M + 127) / 128));
+  a.TM = (M + k2c::BM - 1) / k2c::BM;
+  a.TN = (w->N + k2c::BN - 1) / k2c::BN;
+  const dim3 grid((unsigned)round_up((int64_t)a.TM * a.TN, 8));
+  const dim3 block(k2c::THREADS);
   const bool f32 = y_dtype == SVDQ_FP32;
   const bool gelu = epilogue == SVDQ_EPILOGUE_GELU_TANH;
   if (!gelu && f32)
-    hipLaunchKernelGGL((k2_w4a4_gemm<MODE_FWD, SVDQ_EPILOGUE_NONE, true>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k2_w4a4_gemm<MODE_FWD, SVDQ_EPILOGUE_NONE, true>), grid, block, 0, stream, a);
   else if (!gelu)
-    hipLaunchKernelGGL((k2_w4a4_gemm<MODE_FWD, SVDQ_EPILOGUE_NONE, false>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k2_w4a4_gemm<MODE_FWD, SVDQ_EPILOGUE_NONE, false>), grid, block, 0, stream, a);
   else if (f32)
-    hipLaunchKernelGGL((k2_w4a4_gemm<MODE_FWD, SVDQ_EPILOGUE_GELU_TANH, true>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k2_w4a4_gemm<MODE_FWD, SVDQ_EPILOGUE_GELU_TANH, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((k2_w4a4_gemm<MODE_FWD, SVDQ_EPILOGUE_GELU_TANH, false>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k2_w4a4_gemm<MODE_FWD, SVDQ_EPILOGUE_GELU_TANH, false>), grid, block, 0, stream, a);
   return launch_status("GEMM kernel launch");
 }
 
@@ -644,7 +855,7 @@ svdq_status_t svdq_quantize_activations(const svdq_weights_t *w, const void *X, 
   if ((st = launch_k1(L, Wl, w, X, M, ws, stream)) != SVDQ_OK) return st;
   const int64_t nb = (int64_t)M * (w->K / 2);
   hipLaunchKernelGGL(canon_codes_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream,
-                     reinterpret_cast<const int8_t *>(ws + Wl.qa), M, w->K, (int)(Wl.Mp / kTile), qact);
+                     ws + Wl.qa, M, w->K, (int)(Wl.Mp / kTile), qact);
   const int64_t ns = (int64_t)M * Wl.G;
   hipLaunchKernelGGL(canon_scales_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, stream,
                      reinterpret_cast<const float *>(ws + Wl.sa), M, (int)Wl.Mp, (int)Wl.G, ascales);
@@ -674,11 +885,12 @@ svdq_status_t svdq_debug_group_sums(const svdq_weights_t *w, int M, int m0, int 
   K2Args a = make_k2_args(L, Wl, w, M, static_cast<const uint8_t *>(workspace));
   a.P = P;
   a.m0 = m0; a.mcount = mcount; a.n0 = n0; a.ncount = ncount;
-  a.tile_m0 = m0 / 128 * 128;
-  a.tile_n0 = n0 / 128 * 128;
-  const int tm1 = (m0 + mcount + 127) / 128 * 128, tn1 = (n0 + ncount + 127) / 128 * 128;
-  const dim3 grid((unsigned)((tn1 - a.tile_n0) / 128), (unsigned)((tm1 - a.tile_m0) / 128));
-  hipLaunchKernelGGL((k2_w4a4_gemm<MODE_SUMS, SVDQ_EPILOGUE_NONE, true>), grid, dim3(256), 0,
+  a.tile_m0 = m0 / k2c::BM * k2c::BM;
+  a.tile_n0 = n0 / k2c::BN * k2c::BN;
+  a.TM = (m0 + mcount - a.tile_m0 + k2c::BM - 1) / k2c::BM;
+  a.TN = (n0 + ncount - a.tile_n0 + k2c::BN - 1) / k2c::BN;
+  const dim3 grid((unsigned)round_up((int64_t)a.TM * a.TN, 8));
+  hipLaunchKernelGGL((k2_w4a4_gemm<MODE_SUMS, SVDQ_EPILOGUE_NONE, true>), grid, dim3(k2c::THREADS), 0,
                      static_cast<hipStream_t>(hip_stream), a);
   return launch_status("group-sum kernel launch");
 }

@@ -177,14 +177,30 @@ svdq_status_t pack_device_weights(const svdq_host_weights_t *in, void *host_blob
   uint8_t *b = static_cast<uint8_t *>(host_blob);
   std::memset(b, 0, (size_t)L.total);
   const int64_t N = in->N, K = in->K, r = in->rank, T = L.Np / kTile;
-  int8_t *q = reinterpret_cast<int8_t *>(b + L.q);
-  parallel_for(N, 64, [&](int64_t n0, int64_t n1) {
-    for (int64_t n = n0; n < n1; ++n)
-      for (int64_t k = 0; k < K; k += 2) {
-        const uint8_t byte = in->qweight[n * (K / 2) + k / 2];
-        q[code_offset_rk(n, k, T)] = (int8_t)((int8_t)(byte << 4) >> 4);
-        q[code_offset_rk(n, k + 1, T)] = (int8_t)((int8_t)byte >> 4);
-      }
+  // fp6 codes: for every (group, tile, lane) the lane's 32 codes as 6-bit
+  // fields of a 192-bit word string, stored as three 8-byte word pairs
+  uint8_t *q = b + L.q;
+  const int64_t G = L.G;
+  parallel_for(T, 1, [&](int64_t t0, int64_t t1) {
+    for (int64_t t = t0; t < t1; ++t)
+      for (int64_t g = 0; g < G; ++g)
+        for (int lane = 0; lane < 64; ++lane) {
+          const int64_t n = t * kTile + (lane & 31);
+          const int h = lane >> 5;
+          uint32_t w[6] = {0, 0, 0, 0, 0, 0};
+          if (n < N)
+            for (int c = 0; c < 32; ++c) {
+              const int64_t k = g * kGroup + lane_code_k(h, c);
+              const uint8_t byte = in->qweight[n * (K / 2) + k / 2];
+              const int code = (k & 1) ? ((int8_t)byte >> 4) : ((int8_t)(byte << 4) >> 4);
+              const uint32_t v = e2m3_of_int(code);
+              const int bit = 6 * c;
+              w[bit / 32] |= v << (bit % 32);
+              if (bit % 32 > 26) w[bit / 32 + 1] |= v >> (32 - bit % 32);
+            }
+          for (int j = 0; j < 3; ++j)
+            std::memcpy(q + pair_offset(g, t, T, lane, j), &w[2 * j], 8);
+        }
   });
   float *s = reinterpret_cast<float *>(b + L.s);
   for (int64_t n = 0; n < N; ++n)

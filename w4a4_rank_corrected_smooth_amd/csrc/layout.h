@@ -1,15 +1,18 @@
 // Device data layouts shared by the host packer and the device kernels.
 // Everything here is constexpr so the same definitions serve both sides.
 //
-// INT4 codes live on the device one byte per code ("int8 containers") in a
-// matrix-core friendly tiling: rows (tokens for activations, output channels
-// for weights) are cut into tiles of 32; for every (group g of 64 input
-// channels, tile t) there is one 2048-byte block holding 32 codes for each of
-// the 64 lanes of a wavefront.  Lane l covers row l % 32 of the tile and half
-// h = l / 32 of the group; its code c (0..31) is input channel
-//     k = 64 g + 16 (c / 8) + 8 h + (c % 8).
-// Inside the block, code c of lane l sits at byte (c / 8) * 512 + l * 8 + c % 8,
-// so each 8-code chunk is one coalesced 512-byte line per wavefront.
+// INT4 codes live on the device as 6-bit floating-point values (OCP FP6
+// E2M3: sign, 2 exponent bits with bias 1, 3 mantissa bits), which hold the
+// integers -7..7 exactly and are the native operand of gfx950's fp6 matrix
+// instructions.  Rows (tokens for activations, output channels for weights)
+// are cut into tiles of 32; for every (group g of 64 input channels, tile t)
+// one 1536-byte block holds 32 codes for each of the 64 lanes of a
+// wavefront.  Lane l covers row l % 32 of the tile and half h = l / 32 of the
+// group; its code c (0..31) is input channel
+//     k = 64 g + 16 (c / 8) + 8 h + (c % 8)
+// and sits at bits 6c..6c+5 of the lane's 192-bit little-endian word string.
+// Inside the block, 8-byte word pair j (j = 0..2) of lane l is at byte
+// 512 j + 8 l, so every pair is one coalesced 512-byte line per wavefront.
 // Activations and weights use the identical assignment, which is all the
 // integer dot products need: a group's sum does not depend on how its 64
 // channels are ordered as long as both operands agree.
@@ -22,7 +25,7 @@ namespace svdq {
 constexpr int kGroup = 64;
 constexpr int kTile = 32;
 constexpr int kPad = 256;                // M and N are padded to multiples of this
-constexpr int kLaneBytes = 32;           // one int8 per code, 32 codes per lane
+constexpr int kLaneBytes = 24;           // 32 fp6 codes per lane
 constexpr int kBlockBytes = 64 * kLaneBytes;
 constexpr int64_t kAlign = 256;
 
@@ -32,16 +35,30 @@ constexpr int rank_pad(int rank) { return rank <= 0 ? 0 : (int)round_up(rank, 32
 // input channel (within the group) of code c held by half h
 constexpr int lane_code_k(int h, int c) { return 16 * (c >> 3) + 8 * h + (c & 7); }
 
-// byte offset of code c of lane `lane` in block (g, t) of a code array with T tiles
-constexpr int64_t code_offset(int64_t g, int64_t t, int64_t T, int lane, int c) {
-  return (g * T + t) * kBlockBytes + (int64_t)(c >> 3) * 512 + (int64_t)lane * 8 + (c & 7);
+// where the code for (row, k) lives: block (g, t), lane, code index c
+struct CodePos { int64_t g, t; int lane, c; };
+constexpr CodePos code_pos(int64_t row, int64_t k) {
+  return CodePos{k / kGroup, row / kTile, (int)(row % kTile) + 32 * (int)((k % 16) / 8),
+                 8 * (int)((k % kGroup) / 16) + (int)(k % 8)};
 }
 
-// byte offset of the code for (row, k) in a code array with T tiles
-constexpr int64_t code_offset_rk(int64_t row, int64_t k, int64_t T) {
-  return code_offset(k / kGroup, row / kTile, T,
-                     (int)(row % kTile) + 32 * (int)((k % 16) / 8),
-                     8 * (int)((k % kGroup) / 16) + (int)(k % 8));
+// byte offset of 8-byte word pair j of `lane` in block (g, t), T tiles
+constexpr int64_t pair_offset(int64_t g, int64_t t, int64_t T, int lane, int j) {
+  return (g * T + t) * kBlockBytes + (int64_t)j * 512 + (int64_t)lane * 8;
+}
+
+// FP6 E2M3 encoding of an integer code in [-7, 7]
+constexpr uint32_t e2m3_of_int(int q) {
+  const int a = q < 0 ? -q : q;
+  const uint32_t mag = a == 0 ? 0u : a == 1 ? 8u : a < 4 ? (uint32_t)(8 + 4 * a) : (uint32_t)(16 + 2 * a);
+  return (q < 0 ? 0x20u : 0u) | mag;
+}
+
+// integer value of an FP6 E2M3 code that holds an integer
+constexpr int int_of_e2m3(uint32_t v) {
+  const int e = (int)((v >> 3) & 3u), m = (int)(v & 7u);
+  const int mag = e == 0 ? 0 : ((8 + m) << (e - 1)) / 8;
+  return (v & 0x20u) ? -mag : mag;
 }
 
 // Device weight blob of one prepared layer.
@@ -52,7 +69,7 @@ struct WeightLayout {
       : N(N_), K(K_), rank(rank_), Np(round_up(N_, kPad)), rp(rank_pad((int)rank_)),
         G(K_ / kGroup) {
     int64_t o = 0;
-    q = o;    o = round_up(o + Np * K, kAlign);          // int8 codes, tiled
+    q = o;    o = round_up(o + Np * K * 3 / 4, kAlign);  // fp6 codes, tiled
     s = o;    o = round_up(o + G * Np * 4, kAlign);      // fp32 scales [G][Np]
     l2t = o;  o = round_up(o + Np * rp * 2, kAlign);     // bf16 L2^T [Np][rp]
     l1t = o;  o = round_up(o + rp * K * 2, kAlign);      // bf16 L1s^T [rp][K]
@@ -83,7 +100,7 @@ struct WorkLayout {
       : M(M_), Mp(round_up(M_, kPad)), K(K_), G(K_ / kGroup), rp(rank_pad((int)rank_)),
         S(k1_splits(round_up(M_, kPad), K_ / kGroup)) {
     int64_t o = 0;
-    qa = o; o = round_up(o + Mp * K, kAlign);            // int8 codes, tiled
+    qa = o; o = round_up(o + Mp * K * 3 / 4, kAlign);    // fp6 codes, tiled
     sa = o; o = round_up(o + G * Mp * 4, kAlign);        // fp32 scales [G][Mp]
     d = o;  o = round_up(o + S * Mp * rp * 4, kAlign);   // fp32 partial X L1s [S][Mp][rp]
     total = o;
