@@ -43,15 +43,20 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(sample_rows_fc1=3072, sample_rows_fc2=1536):
+def cpu_baseline(sample_rows_fc1=3072, sample_rows_fc2=1536, min_seconds=10.0, max_runs=40):
     """The oracle as it stands, timed on the host cores over a bounded sample:
     every token row of both layers, for a slice of each layer's output
-    channels (prepare untimed)."""
+    channels (prepare untimed).  The sample's forward is repeated until at
+    least ``min_seconds`` of CPU work have been timed."""
     import numpy as np
     import synth
     from oracle import svdquant as O
     from oracle import glue as OG
-    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) or 1
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
     fc1, W2, b2 = synth.mlp_cases()
     M, K1, K2 = fc1.M, fc1.K, W2.shape[1]
     ref1 = O.prepare(fc1.W[:sample_rows_fc1], fc1.calib_absmax(), fc1.bias[:sample_rows_fc1], 32)
@@ -60,17 +65,103 @@ def cpu_baseline(sample_rows_fc1=3072, sample_rows_fc2=1536):
     X2 = O.bf16_bits_of(OG.gelu_tanh_bf16(O.bf16_values(pre)))
     ref2 = O.prepare(W2[:sample_rows_fc2], O.calibration_absmax(O.bf16_values(X2[:64])),
                      b2[:sample_rows_fc2], 32)
-    t0 = time.perf_counter()
-    O.forward(ref1, fc1.X)
-    O.forward(ref2, X2)
-    t = time.perf_counter() - t0
-    ops = 2.0 * M * sample_rows_fc1 * K1 + 2.0 * M * sample_rows_fc2 * K2
+    runs, t = 0, 0.0
+    while runs < max_runs and (runs == 0 or t < min_seconds):
+        t0 = time.perf_counter()
+        O.forward(ref1, fc1.X)
+        O.forward(ref2, X2)
+        t += time.perf_counter() - t0
+        runs += 1
+    ops = runs * (2.0 * M * sample_rows_fc1 * K1 + 2.0 * M * sample_rows_fc2 * K2)
     return {"value": ops / t / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
             "sample": (f"oracle forward (activation quantisation, low-rank down, float64 "
                        f"group-scaled GEMM, low-rank up, bias) over all {M} tokens for "
                        f"{sample_rows_fc1} of fc1's 12288 and {sample_rows_fc2} of fc2's 3072 "
-                       f"output channels; {t:.1f} s"),
-            "seconds": t}
+                       f"output channels, repeated {runs} times: {t:.1f} s"),
+            "seconds": round(t, 2)}
+
+
+# ------------------------------------------------------------------ profiles
+K2_NAME = "k2_w4a4_gemm"
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "")
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir, command):
+    """CPU-only: turn rocprofv3 output (one --kernel-trace --stats run, one
+    FETCH_SIZE pass, one WRITE_SIZE pass, all of ``bench.py
+    --calibration-copy``) into the text summaries kept under profiles/ and
+    the per-launch HBM traffic of the GEMM kernel."""
+    import numpy as np
+    stats = _read_csv(_find(trace_dir, "kernel_stats.csv"))
+    lines = ["# Kernel durations, Flux MLP pair 4608x3072x12288 r32 + AWQ 1x3072x18432",
+             "", "Command (rocprofv3 --kernel-trace --stats):", "", "```", command["trace"], "```", "",
+             "| kernel | calls | average us | min us | max us | share |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for r in stats:
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    with open(os.path.join(out_dir, "kernels_flux_mlp_pair.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def per_kernel(d, counter):
+        rows = [r for r in _read_csv(_find(d, "counter_collection.csv")) if r["Counter_Name"] == counter]
+        by = {}
+        for r in rows:
+            by.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return by
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    copy_name = [k for k in fetch if "neg" in k.lower()]
+    if not copy_name:
+        raise RuntimeError("the calibration copy kernel is missing from the FETCH_SIZE pass")
+    copy_bytes = CALIBRATION_BYTES
+    f_fac = float(np.median(fetch[copy_name[0]])) / copy_bytes
+    w_fac = float(np.median(write[copy_name[0]])) / copy_bytes
+    out = {"source_hash": source_hash(), "fetch_factor": f_fac, "write_factor": w_fac,
+           "calibration": f"elementwise negate of {copy_bytes} bytes float32 into a second buffer",
+           "kernels": {}}
+    tl = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE and WRITE_SIZE, calibrated)", "",
+          "Commands (one pass per counter):", "", "```", command["fetch"], command["write"], "```", "",
+          f"Calibration: elementwise negate of {copy_bytes / 2**20:.0f} MiB float32 reads and writes "
+          f"{copy_bytes / 2**20:.0f} MiB; the counters read {f_fac:.3f}x (fetch) and {w_fac:.3f}x (write) "
+          "of that, and every figure below is divided by those factors.", "",
+          "| kernel | launches | fetch MB | write MB | total MB |", "|---|---:|---:|---:|---:|"]
+    for k in fetch:
+        if k not in write:
+            continue
+        fb = float(np.mean(fetch[k])) / f_fac
+        wb = float(np.mean(write[k])) / w_fac
+        out["kernels"][k] = {"fetch_bytes": fb, "write_bytes": wb, "launches": len(fetch[k])}
+        tl.append(f"| `{k[:90]}` | {len(fetch[k])} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {(fb + wb) / 1e6:.1f} |")
+    k2 = [v for k, v in out["kernels"].items() if K2_NAME in k]
+    if k2:
+        out["bytes_per_launch"] = float(np.mean([v["fetch_bytes"] + v["write_bytes"] for v in k2]))
+        tl += ["", f"{K2_NAME} mean over its launches: {out['bytes_per_launch'] / 1e6:.1f} MB per launch."]
+    with open(os.path.join(out_dir, "hbm_traffic_flux_mlp_pair.md"), "w") as f:
+        f.write("\n".join(tl) + "\n")
+    with open(os.path.join(out_dir, "k2_traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print("\n".join(lines + [""] + tl))
+
+
+CALIBRATION_BYTES = 256 << 20
 
 
 def main():
@@ -80,7 +171,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sets", type=int, default=3, help="rotating copies of inputs and weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="first run an elementwise copy of known size (for HBM counter calibration)")
+    ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="CPU only: summarise rocprofv3 output into profiles/ and exit")
     args = ap.parse_args()
+    if args.summarize_profile:
+        t, fe, wr = args.summarize_profile
+        base = "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --calibration-copy"
+        cmd = {"trace": f"rocprofv3 --kernel-trace --stats -f csv -d {t} -- {base}",
+               "fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d {fe} -- {base}",
+               "write": f"rocprofv3 --pmc WRITE_SIZE -f csv -d {wr} -- {base}"}
+        summarize_profiles(t, fe, wr, os.path.join(ROOT, "profiles"), cmd)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this library runs the layer on a single MI355X and "
               f"has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -128,6 +231,14 @@ def main():
     xm = [torch.from_numpy(np.ascontiguousarray(a.x[:1])).to(dev) for _ in range(R)]
     ym = [torch.empty((1, a.N), dtype=torch.float16, device=dev) for _ in range(R)]
     torch.cuda.synchronize()
+
+    if args.calibration_copy:
+        src = torch.randn(CALIBRATION_BYTES // 4, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     stream = torch.cuda.current_stream(dev)
     NEV = 6
