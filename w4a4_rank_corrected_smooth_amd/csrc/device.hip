@@ -83,13 +83,30 @@ __global__ __launch_bounds__(256) void k1_quantize_lowrank_down(
 #pragma unroll
   for (int b = 0; b < NB; ++b) dacc[b] = v16f{};
 
-  for (int gi = w; gi < Gs; gi += 4) {
-    const int g = s * Gs + gi;
-    uint4 xr[4];
-    const uint16_t *xp = X + (int64_t)row * K + g * kGroup + 8 * h;
+  // Register prefetch ring: each wavefront keeps the loads of its next
+  // K1_PF groups in flight while it quantises the current one.
+  constexpr int K1_PF = 3;
+  uint4 ring[K1_PF][4];
+  auto load_group = [&](int gi, uint4 (&dst)[4]) {
+    const uint16_t *xp = X + (int64_t)row * K + (s * Gs + gi) * kGroup + 8 * h;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      xr[j] = valid ? *reinterpret_cast<const uint4 *>(xp + 16 * j) : make_uint4(0, 0, 0, 0);
+      dst[j] = valid ? *reinterpret_cast<const uint4 *>(xp + 16 * j) : make_uint4(0, 0, 0, 0);
+  };
+#pragma unroll
+  for (int p = 0; p < K1_PF; ++p)
+    if (w + 4 * p < Gs) load_group(w + 4 * p, ring[p]);
+
+  for (int base = w; base < Gs; base += 4 * K1_PF)
+#pragma unroll
+  for (int p = 0; p < K1_PF; ++p) {
+    const int gi = base + 4 * p;
+    if (gi >= Gs) break;
+    const int g = s * Gs + gi;
+    uint4 xr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xr[j] = ring[p][j];
+    if (gi + 4 * K1_PF < Gs) load_group(gi + 4 * K1_PF, ring[p]);
     float xh[32];
     float a = 0.0f;
 #pragma unroll
@@ -212,19 +229,21 @@ struct K2Args {
 };
 
 namespace k2c {
-constexpr int BM = 256, BN = 128, THREADS = 512;
+constexpr int BM = 128, BN = 128, THREADS = 256, NWAVES = THREADS / 64;
 constexpr int A_BLK = BM / kTile, B_BLK = BN / kTile;
 constexpr int A_BYTES = A_BLK * kBlockBytes;     // one group per stage
 constexpr int B_BYTES = B_BLK * kBlockBytes;
 constexpr int SA_BYTES = BM * 4, SW_BYTES = BN * 4;
-constexpr int STAGE_USED = A_BYTES + B_BYTES + SA_BYTES + SW_BYTES;   // 19968
-constexpr int UNITS = STAGE_USED / 16;                                 // 1248
-constexpr int WAVE_LOADS = (UNITS + 63) / 64;                          // 20
-constexpr int STAGE = WAVE_LOADS * 64 * 16;                            // 20480, padded
-constexpr int NBUF = 4;                                                // stages in LDS
-constexpr int GM = 4;             // tile-rows walked together on one XCD
+constexpr int STAGE_USED = A_BYTES + B_BYTES + SA_BYTES + SW_BYTES;   // 13312
+constexpr int UNITS = STAGE_USED / 16;                                 // 832
+constexpr int WAVE_LOADS = (UNITS + 63) / 64;                          // 13
+constexpr int STAGE = WAVE_LOADS * 64 * 16;                            // 13312
+constexpr int MAX_LOADS = (WAVE_LOADS + NWAVES - 1) / NWAVES;          // 4 per wave
+constexpr int NBUF = 6;                                                // stages in LDS
+constexpr int GM = 8;             // tile-rows walked together on one XCD
 static_assert(STAGE_USED % 16 == 0, "stage must be whole 16-byte units");
-static_assert(WAVE_LOADS > 16 && WAVE_LOADS <= 24, "copy schedule below: 3 loads for waves 0-3, 2 for 4-7");
+static_assert(MAX_LOADS <= 4, "vmcnt waits below assume at most 4 copies per wave and stage");
+static_assert(2 * NBUF * STAGE <= 160 * 1024, "two workgroups must fit in one CU's LDS");
 }  // namespace k2c
 
 // Stage layout in LDS (one group of 64 input channels):
@@ -246,15 +265,37 @@ __device__ __forceinline__ const uint4 *k2_unit_src(const K2Args &p, int g, int 
   return reinterpret_cast<const uint4 *>(p.sw + (int64_t)g * p.Np + bn + off / 4);
 }
 
+// The fp6 operand occupies six registers; the instruction's 8-register
+// operand slot leaves the last two unread, so they are left undefined
+// rather than cleared on every load.
 __device__ __forceinline__ v8i k2_frag(const uint8_t *blk, int lane) {
   const uint2 w0 = *reinterpret_cast<const uint2 *>(blk + lane * 8);
   const uint2 w1 = *reinterpret_cast<const uint2 *>(blk + 512 + lane * 8);
   const uint2 w2 = *reinterpret_cast<const uint2 *>(blk + 1024 + lane * 8);
-  return v8i{(int)w0.x, (int)w0.y, (int)w1.x, (int)w1.y, (int)w2.x, (int)w2.y, 0, 0};
+  v8i r = __builtin_nondeterministic_value(r);
+  r[0] = (int)w0.x; r[1] = (int)w0.y; r[2] = (int)w1.x;
+  r[3] = (int)w1.y; r[4] = (int)w2.x; r[5] = (int)w2.y;
+  return r;
+}
+
+// Instruction order inside one step of K2's pipeline: the step's matrix
+// instruction(s) first (the second one after `gap` vector instructions),
+// then its LDS reads, then the FMAs, and a fence so nothing crosses into the
+// next step.  This keeps the matrix core busy under the FMAs.
+template <int NMFMA, int GAP>
+__device__ __forceinline__ void k2_order() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  if constexpr (NMFMA == 2) {
+    __builtin_amdgcn_sched_group_barrier(0x002, GAP, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int MODE, int EPI, bool OUT_F32>
-__global__ __launch_bounds__(512) void k2_w4a4_gemm(K2Args p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_w4a4_gemm(K2Args p) {
   using namespace k2c;
   // ---- tile of this workgroup (XCD-aware, grouped)
   const int T = p.TM * p.TN;
@@ -282,22 +323,22 @@ __global__ __launch_bounds__(512) void k2_w4a4_gemm(K2Args p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
 
-  // Copy schedule: a stage is 20 wavefront-loads of 64 x 16 bytes; wave w
-  // issues loads w, w + 8 and (waves 0-3 only) w + 16, every lane active,
-  // so each wavefront issues the same number of copies per stage and the
-  // vmcnt waits below count exactly.  The last 32 units are padding
-  // (source: the first codes of this panel, destination: the pad).
+  // Copy schedule: a stage is WAVE_LOADS wavefront-loads of 64 x 16 bytes;
+  // wave w issues loads w, w + 4, w + 8, ... with every lane active, so the
+  // number of copies a wave has in flight per stage (nload) is fixed and the
+  // vmcnt waits below count exactly.  Units past the stage (if any) re-read
+  // the A panel into the padding.
   const int wu = __builtin_amdgcn_readfirstlane(w);      // wavefront index, scalar
-  const int nload = wu < WAVE_LOADS - 16 ? 3 : 2;
+  const int nload = (WAVE_LOADS - wu + NWAVES - 1) / NWAVES;
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
   // per copy slot: source of group 0 and the byte stride from one group to
   // the next (A and B panels advance by a row of blocks, the scales by a row
-  // of the [G][Mp] / [G][Np] arrays); padding lanes re-read the A panel
-  const uint8_t *src0[3];
-  int64_t sstride[3];
+  // of the [G][Mp] / [G][Np] arrays)
+  const uint8_t *src0[MAX_LOADS];
+  int64_t sstride[MAX_LOADS];
 #pragma unroll
-  for (int r = 0; r < 3; ++r) {
-    const int u = 64 * (wu + 8 * r) + lane;
+  for (int r = 0; r < MAX_LOADS; ++r) {
+    const int u = 64 * (wu + NWAVES * r) + lane;
     const int off = u * 16;
     if (u >= UNITS || off < A_BYTES) {
       src0[r] = p.qa + (int64_t)(bm / kTile) * kBlockBytes + (u < UNITS ? off : 0);
@@ -316,91 +357,107 @@ __global__ __launch_bounds__(512) void k2_w4a4_gemm(K2Args p) {
   auto fetch = [&](int g) {
     const uint32_t buf = smem_lds + (uint32_t)((g % NBUF) * STAGE) + (uint32_t)(wu * 64 * 16);
 #pragma unroll
-    for (int r = 0; r < 3; ++r)
-      if (r < nload) lds_dma16(src0[r] + g * sstride[r], buf + (uint32_t)(r * 8 * 64 * 16));
+    for (int r = 0; r < MAX_LOADS; ++r)
+      if (r < nload) lds_dma16(src0[r] + g * sstride[r], buf + (uint32_t)(r * NWAVES * 64 * 16));
   };
-  // wait until at most `later` stages issued after the one needed are in flight
+  // wait until at most `later` stages issued after the ones needed are in flight
   auto wait_stage = [&](int later) {
     if (MODE == MODE_SUMS) { vmcnt_wait0(); return; }   // P stores also count
-    if (nload == 3) {
-      if (later >= 2) vmcnt_wait<6>(); else if (later == 1) vmcnt_wait<3>(); else vmcnt_wait0();
+    if (nload == 4) {
+      if (later >= 4) vmcnt_wait<16>(); else if (later == 3) vmcnt_wait<12>();
+      else if (later == 2) vmcnt_wait<8>(); else if (later == 1) vmcnt_wait<4>(); else vmcnt_wait0();
     } else {
-      if (later >= 2) vmcnt_wait<4>(); else if (later == 1) vmcnt_wait<2>(); else vmcnt_wait0();
+      if (later >= 4) vmcnt_wait<12>(); else if (later == 3) vmcnt_wait<9>();
+      else if (later == 2) vmcnt_wait<6>(); else if (later == 1) vmcnt_wait<3>(); else vmcnt_wait0();
     }
   };
 
-  // Operands of one group as a wavefront holds them in registers.
-  struct Frags { v8i a0, a1, b0, b1; float sa0, sa1, sw; };
-  auto read_stage = [&](int g) {
-    const uint8_t *st = smem + (g % NBUF) * STAGE;
-    const float *lsa = reinterpret_cast<const float *>(st + A_BYTES + B_BYTES);
-    const float *lsw = reinterpret_cast<const float *>(st + A_BYTES + B_BYTES + SA_BYTES);
-    Frags f;
-    f.b0 = k2_frag(st + A_BYTES + (2 * wni) * kBlockBytes, lane);
-    f.b1 = k2_frag(st + A_BYTES + (2 * wni + 1) * kBlockBytes, lane);
-    f.a0 = k2_frag(st + (2 * wmi) * kBlockBytes, lane);
-    f.a1 = k2_frag(st + (2 * wmi + 1) * kBlockBytes, lane);
-    // outer-product operands: block 0 (lanes 0-31) pairs a row tile with
-    // column tile 0, block 1 (lanes 32-63) with column tile 1
-    f.sw = lsw[64 * wni + 32 * hl + ln];
-    f.sa0 = lsa[64 * wmi + ln];
-    f.sa1 = lsa[64 * wmi + 32 + ln];
-    return f;
+  // Operands of one group as a wavefront holds them in registers: the fp6
+  // codes of its two row tiles and two column tiles, and the scales for the
+  // outer products (block 0, lanes 0-31, pairs a row tile with column tile
+  // 0; block 1, lanes 32-63, with column tile 1).
+  struct Frags { v8i a[2], b[2]; float sa[2], sw; };
+  Frags F;
+  auto stage_of = [&](int g) { return smem + (g % NBUF) * STAGE; };
+  auto load_a = [&](int g, int i) { F.a[i] = k2_frag(stage_of(g) + (2 * wmi + i) * kBlockBytes, lane); };
+  auto load_b = [&](int g, int j) {
+    F.b[j] = k2_frag(stage_of(g) + A_BYTES + (2 * wni + j) * kBlockBytes, lane);
   };
-  Frags f;
-
-  // Software pipeline over (group, row tile).  Each wavefront keeps the
-  // products of one row tile in flight while it applies the scales of the
-  // other, so its own matrix and FMA work overlap:
-  //   A. matrix work of row tile 1, group g   |  FMAs of row tile 0, group g
-  //   B. wait for stage g+1, barrier (buffer (g-1) % NBUF is then free),
-  //      read stage g+1 into f, request stage g+NBUF-1
-  //   C. matrix work of row tile 0, group g+1 |  FMAs of row tile 1, group g
-  auto mm_row = [&](const v8i &a, float sa, v16f &P0, v16f &P1, v32f &Sc) {
-    P0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, f.b0, v16f{}, 2, 2, 0, 127, 0, 127);
-    P1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, f.b1, v16f{}, 2, 2, 0, 127, 0, 127);
-    if constexpr (MODE == MODE_FWD) Sc = __builtin_amdgcn_mfma_f32_32x32x1f32(sa, f.sw, v32f{}, 0, 0, 0);
+  auto load_sa = [&](int g, int i) {
+    F.sa[i] = reinterpret_cast<const float *>(stage_of(g) + A_BYTES + B_BYTES)[64 * wmi + 32 * i + ln];
   };
-  auto apply_row = [&](int i, int g, const v16f &P0, const v16f &P1, const v32f &Sc) {
+  auto load_sw = [&](int g) {
+    F.sw = reinterpret_cast<const float *>(stage_of(g) + A_BYTES + B_BYTES + SA_BYTES)[64 * wni + 32 * hl + ln];
+  };
+  // Per group the wavefront's four 32 x 32 tiles t = (i, j) = (t / 2, t % 2)
+  // each take one fp6 product; each row tile takes one outer product of
+  // scales, issued with its first tile.
+  auto mm = [&](int t, v16f &P, v32f &Sr) {
+    const int i = t >> 1, j = t & 1;
+    P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[i], F.b[j], v16f{}, 2, 2, 0, 127, 0, 127);
+    if constexpr (MODE == MODE_FWD)
+      if (j == 0) Sr = __builtin_amdgcn_mfma_f32_32x32x1f32(F.sa[i], F.sw, v32f{}, 0, 0, 0);
+  };
+  auto consume = [&](int t, int g, const v16f &P, const v32f &Sr) {
+    const int i = t >> 1, j = t & 1;
     if constexpr (MODE == MODE_SUMS) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = wn + 32 * j + ln;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = wm + 32 * i + 8 * (e >> 2) + 4 * hl + (e & 3);
-          const float v = j ? P1[e] : P0[e];
-          if (m >= p.m0 && m < p.m0 + p.mcount && n >= p.n0 && n < p.n0 + p.ncount)
-            p.P[((int64_t)(m - p.m0) * p.ncount + (n - p.n0)) * G + g] = (int32_t)v;
-        }
-      }
-    } else {
+      const int n = wn + 32 * j + ln;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        acc[i][0][e] = __builtin_fmaf(P0[e], Sc[e], acc[i][0][e]);
-        acc[i][1][e] = __builtin_fmaf(P1[e], Sc[16 + e], acc[i][1][e]);
+        const int m = wm + 32 * i + 8 * (e >> 2) + 4 * hl + (e & 3);
+        if (m >= p.m0 && m < p.m0 + p.mcount && n >= p.n0 && n < p.n0 + p.ncount)
+          p.P[((int64_t)(m - p.m0) * p.ncount + (n - p.n0)) * G + g] = (int32_t)P[e];
       }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = __builtin_fmaf(P[e], Sr[16 * j + e], acc[i][j][e]);
     }
   };
 
+  // Software pipeline over (group, tile): while the FMAs of tile t run on
+  // the vector ALU, the matrix core works on tile t + 1 (the next group's
+  // first tile after t = 3).  Each operand of group g + 1 is read from LDS
+  // into its registers right after the last instruction of group g that
+  // uses them, one to three tiles before it is needed.  A barrier every
+  // second group: at even g every wave waits for stages g+1 and g+2, meets
+  // the others, and requests stages g+5 and g+6 (the buffers of stages g-1
+  // and g, which every wave has read before this barrier).  The scheduling
+  // fences keep each step's products from being hoisted above the FMAs that
+  // still read the registers they overwrite.  After the last group the
+  // loads and the first product still run, on a stale but in-bounds LDS
+  // buffer, and their results are never used: branch-free code keeps the
+  // operands and products in fixed registers.
+  v16f Pa, Pb;
+  v32f S0, S1;
   for (int g = 0; g < NBUF - 1 && g < G; ++g) fetch(g);
   wait_stage(min(NBUF - 2, G - 1));
   __syncthreads();
-  f = read_stage(0);
-  v16f P00, P01, P10, P11;
-  v32f S0, S1;
-  mm_row(f.a0, f.sa0, P00, P01, S0);
+  load_a(0, 0); load_a(0, 1); load_b(0, 0); load_b(0, 1);
+  load_sa(0, 0); load_sa(0, 1); load_sw(0);
+  mm(0, Pa, S0);
   for (int g = 0; g < G; ++g) {
-    mm_row(f.a1, f.sa1, P10, P11, S1);                      // A
-    apply_row(0, g, P00, P01, S0);
-    if (g + 1 < G) {                                        // B
-      wait_stage(min(NBUF - 3, G - 2 - g));
+    const bool nx = g + 1 < G;
+    if ((g & 1) == 0 && nx) {
+      wait_stage(min(g + 4, G - 1) - min(g + 2, G - 1));
       __syncthreads();
-      f = read_stage(g + 1);
-      if (g + NBUF - 1 < G) fetch(g + NBUF - 1);
+      if (g + 5 < G) fetch(g + 5);
+      if (g + 6 < G) fetch(g + 6);
     }
-    mm_row(f.a0, f.sa0, P00, P01, S0);                      // C (unused after the last group)
-    apply_row(1, g, P10, P11, S1);
+    mm(1, Pb, S0);                                  // tile (0,1): last use of a0
+    load_a(g + 1, 0); load_sa(g + 1, 0);
+    consume(0, g, Pa, S0);
+    k2_order<1, 0>();
+    mm(2, Pa, S1);                                  // tile (1,0) + row 1 scales: last use of b0, sa1, sw
+    load_b(g + 1, 0); load_sa(g + 1, 1); load_sw(g + 1);
+    consume(1, g, Pb, S0);
+    k2_order<2, 4>();
+    mm(3, Pb, S1);                                  // tile (1,1): last use of a1, b1
+    load_a(g + 1, 1); load_b(g + 1, 1);
+    consume(2, g, Pa, S1);
+    k2_order<1, 0>();
+    mm(0, Pa, S0);                                  // next group's tile (0,0) + row 0 scales
+    consume(3, g, Pb, S1);
+    k2_order<2, 4>();
   }
 
   if constexpr (MODE == MODE_FWD) {
@@ -496,68 +553,94 @@ __global__ __launch_bounds__(512) void k2_w4a4_gemm(K2Args p) {
 }
 
 // ======================================================================= K3
-// AWQ W4A16: one wavefront per tile of 16 output channels.  For each group of
-// 64 input channels, lane l (channel l % 16, quarter q = l / 16) turns its 16
-// codes into fp16 (q - z) with the 1024-offset trick (0x6400 | code is the
-// fp16 value 1024 + code; subtracting 1024 + z is exact), the activations
-// [16, 64] are the A operand, and two v_mfma_f32_16x16x32_f16 give the
-// group's inner sums; acc += s * sum in fp32.  Rows m >= M are zero.
-__global__ __launch_bounds__(64) void k3_awq_w4a16(const uint8_t *__restrict__ qd,
-                                                    const uint32_t *__restrict__ sz,
-                                                    const uint16_t *__restrict__ x, int M,
-                                                    int N, int Np, int K,
-                                                    const uint16_t *__restrict__ bias,
-                                                    uint16_t *__restrict__ y) {
-  const int lane = threadIdx.x;
+// AWQ W4A16.  A workgroup of 4 wavefronts owns a tile of 16 output channels;
+// wavefront w takes a contiguous quarter of the groups of 64 input channels
+// and issues the loads of 8 groups before it computes any of them, so every
+// CU keeps tens of kilobytes of weight reads in flight.  For each group,
+// lane l (channel l % 16, quarter q = l / 16) turns its 16 codes into fp16
+// (q - z) with the 1024-offset trick (0x6400 | code is the fp16 value
+// 1024 + code; subtracting 1024 + z is exact), the activations [16, 64] are
+// the A operand, and two v_mfma_f32_16x16x32_f16 give the group's inner
+// sums; acc += s * sum in fp32.  Rows m >= M are zero.  The four partial
+// sums meet in LDS, in a fixed order.
+constexpr int kAwqChunk = 8;
+__global__ __launch_bounds__(256) void k3_awq_w4a16(const uint8_t *__restrict__ qd,
+                                                     const uint32_t *__restrict__ sz,
+                                                     const uint16_t *__restrict__ x, int M,
+                                                     int N, int Np, int K,
+                                                     const uint16_t *__restrict__ bias,
+                                                     uint16_t *__restrict__ y) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int tile = blockIdx.x;
   const int G = K / kGroup;
+  const int Gq = (G + 3) / 4;
+  const int g0 = min(G, w * Gq), g1 = min(G, g0 + Gq);
   const int m = lane & 15, qtr = lane >> 4;
   const int n = tile * kAwqTile + (lane & 15);
+  const uint8_t *qbase = qd + (int64_t)tile * G * kAwqBlockBytes + lane * 8;
+  const uint16_t *xrow = x + (int64_t)m * K + 16 * qtr;
   v4f acc = v4f{};
-  for (int g = 0; g < G; ++g) {
-    const uint2 cw = *reinterpret_cast<const uint2 *>(
-        qd + ((int64_t)tile * G + g) * kAwqBlockBytes + lane * 8);
-    const uint32_t szw = sz[(int64_t)g * Np + n];
-    const _Float16 zf = __builtin_bit_cast(_Float16, (uint16_t)(szw >> 16));
-    const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)(szw & 0xFFFF));
-    const _Float16 off = -((_Float16)1024.0f + zf);
-    const v2h off2 = v2h{off, off};
-    v8h bop[2];
+  for (int gc = g0; gc < g1; gc += kAwqChunk) {
+    uint2 cw[kAwqChunk];
+    uint32_t szw[kAwqChunk];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const uint32_t word = half ? cw.y : cw.x;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t pr = ((word >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-        const v2h v = __builtin_bit_cast(v2h, pr) + off2;
-        bop[half][2 * j] = v.x;
-        bop[half][2 * j + 1] = v.y;
+    for (int i = 0; i < kAwqChunk; ++i) {
+      const int g = gc + i;
+      if (g < g1) {
+        cw[i] = *reinterpret_cast<const uint2 *>(qbase + (int64_t)g * kAwqBlockBytes);
+        szw[i] = sz[(int64_t)g * Np + n];
+      } else {
+        cw[i] = make_uint2(0, 0);
+        szw[i] = 0;
       }
     }
-    v8h aop[2];
-    if (m < M) {
-      const uint16_t *xp = x + (int64_t)m * K + g * kGroup + 16 * qtr;
-      aop[0] = __builtin_bit_cast(v8h, *reinterpret_cast<const uint4 *>(xp));
-      aop[1] = __builtin_bit_cast(v8h, *reinterpret_cast<const uint4 *>(xp + 8));
-    } else {
-      aop[0] = v8h{};
-      aop[1] = v8h{};
-    }
-    v4f part = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[0], bop[0], v4f{}, 0, 0, 0);
-    part = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[1], bop[1], part, 0, 0, 0);
-    // output layout: lane holds rows 4 * (lane / 16) + i, column lane % 16
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(part[i], sf, acc[i]);
+    for (int i = 0; i < kAwqChunk; ++i) {
+      // the activations are a few kilobytes shared by every workgroup: L2 hits
+      uint4 xa[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+      if (gc + i < g1 && m < M) {
+        xa[0] = *reinterpret_cast<const uint4 *>(xrow + (gc + i) * kGroup);
+        xa[1] = *reinterpret_cast<const uint4 *>(xrow + (gc + i) * kGroup + 8);
+      }
+      const _Float16 zf = __builtin_bit_cast(_Float16, (uint16_t)(szw[i] >> 16));
+      const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)(szw[i] & 0xFFFF));
+      const _Float16 off = -((_Float16)1024.0f + zf);
+      const v2h off2 = v2h{off, off};
+      v8h bop[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const uint32_t word = half ? cw[i].y : cw[i].x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t pr = ((word >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+          const v2h v = __builtin_bit_cast(v2h, pr) + off2;
+          bop[half][2 * j] = v.x;
+          bop[half][2 * j + 1] = v.y;
+        }
+      }
+      v4f part = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, xa[0]), bop[0],
+                                                       v4f{}, 0, 0, 0);
+      part = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, xa[1]), bop[1], part,
+                                                   0, 0, 0);
+      // output layout: lane holds rows 4 * (lane / 16) + e, column lane % 16
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(part[e], sf, acc[e]);
+    }
   }
+  __shared__ v4f red[4][64];
+  red[w][lane] = acc;
+  __syncthreads();
+  if (w != 0) return;
+  const v4f r0 = red[0][lane], r1 = red[1][lane], r2 = red[2][lane], r3 = red[3][lane];
   const int col = tile * kAwqTile + (lane & 15);
   if (col < N) {
     const float b = bias ? (float)__builtin_bit_cast(_Float16, bias[col]) : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * (lane >> 4) + i;
+    for (int e = 0; e < 4; ++e) {
+      const int row = 4 * (lane >> 4) + e;
       if (row < M) {
-        const _Float16 o = (_Float16)(acc[i] + b);
-        y[(int64_t)row * N + col] = __builtin_bit_cast(uint16_t, o);
+        const float v = ((r0[e] + r1[e]) + (r2[e] + r3[e])) + b;
+        y[(int64_t)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
       }
     }
   }
@@ -906,7 +989,7 @@ svdq_status_t awq_w4a16_forward(const void *blob, int N, int K, const void *x, i
   if (st != SVDQ_OK) return st;
   const AwqLayout L(N, K);
   const uint8_t *b = static_cast<const uint8_t *>(blob);
-  hipLaunchKernelGGL(k3_awq_w4a16, dim3((unsigned)(L.Np / kAwqTile)), dim3(64), 0,
+  hipLaunchKernelGGL(k3_awq_w4a16, dim3((unsigned)(L.Np / kAwqTile)), dim3(256), 0,
                      static_cast<hipStream_t>(hip_stream), b + L.q,
                      reinterpret_cast<const uint32_t *>(b + L.sz), static_cast<const uint16_t *>(x), M,
                      N, (int)L.Np, K, static_cast<const uint16_t *>(bias), static_cast<uint16_t *>(y));
