@@ -167,8 +167,10 @@ CALIBRATION_BYTES = 256 << 20
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the GPU takes tens of milliseconds of sustained load to reach its
+    # steady clocks; ~100 untimed steps (~70 ms) cover that
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--sets", type=int, default=3, help="rotating copies of inputs and weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true",

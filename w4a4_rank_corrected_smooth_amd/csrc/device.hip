@@ -58,61 +58,149 @@ __device__ __forceinline__ float gelu_tanh_f32(float y) {
   return y * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
 }
 
+// Global -> LDS copy of 16 bytes per lane by the load unit
+// (global_load_lds_dwordx4): lane i writes LDS address lds_base + 16 i.
+// lds_base must be uniform across the wavefront.  Written as inline asm so
+// that the copy's completion is tracked by the caller's own vmcnt waits
+// (the compiler would otherwise wait for every copy before any LDS read).
+// The asm has no register outputs; M0 is set and used inside the block.
+__device__ __forceinline__ void lds_dma16(const void *gsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gsrc), "s"(lds_base) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void vmcnt_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ void vmcnt_wait0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// wait until at most n vector-memory operations are outstanding, n a runtime
+// value (clamped to the counter's 6-bit maximum, which only waits longer)
+template <int N>
+__device__ __forceinline__ void vmcnt_wait_le(int n) {
+  if constexpr (N == 0) {
+    vmcnt_wait0();
+  } else {
+    if (n >= N) vmcnt_wait<N>(); else vmcnt_wait_le<N - 1>(n);
+  }
+}
+__device__ __forceinline__ void vmcnt_wait_dyn(int n) { vmcnt_wait_le<63>(min(n, 63)); }
+
 // ======================================================================= K1
-// One workgroup (4 wavefronts) per (tile of 32 token rows, K split).  Lane l
-// of a wavefront owns row l % 32 and half h = l / 32 of each group: 32 bf16
-// values read as four 16-byte loads.  The four wavefronts interleave groups.
-// Per group:  x_hat = fl32(x * iota);  a = max |x_hat| over 64 (two lanes);
-// s = a / 7, inv = 7 / a (correctly rounded), q = clamp(rint(x_hat inv), +-7),
-// stored as fp6 E2M3 (exact for these integers).
-// The raw bf16 values also feed a 32x32x16 bf16 MFMA against L1s^T, giving
-// the low-rank down-projection; the four wavefronts' partial products are
-// summed through LDS and written as this split's partial D.
+// One workgroup (4 wavefronts) per (tile of 32 token rows, K split).  The
+// split's groups are taken kK1Chunk = 4 at a time: the workgroup copies the
+// chunk's 32 rows x 512 bytes of X, and the chunk's 256 smoothing factors,
+// into LDS with the load unit's global->LDS path, each X copy instruction
+// moving two whole 512-byte row segments (long contiguous bursts for HBM);
+// wavefront w then quantises group w of the chunk.  Three chunk buffers are
+// in flight.  Inside a row segment the 16-byte pieces are permuted (piece p
+// stored at slot p ^ (row % 16)) so that the reads below, one row per lane,
+// hit 16 different bank quads.
+// Per group, lane l owns row l % 32 and half h = l / 32: its 32 values are
+// channels 16 j + 8 h + [0, 8) (j = 0..3).
+//   x_hat = fl32(x * iota);  a = max |x_hat| over 64 (two lanes);
+//   s = a / 7, inv = 7 / a (correctly rounded), q = rint(x_hat inv),
+// stored as fp6 E2M3 (exact for these integers).  The raw bf16 values also
+// feed a 32x32x16 bf16 MFMA against L1s^T for the low-rank down-projection;
+// the four wavefronts' partial products are summed through LDS and written
+// as this split's partial D.
+constexpr int kK1Chunk = 4;                        // groups per chunk = wavefronts
+constexpr int kK1RowBytes = kK1Chunk * kGroup * 2;  // 512
+constexpr int kK1XBytes = kTile * kK1RowBytes;     // 16 KB of X per chunk
+constexpr int kK1BufBytes = kK1XBytes + kK1Chunk * kGroup * 4;   // + 1 KB of 1/lambda
+constexpr int kK1Bufs = 3;
+constexpr int kK1LdsBytes = kK1Bufs * kK1BufBytes;
 template <int TB>   // rank_pad / 32
-__global__ __launch_bounds__(256) void k1_quantize_lowrank_down(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3 : 1))) void k1_quantize_lowrank_down(
     const uint16_t *__restrict__ X, int M, int K, int Mp, int S,
     const float *__restrict__ iota, const uint16_t *__restrict__ l1t,
     uint8_t *__restrict__ qa, float *__restrict__ sa, float *__restrict__ dpart) {
+  __shared__ __attribute__((aligned(16))) uint8_t k1_lds[kK1LdsBytes];
+  const uint32_t lds_u32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)k1_lds;
   const int t = blockIdx.x, s = blockIdx.y;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int G = K / kGroup, Gs = G / S, T = Mp / kTile;
-  const int row = t * kTile + (lane & 31), h = lane >> 5;
-  const bool valid = row < M;
+  const int rr = lane & 31, h = lane >> 5;
+  const int row = t * kTile + rr;
+  const int nch = (Gs + kK1Chunk - 1) / kK1Chunk;
   constexpr int NB = TB > 0 ? TB : 1;
+  constexpr int L1N = 4 * TB;                      // L1s^T loads per wave and chunk
+  const int ncopy = wu == 0 ? 5 : 4;               // copy instructions per wave and chunk
+  // Copy of chunk c: wave w issues X instructions i = 4w .. 4w+3; instruction
+  // i, lane l moves piece (l % 32) ^ (r % 16) of row r = 2i + l / 32.  Wave 0
+  // also copies the chunk's 1/lambda.  Rows past M (padding, never stored by
+  // the GEMM nor exported) repeat row M-1; groups past the split repeat its
+  // last group.
+  auto copy_chunk = [&](int c) {
+    const uint32_t dst = lds_u32 + (uint32_t)((c % kK1Bufs) * kK1BufBytes);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = 4 * wu + k;
+      const int r = 2 * i + (lane >> 5);
+      const int piece = (lane & 31) ^ (r & 15);
+      const int gq = s * Gs + min(c * kK1Chunk + (piece >> 3), Gs - 1);
+      const uint16_t *src = X + (int64_t)min(t * kTile + r, M - 1) * K + gq * kGroup + (piece & 7) * 8;
+      lds_dma16(src, dst + (uint32_t)(i * 1024));
+    }
+    if (wu == 0) {
+      const int gq = s * Gs + min(c * kK1Chunk + (lane >> 4), Gs - 1);
+      lds_dma16(iota + (int64_t)gq * kGroup + (lane & 15) * 4, dst + (uint32_t)kK1XBytes);
+    }
+  };
+  // L1s^T operand of this wavefront's group in chunk c (clamped; unused past the split)
+  uint4 lring[kK1Bufs][4 * NB];
+  auto load_l1 = [&](int c, uint4 (&d)[4 * NB]) {
+    if constexpr (TB > 0) {
+      const int g = s * Gs + min(c * kK1Chunk + wu, Gs - 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+          d[j * NB + b] = *reinterpret_cast<const uint4 *>(
+              l1t + (int64_t)(b * 32 + rr) * K + g * kGroup + 16 * j + 8 * h);
+    }
+  };
   v16f dacc[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) dacc[b] = v16f{};
 
-  // Register prefetch ring: each wavefront keeps the loads of its next
-  // K1_PF groups in flight while it quantises the current one.
-  constexpr int K1_PF = 3;
-  uint4 ring[K1_PF][4];
-  auto load_group = [&](int gi, uint4 (&dst)[4]) {
-    const uint16_t *xp = X + (int64_t)row * K + (s * Gs + gi) * kGroup + 8 * h;
+  // Vector-memory operations of one wavefront in issue order: copy(0)
+  // l1(0) copy(1) l1(1) copy(2) l1(2), then per chunk c: stores(c) [4],
+  // copy(c+3) l1(c+3).  Before chunk c it waits until copy(c) and l1(c) are
+  // done, leaving everything issued after them in flight, then the
+  // workgroup meets.
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dst[j] = valid ? *reinterpret_cast<const uint4 *>(xp + 16 * j) : make_uint4(0, 0, 0, 0);
-  };
+  for (int c = 0; c < kK1Bufs; ++c) {
+    if (c < nch) { copy_chunk(c); load_l1(c, lring[c]); }
+  }
+  for (int c0 = 0; c0 < nch; c0 += kK1Bufs)
 #pragma unroll
-  for (int p = 0; p < K1_PF; ++p)
-    if (w + 4 * p < Gs) load_group(w + 4 * p, ring[p]);
-
-  for (int base = w; base < Gs; base += 4 * K1_PF)
-#pragma unroll
-  for (int p = 0; p < K1_PF; ++p) {
-    const int gi = base + 4 * p;
-    if (gi >= Gs) break;
-    const int g = s * Gs + gi;
+  for (int u = 0; u < kK1Bufs; ++u) {
+    const int c = c0 + u;
+    if (c >= nch) break;
+    int later = (c >= 2 ? 4 : 0) + (c >= 1 ? 4 : 0);
+    if (c + 1 < nch) later += ncopy + L1N;
+    if (c + 2 < nch) later += ncopy + L1N;
+    vmcnt_wait_dyn(later);
+    __syncthreads();
+    const uint8_t *buf = k1_lds + u * kK1BufBytes;
+    const float4 *iota_c = reinterpret_cast<const float4 *>(buf + kK1XBytes) + wu * 16;
+    const int gi = c * kK1Chunk + wu;              // this wavefront's group in the split
+    const bool live = gi < Gs;                     // uniform across the wavefront
+    const int g = s * Gs + min(gi, Gs - 1);
+    const uint8_t *xb = buf + rr * kK1RowBytes;
     uint4 xr[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xr[j] = ring[p][j];
-    if (gi + 4 * K1_PF < Gs) load_group(gi + 4 * K1_PF, ring[p]);
+    for (int j = 0; j < 4; ++j) {
+      const int piece = wu * 8 + 2 * j + h;
+      xr[j] = *reinterpret_cast<const uint4 *>(xb + ((piece ^ (rr & 15)) << 4));
+    }
     float xh[32];
     float a = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float4 i0 = *reinterpret_cast<const float4 *>(iota + g * kGroup + 16 * j + 8 * h);
-      const float4 i1 = *reinterpret_cast<const float4 *>(iota + g * kGroup + 16 * j + 8 * h + 4);
+      const float4 i0 = iota_c[4 * j + 2 * h];
+      const float4 i1 = iota_c[4 * j + 2 * h + 1];
       const uint32_t wv[4] = {xr[j].x, xr[j].y, xr[j].z, xr[j].w};
       const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
 #pragma unroll
@@ -131,36 +219,37 @@ __global__ __launch_bounds__(256) void k1_quantize_lowrank_down(
     }
     // codes as fp6 E2M3: the hardware packer interleaves its two 16-value
     // inputs (field 2i from the first, 2i+1 from the second), so even and odd
-    // elements go in to get element order 0..31 at bits 6c.
+    // elements go in to get element order 0..31 at bits 6c.  No clamp to
+    // [-7, 7] is needed: |x_hat| <= a and inv <= (7/a)(1 + 2^-24) give
+    // |fl32(x_hat inv)| < 7.0000009, which rounds to at most 7.
     v16f ev, od;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      float q0 = rintf(__fmul_rn(xh[2 * c], inv));
-      float q1 = rintf(__fmul_rn(xh[2 * c + 1], inv));
-      ev[c] = fminf(7.0f, fmaxf(-7.0f, q0));
-      od[c] = fminf(7.0f, fmaxf(-7.0f, q1));
+    for (int cc = 0; cc < 16; ++cc) {
+      ev[cc] = rintf(__fmul_rn(xh[2 * cc], inv));
+      od[cc] = rintf(__fmul_rn(xh[2 * cc + 1], inv));
     }
     const v6u packed = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
     uint8_t *qp = qa + pair_offset(g, t, T, lane, 0);
 #pragma unroll
     for (int j = 0; j < 3; ++j)
       *reinterpret_cast<uint2 *>(qp + 512 * j) = make_uint2(packed[2 * j], packed[2 * j + 1]);
-    if (h == 0) sa[(int64_t)g * Mp + row] = sc;
-    if constexpr (TB > 0) {
+    sa[(int64_t)g * Mp + row] = sc;              // both halves hold the same scale
+    if (TB > 0 && live) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const v8bf av = as_v8bf(xr[j]);
 #pragma unroll
-        for (int b = 0; b < TB; ++b) {
-          const uint4 lw = *reinterpret_cast<const uint4 *>(
-              l1t + (int64_t)(b * 32 + (lane & 31)) * K + g * kGroup + 16 * j + 8 * h);
-          dacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, as_v8bf(lw), dacc[b], 0, 0, 0);
-        }
+        for (int b = 0; b < TB; ++b)
+          dacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, as_v8bf(lring[u][j * NB + b]), dacc[b], 0, 0, 0);
       }
     }
+    __syncthreads();                               // buffer u is free again
+    if (c + kK1Bufs < nch) { copy_chunk(c + kK1Bufs); load_l1(c + kK1Bufs, lring[u]); }
   }
   if constexpr (TB > 0) {
-    __shared__ float red[4][16][64];
+    // the copy buffers are free now: the four wavefronts' partial products
+    // meet there (4 x 16 x 64 floats = 16 KB)
+    float (*red)[16][64] = reinterpret_cast<float (*)[16][64]>(k1_lds);
     constexpr int RP = TB * 32;
     for (int b = 0; b < TB; ++b) {
 #pragma unroll
@@ -177,22 +266,6 @@ __global__ __launch_bounds__(256) void k1_quantize_lowrank_down(
     }
   }
 }
-
-// Global -> LDS copy of 16 bytes per lane by the load unit
-// (global_load_lds_dwordx4): lane i writes LDS address lds_base + 16 i.
-// lds_base must be uniform across the wavefront.  Written as inline asm so
-// that the copy's completion is tracked by the caller's own vmcnt waits
-// (the compiler would otherwise wait for every copy before any LDS read).
-// The asm has no register outputs; M0 is set and used inside the block.
-__device__ __forceinline__ void lds_dma16(const void *gsrc, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(gsrc), "s"(lds_base) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void vmcnt_wait() {
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-__device__ __forceinline__ void vmcnt_wait0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ======================================================================= K2
 // INT4 x INT4 group GEMM with per-group fp32 scaling.
@@ -418,44 +491,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // the vector ALU, the matrix core works on tile t + 1 (the next group's
   // first tile after t = 3).  Each operand of group g + 1 is read from LDS
   // into its registers right after the last instruction of group g that
-  // uses them, one to three tiles before it is needed.  A barrier every
-  // second group: at even g every wave waits for stages g+1 and g+2, meets
-  // the others, and requests stages g+5 and g+6 (the buffers of stages g-1
-  // and g, which every wave has read before this barrier).  The scheduling
-  // fences keep each step's products from being hoisted above the FMAs that
-  // still read the registers they overwrite.  After the last group the
-  // loads and the first product still run, on a stale but in-bounds LDS
-  // buffer, and their results are never used: branch-free code keeps the
-  // operands and products in fixed registers.
+  // uses them, one to three tiles before it is needed.  The matrix
+  // instructions are issued at raised wave priority so the SIMD's other
+  // wavefront does not delay them.  A barrier every third group: at
+  // g = 0 mod 3 every wave waits for its copies of stages g+1..g+3, meets
+  // the others, and requests stages g+4..g+6 (the buffers of stages g-2..g,
+  // which every wave has read before this barrier); the six buffers hold
+  // stages g+1..g+6.  The scheduling fences keep each step's products from
+  // being hoisted above the FMAs that still read the registers they
+  // overwrite.  After the last group the loads and the first product still
+  // run, on a stale but in-bounds LDS buffer, and their results are never
+  // used: branch-free code keeps the operands and products in fixed
+  // registers.
   v16f Pa, Pb;
   v32f S0, S1;
-  for (int g = 0; g < NBUF - 1 && g < G; ++g) fetch(g);
-  wait_stage(min(NBUF - 2, G - 1));
+  for (int g = 0; g < 4 && g < G; ++g) fetch(g);
+  wait_stage(min(3, G - 1));
   __syncthreads();
   load_a(0, 0); load_a(0, 1); load_b(0, 0); load_b(0, 1);
   load_sa(0, 0); load_sa(0, 1); load_sw(0);
   mm(0, Pa, S0);
   for (int g = 0; g < G; ++g) {
     const bool nx = g + 1 < G;
-    if ((g & 1) == 0 && nx) {
-      wait_stage(min(g + 4, G - 1) - min(g + 2, G - 1));
+    if ((g % 3) == 0 && nx) {
+      wait_stage(0);
       __syncthreads();
+      if (g + 4 < G) fetch(g + 4);
       if (g + 5 < G) fetch(g + 5);
       if (g + 6 < G) fetch(g + 6);
     }
+    __builtin_amdgcn_s_setprio(1);
     mm(1, Pb, S0);                                  // tile (0,1): last use of a0
+    __builtin_amdgcn_s_setprio(0);
     load_a(g + 1, 0); load_sa(g + 1, 0);
     consume(0, g, Pa, S0);
     k2_order<1, 0>();
+    __builtin_amdgcn_s_setprio(1);
     mm(2, Pa, S1);                                  // tile (1,0) + row 1 scales: last use of b0, sa1, sw
+    __builtin_amdgcn_s_setprio(0);
     load_b(g + 1, 0); load_sa(g + 1, 1); load_sw(g + 1);
     consume(1, g, Pb, S0);
     k2_order<2, 4>();
+    __builtin_amdgcn_s_setprio(1);
     mm(3, Pb, S1);                                  // tile (1,1): last use of a1, b1
+    __builtin_amdgcn_s_setprio(0);
     load_a(g + 1, 1); load_b(g + 1, 1);
     consume(2, g, Pa, S1);
     k2_order<1, 0>();
+    __builtin_amdgcn_s_setprio(1);
     mm(0, Pa, S0);                                  // next group's tile (0,0) + row 0 scales
+    __builtin_amdgcn_s_setprio(0);
     consume(3, g, Pb, S1);
     k2_order<2, 4>();
   }
@@ -554,16 +639,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // ======================================================================= K3
 // AWQ W4A16.  A workgroup of 4 wavefronts owns a tile of 16 output channels;
-// wavefront w takes a contiguous quarter of the groups of 64 input channels
-// and issues the loads of 8 groups before it computes any of them, so every
-// CU keeps tens of kilobytes of weight reads in flight.  For each group,
-// lane l (channel l % 16, quarter q = l / 16) turns its 16 codes into fp16
-// (q - z) with the 1024-offset trick (0x6400 | code is the fp16 value
+// wavefront w takes a contiguous quarter of the groups of 64 input channels.
+// It issues all its activation loads (a few kilobytes shared by every
+// workgroup, so cache hits) and then all its code and scale loads (the HBM
+// stream), up to kAwqChunk groups at once, and waits once: every load is
+// unconditional (indices clamped) so the completion count is exact.  For each
+// group, lane l (channel l % 16, quarter q = l / 16) turns its 16 codes into
+// fp16 (q - z) with the 1024-offset trick (0x6400 | code is the fp16 value
 // 1024 + code; subtracting 1024 + z is exact), the activations [16, 64] are
 // the A operand, and two v_mfma_f32_16x16x32_f16 give the group's inner
-// sums; acc += s * sum in fp32.  Rows m >= M are zero.  The four partial
-// sums meet in LDS, in a fixed order.
-constexpr int kAwqChunk = 8;
+// sums; acc += s * sum in fp32.  Rows m >= M repeat row M - 1 and are never
+// stored.  The four partial sums meet in LDS, in a fixed order.
+constexpr int kAwqChunk = 12;
 __global__ __launch_bounds__(256) void k3_awq_w4a16(const uint8_t *__restrict__ qd,
                                                      const uint32_t *__restrict__ sz,
                                                      const uint16_t *__restrict__ x, int M,
@@ -578,30 +665,28 @@ __global__ __launch_bounds__(256) void k3_awq_w4a16(const uint8_t *__restrict__ 
   const int m = lane & 15, qtr = lane >> 4;
   const int n = tile * kAwqTile + (lane & 15);
   const uint8_t *qbase = qd + (int64_t)tile * G * kAwqBlockBytes + lane * 8;
-  const uint16_t *xrow = x + (int64_t)m * K + 16 * qtr;
+  const uint16_t *xrow = x + (int64_t)min(m, M - 1) * K + 16 * qtr;
   v4f acc = v4f{};
   for (int gc = g0; gc < g1; gc += kAwqChunk) {
+    uint4 xa[kAwqChunk][2];
     uint2 cw[kAwqChunk];
     uint32_t szw[kAwqChunk];
 #pragma unroll
     for (int i = 0; i < kAwqChunk; ++i) {
-      const int g = gc + i;
-      if (g < g1) {
-        cw[i] = *reinterpret_cast<const uint2 *>(qbase + (int64_t)g * kAwqBlockBytes);
-        szw[i] = sz[(int64_t)g * Np + n];
-      } else {
-        cw[i] = make_uint2(0, 0);
-        szw[i] = 0;
-      }
+      const int gg = min(gc + i, g1 - 1);
+      xa[i][0] = *reinterpret_cast<const uint4 *>(xrow + gg * kGroup);
+      xa[i][1] = *reinterpret_cast<const uint4 *>(xrow + gg * kGroup + 8);
     }
 #pragma unroll
     for (int i = 0; i < kAwqChunk; ++i) {
-      // the activations are a few kilobytes shared by every workgroup: L2 hits
-      uint4 xa[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-      if (gc + i < g1 && m < M) {
-        xa[0] = *reinterpret_cast<const uint4 *>(xrow + (gc + i) * kGroup);
-        xa[1] = *reinterpret_cast<const uint4 *>(xrow + (gc + i) * kGroup + 8);
-      }
+      const int gg = min(gc + i, g1 - 1);
+      cw[i] = *reinterpret_cast<const uint2 *>(qbase + (int64_t)gg * kAwqBlockBytes);
+      szw[i] = sz[(int64_t)gg * Np + n];
+    }
+    __builtin_amdgcn_sched_barrier(0);         // keep every load ahead of the math
+#pragma unroll
+    for (int i = 0; i < kAwqChunk; ++i) {
+      if (gc + i < g1) {                       // uniform across the wavefront
       const _Float16 zf = __builtin_bit_cast(_Float16, (uint16_t)(szw[i] >> 16));
       const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)(szw[i] & 0xFFFF));
       const _Float16 off = -((_Float16)1024.0f + zf);
@@ -618,13 +703,14 @@ __global__ __launch_bounds__(256) void k3_awq_w4a16(const uint8_t *__restrict__ 
           bop[half][2 * j + 1] = v.y;
         }
       }
-      v4f part = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, xa[0]), bop[0],
+      v4f part = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, xa[i][0]), bop[0],
                                                        v4f{}, 0, 0, 0);
-      part = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, xa[1]), bop[1], part,
+      part = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, xa[i][1]), bop[1], part,
                                                    0, 0, 0);
       // output layout: lane holds rows 4 * (lane / 16) + e, column lane % 16
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(part[e], sf, acc[e]);
+      }
     }
   }
   __shared__ v4f red[4][64];
@@ -772,10 +858,11 @@ svdq_status_t launch_k1(const WeightLayout &L, const WorkLayout &Wl, const svdq_
   float *sa = reinterpret_cast<float *>(ws + Wl.sa);
   float *dp = reinterpret_cast<float *>(ws + Wl.d);
   const int K = w->K, Mp = (int)Wl.Mp, S = (int)Wl.S;
+  const size_t lds = 0;
   switch (L.rp / 32) {
 #define K1_CASE(TB)                                                                       \
   case TB:                                                                                \
-    hipLaunchKernelGGL(k1_quantize_lowrank_down<TB>, grid, dim3(256), 0, st, x, M, K, Mp, \
+    hipLaunchKernelGGL(k1_quantize_lowrank_down<TB>, grid, dim3(256), lds, st, x, M, K, Mp, \
                        S, iota, l1t, qa, sa, dp);                                         \
     break;
     K1_CASE(0) K1_CASE(1) K1_CASE(2) K1_CASE(3) K1_CASE(4) K1_CASE(5) K1_CASE(6) K1_CASE(7)
