@@ -270,25 +270,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
 // ======================================================================= K2
 // INT4 x INT4 group GEMM with per-group fp32 scaling.
 //
-// Workgroup: 8 wavefronts, output tile 256 x 128; wavefront tile 64 x 64
-// (2 x 2 MFMA tiles of 32 x 32).  One pipeline stage holds two groups of 64
-// input channels (A codes, B codes, their fp32 scales) in LDS, double
-// buffered: the next stage's global loads are issued before the current
-// stage is consumed and written to LDS after it.
+// Workgroup: 4 wavefronts (2 x 2), output tile 128 x 128; wavefront tile
+// 64 x 64 (2 x 2 MFMA tiles of 32 x 32).  Two workgroups share a CU, so each
+// SIMD runs wavefronts of two independent workgroups.  One pipeline stage
+// holds one group of 64 input channels in LDS (A codes, B codes, their fp32
+// scales), copied global -> LDS by the load unit; six stages rotate.
 //
 // Per 32 x 32 tile and group:
 //   P  = v_mfma_scale_f32_32x32x64_f8f6f4 on fp6 codes (unit block scales):
 //        the exact int32 group sums, delivered as fp32 (|P| <= 3136)
-//   S  = v_mfma_f32_32x32x1_2b_f32: the outer product sA[m,g] sW[n,g] for
-//        two groups at once (one IEEE fp32 product per element)
-//   acc = fma(P, S, acc)                  (the only VALU work per element)
+//   acc = fma(P, fl32(sA[m] sW[n]), acc)        (two VALU ops per element)
 // The epilogue adds the low-rank up-projection D L2 on bf16 MFMA (D split
 // into a bf16 high part and a bf16 remainder), the bias, the optional GELU,
 // and stores bf16 or fp32.  MODE_SUMS stores P for a window instead.
 //
 // Tile order: workgroups are dealt round-robin to the 8 XCDs, so block id b
 // runs on XCD b % 8; each XCD is given a contiguous range of tiles, walked
-// four tile-rows at a time, so the A and B panels its CUs share stay in its
+// GM tile-rows at a time, so the A and B panels its CUs share stay in its
 // L2.
 enum { MODE_FWD = 0, MODE_SUMS = 1 };
 
@@ -298,7 +296,7 @@ struct K2Args {
   int N, Np, K, rp;
   void *Y;
   int32_t *P; int m0, mcount, n0, ncount;
-  int tile_m0, tile_n0, TM, TN;     // tile grid (units of 256 x 128)
+  int tile_m0, tile_n0, TM, TN;     // tile grid (units of the workgroup tile)
 };
 
 namespace k2c {
@@ -320,23 +318,8 @@ static_assert(2 * NBUF * STAGE <= 160 * 1024, "two workgroups must fit in one CU
 }  // namespace k2c
 
 // Stage layout in LDS (one group of 64 input channels):
-//   A codes [8 blocks][1536] | B codes [4 blocks][1536] | sA [256] | sW [128]
-// Unit u (16 bytes) of the stage sits at LDS byte 16 u; its global source:
-__device__ __forceinline__ const uint4 *k2_unit_src(const K2Args &p, int g, int u, int bm, int bn,
-                                                   int Ta, int Tw) {
-  using namespace k2c;
-  int off = u * 16;
-  if (off < A_BYTES)
-    return reinterpret_cast<const uint4 *>(p.qa + ((int64_t)g * Ta + bm / kTile) * kBlockBytes + off);
-  off -= A_BYTES;
-  if (off < B_BYTES)
-    return reinterpret_cast<const uint4 *>(p.qw + ((int64_t)g * Tw + bn / kTile) * kBlockBytes + off);
-  off -= B_BYTES;
-  if (off < SA_BYTES)
-    return reinterpret_cast<const uint4 *>(p.sa + (int64_t)g * p.Mp + bm + off / 4);
-  off -= SA_BYTES;
-  return reinterpret_cast<const uint4 *>(p.sw + (int64_t)g * p.Np + bn + off / 4);
-}
+//   A codes [BM / 32 blocks][1536] | B codes [BN / 32 blocks][1536] | sA [BM] | sW [BN]
+// padded to whole wavefront loads of 64 x 16 bytes.
 
 // The fp6 operand occupies six registers; the instruction's 8-register
 // operand slot leaves the last two unread, so they are left undefined
@@ -352,18 +335,16 @@ __device__ __forceinline__ v8i k2_frag(const uint8_t *blk, int lane) {
 }
 
 // Instruction order inside one step of K2's pipeline: the step's matrix
-// instruction(s) first (the second one after `gap` vector instructions),
-// then its LDS reads, then the FMAs, and a fence so nothing crosses into the
-// next step.  This keeps the matrix core busy under the FMAs.
-template <int NMFMA, int GAP>
+// instruction first, then D1 LDS reads (operands it no longer needs), the
+// vector work, then D2 more LDS reads (scales the vector work has just used
+// for the last time), and a fence so nothing crosses into the next step.
+// This keeps the matrix core busy under the FMAs.
+template <int D1, int D2>
 __device__ __forceinline__ void k2_order() {
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  if constexpr (NMFMA == 2) {
-    __builtin_amdgcn_sched_group_barrier(0x002, GAP, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+  if constexpr (D1 > 0) __builtin_amdgcn_sched_group_barrier(0x100, D1, 0);
   __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
+  if constexpr (D2 > 0) __builtin_amdgcn_sched_group_barrier(0x100, D2, 0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -446,10 +427,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   // Operands of one group as a wavefront holds them in registers: the fp6
-  // codes of its two row tiles and two column tiles, and the scales for the
-  // outer products (block 0, lanes 0-31, pairs a row tile with column tile
-  // 0; block 1, lanes 32-63, with column tile 1).
-  struct Frags { v8i a[2], b[2]; float sa[2], sw; };
+  // codes of its two row tiles and two column tiles, the activation scales
+  // of the 16 rows each lane's accumulator elements belong to (per row tile:
+  // rows 8 q + 4 (lane / 32) + [0, 4), q = 0..3, four float4 reads), and the
+  // weight scale of the lane's column in each column tile.
+  struct Frags { v8i a[2], b[2]; float4 sa[2][4]; float sw[2]; };
   Frags F;
   auto stage_of = [&](int g) { return smem + (g % NBUF) * STAGE; };
   auto load_a = [&](int g, int i) { F.a[i] = k2_frag(stage_of(g) + (2 * wmi + i) * kBlockBytes, lane); };
@@ -457,21 +439,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     F.b[j] = k2_frag(stage_of(g) + A_BYTES + (2 * wni + j) * kBlockBytes, lane);
   };
   auto load_sa = [&](int g, int i) {
-    F.sa[i] = reinterpret_cast<const float *>(stage_of(g) + A_BYTES + B_BYTES)[64 * wmi + 32 * i + ln];
+    const float4 *lsa = reinterpret_cast<const float4 *>(stage_of(g) + A_BYTES + B_BYTES) +
+                        (64 * wmi + 32 * i + 4 * hl) / 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) F.sa[i][q] = lsa[2 * q];
   };
-  auto load_sw = [&](int g) {
-    F.sw = reinterpret_cast<const float *>(stage_of(g) + A_BYTES + B_BYTES + SA_BYTES)[64 * wni + 32 * hl + ln];
+  auto load_sw = [&](int g, int j) {
+    F.sw[j] = reinterpret_cast<const float *>(stage_of(g) + A_BYTES + B_BYTES + SA_BYTES)[64 * wni + 32 * j + ln];
   };
   // Per group the wavefront's four 32 x 32 tiles t = (i, j) = (t / 2, t % 2)
-  // each take one fp6 product; each row tile takes one outer product of
-  // scales, issued with its first tile.
-  auto mm = [&](int t, v16f &P, v32f &Sr) {
+  // each take one fp6 product; its elements are then scaled by the fp32
+  // product sA[m] sW[n] (one rounding) and accumulated with one FMA.
+  auto mm = [&](int t, v16f &P) {
     const int i = t >> 1, j = t & 1;
     P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[i], F.b[j], v16f{}, 2, 2, 0, 127, 0, 127);
-    if constexpr (MODE == MODE_FWD)
-      if (j == 0) Sr = __builtin_amdgcn_mfma_f32_32x32x1f32(F.sa[i], F.sw, v32f{}, 0, 0, 0);
   };
-  auto consume = [&](int t, int g, const v16f &P, const v32f &Sr) {
+  auto consume = [&](int t, int g, const v16f &P) {
     const int i = t >> 1, j = t & 1;
     if constexpr (MODE == MODE_SUMS) {
       const int n = wn + 32 * j + ln;
@@ -482,8 +465,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           p.P[((int64_t)(m - p.m0) * p.ncount + (n - p.n0)) * G + g] = (int32_t)P[e];
       }
     } else {
+      const float swj = F.sw[j];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = __builtin_fmaf(P[e], Sr[16 * j + e], acc[i][j][e]);
+      for (int q = 0; q < 4; ++q) {
+        const float4 sa4 = F.sa[i][q];
+        const float sv[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int e = 4 * q + k;
+          acc[i][j][e] = __builtin_fmaf(P[e], __fmul_rn(sv[k], swj), acc[i][j][e]);
+        }
+      }
     }
   };
 
@@ -504,13 +496,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // used: branch-free code keeps the operands and products in fixed
   // registers.
   v16f Pa, Pb;
-  v32f S0, S1;
   for (int g = 0; g < 4 && g < G; ++g) fetch(g);
   wait_stage(min(3, G - 1));
   __syncthreads();
   load_a(0, 0); load_a(0, 1); load_b(0, 0); load_b(0, 1);
-  load_sa(0, 0); load_sa(0, 1); load_sw(0);
-  mm(0, Pa, S0);
+  load_sa(0, 0); load_sa(0, 1); load_sw(0, 0); load_sw(0, 1);
+  mm(0, Pa);
   for (int g = 0; g < G; ++g) {
     const bool nx = g + 1 < G;
     if ((g % 3) == 0 && nx) {
@@ -521,28 +512,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (g + 6 < G) fetch(g + 6);
     }
     __builtin_amdgcn_s_setprio(1);
-    mm(1, Pb, S0);                                  // tile (0,1): last use of a0
+    mm(1, Pb);                                      // tile (0,1): last use of a0
     __builtin_amdgcn_s_setprio(0);
-    load_a(g + 1, 0); load_sa(g + 1, 0);
-    consume(0, g, Pa, S0);
-    k2_order<1, 0>();
+    load_a(g + 1, 0);
+    consume(0, g, Pa);
+    k2_order<3, 0>();
     __builtin_amdgcn_s_setprio(1);
-    mm(2, Pa, S1);                                  // tile (1,0) + row 1 scales: last use of b0, sa1, sw
+    mm(2, Pa);                                      // tile (1,0): last use of b0
     __builtin_amdgcn_s_setprio(0);
-    load_b(g + 1, 0); load_sa(g + 1, 1); load_sw(g + 1);
-    consume(1, g, Pb, S0);
-    k2_order<2, 4>();
+    load_b(g + 1, 0);
+    consume(1, g, Pb);                              // last use of sa0
+    load_sa(g + 1, 0);
+    k2_order<3, 4>();
     __builtin_amdgcn_s_setprio(1);
-    mm(3, Pb, S1);                                  // tile (1,1): last use of a1, b1
+    mm(3, Pb);                                      // tile (1,1): last use of a1, b1
     __builtin_amdgcn_s_setprio(0);
     load_a(g + 1, 1); load_b(g + 1, 1);
-    consume(2, g, Pa, S1);
-    k2_order<1, 0>();
+    consume(2, g, Pa);                              // last use of sw0
+    load_sw(g + 1, 0);
+    k2_order<6, 1>();
     __builtin_amdgcn_s_setprio(1);
-    mm(0, Pa, S0);                                  // next group's tile (0,0) + row 0 scales
+    mm(0, Pa);                                      // next group's tile (0,0)
     __builtin_amdgcn_s_setprio(0);
-    consume(3, g, Pb, S1);
-    k2_order<2, 4>();
+    consume(3, g, Pb);                              // last use of sa1, sw1
+    load_sa(g + 1, 1); load_sw(g + 1, 1);
+    k2_order<0, 5>();
   }
 
   if constexpr (MODE == MODE_FWD) {
