@@ -68,6 +68,12 @@ __device__ __forceinline__ void lds_dma16(const void *gsrc, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(gsrc), "s"(lds_base) : "memory");
 }
+// The same copy with a wave-uniform base address in scalar registers and a
+// 32-bit per-lane byte offset.
+__device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
+}
 template <int N>
 __device__ __forceinline__ void vmcnt_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
@@ -270,11 +276,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
 // ======================================================================= K2
 // INT4 x INT4 group GEMM with per-group fp32 scaling.
 //
-// Workgroup: 4 wavefronts (2 x 2), output tile 128 x 128; wavefront tile
-// 64 x 64 (2 x 2 MFMA tiles of 32 x 32).  Two workgroups share a CU, so each
-// SIMD runs wavefronts of two independent workgroups.  One pipeline stage
-// holds one group of 64 input channels in LDS (A codes, B codes, their fp32
-// scales), copied global -> LDS by the load unit; six stages rotate.
+// Workgroup: 4 wavefronts (2 x 2), output tile 128 x 256; wavefront tile
+// 64 x 128 (2 x 4 MFMA tiles of 32 x 32).  Two workgroups share a CU, so
+// each SIMD runs wavefronts of two independent workgroups.  One pipeline
+// stage holds one group of 64 input channels in LDS (A codes, B codes, their
+// fp32 scales), copied global -> LDS by the load unit; four stages rotate.
+// Per group a workgroup copies 20 KB for 32768 outputs.
 //
 // Per 32 x 32 tile and group:
 //   P  = v_mfma_scale_f32_32x32x64_f8f6f4 on fp6 codes (unit block scales):
@@ -300,26 +307,29 @@ struct K2Args {
 };
 
 namespace k2c {
-constexpr int BM = 128, BN = 128, THREADS = 256, NWAVES = THREADS / 64;
+constexpr int WTM = 2, WTN = 4;                   // MFMA tiles per wavefront (rows, columns)
+constexpr int WROWS = 32 * WTM, WCOLS = 32 * WTN; // 64 x 128
+constexpr int BM = 2 * WROWS, BN = 2 * WCOLS, THREADS = 256, NWAVES = THREADS / 64;
 constexpr int A_BLK = BM / kTile, B_BLK = BN / kTile;
 constexpr int A_BYTES = A_BLK * kBlockBytes;     // one group per stage
 constexpr int B_BYTES = B_BLK * kBlockBytes;
 constexpr int SA_BYTES = BM * 4, SW_BYTES = BN * 4;
-constexpr int STAGE_USED = A_BYTES + B_BYTES + SA_BYTES + SW_BYTES;   // 13312
-constexpr int UNITS = STAGE_USED / 16;                                 // 832
-constexpr int WAVE_LOADS = (UNITS + 63) / 64;                          // 13
-constexpr int STAGE = WAVE_LOADS * 64 * 16;                            // 13312
-constexpr int MAX_LOADS = (WAVE_LOADS + NWAVES - 1) / NWAVES;          // 4 per wave
-constexpr int NBUF = 6;                                                // stages in LDS
+constexpr int STAGE_USED = A_BYTES + B_BYTES + SA_BYTES + SW_BYTES;   // 19968
+constexpr int UNITS = STAGE_USED / 16;                                 // 1248
+constexpr int WAVE_LOADS = (UNITS + 63) / 64;                          // 20
+constexpr int STAGE = WAVE_LOADS * 64 * 16;                            // 20480, padded
+constexpr int MAX_LOADS = WAVE_LOADS / NWAVES;                         // 5 per wave
+constexpr int NBUF = 4;                                                // stages in LDS
 constexpr int GM = 8;             // tile-rows walked together on one XCD
+constexpr int EPI_WAVE_BYTES = 32 * WCOLS * 4;   // one 32-row half of a wavefront tile, fp32
 static_assert(STAGE_USED % 16 == 0, "stage must be whole 16-byte units");
-static_assert(MAX_LOADS <= 4, "vmcnt waits below assume at most 4 copies per wave and stage");
+static_assert(WAVE_LOADS % NWAVES == 0, "every wavefront issues the same number of copies per stage");
+static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0 && SW_BYTES % 1024 == 0 && SA_BYTES == 512 &&
+              WAVE_LOADS * 1024 == A_BYTES + B_BYTES + SW_BYTES + 1024,
+              "each copy reads one array; sA is the upper half of the last");
 static_assert(2 * NBUF * STAGE <= 160 * 1024, "two workgroups must fit in one CU's LDS");
+static_assert(NWAVES * EPI_WAVE_BYTES <= NBUF * STAGE, "epilogue staging reuses the stages");
 }  // namespace k2c
-
-// Stage layout in LDS (one group of 64 input channels):
-//   A codes [BM / 32 blocks][1536] | B codes [BN / 32 blocks][1536] | sA [BM] | sW [BN]
-// padded to whole wavefront loads of 64 x 16 bytes.
 
 // The fp6 operand occupies six registers; the instruction's 8-register
 // operand slot leaves the last two unread, so they are left undefined
@@ -348,6 +358,22 @@ __device__ __forceinline__ void k2_order() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// As k2_order, for a step whose vector work swaps the activation scales for
+// the next row tile: each of the four float4 reads goes right after the FMAs
+// that last read the register it overwrites.
+template <int D1, int D2 = 0>
+__device__ __forceinline__ void k2_order_r() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  if constexpr (D1 > 0) __builtin_amdgcn_sched_group_barrier(0x100, D1, 0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  if constexpr (D2 > 0) __builtin_amdgcn_sched_group_barrier(0x100, D2, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int MODE, int EPI, bool OUT_F32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_w4a4_gemm(K2Args p) {
   using namespace k2c;
@@ -365,97 +391,90 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * STAGE];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int wmi = w >> 1, wni = w & 1;
-  const int wm = bm + 64 * wmi, wn = bn + 64 * wni;
+  const int wu = __builtin_amdgcn_readfirstlane(w);      // wavefront index, scalar
+  const int wmi = wu >> 1, wni = wu & 1;
+  const int wm = bm + WROWS * wmi, wn = bn + WCOLS * wni;
   const int G = p.K / kGroup;
   const int Ta = p.Mp / kTile, Tw = p.Np / kTile;
   const int hl = lane >> 5, ln = lane & 31;
 
-  v16f acc[2][2];
+  v16f acc[WTM][WTN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WTM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+    for (int j = 0; j < WTN; ++j) acc[i][j] = v16f{};
 
-  // Copy schedule: a stage is WAVE_LOADS wavefront-loads of 64 x 16 bytes;
-  // wave w issues loads w, w + 4, w + 8, ... with every lane active, so the
-  // number of copies a wave has in flight per stage (nload) is fixed and the
-  // vmcnt waits below count exactly.  Units past the stage (if any) re-read
-  // the A panel into the padding.
-  const int wu = __builtin_amdgcn_readfirstlane(w);      // wavefront index, scalar
-  const int nload = (WAVE_LOADS - wu + NWAVES - 1) / NWAVES;
+  // Copy schedule: a stage is WAVE_LOADS wavefront-loads of 64 x 16 bytes,
+  // A codes | B codes | sW | sA, each load from one array: wave w issues
+  // loads w, w + 4, w + 8, ... with every lane active; the last load's upper
+  // half repeats sA into the padding.  A load's source is a wave-uniform
+  // base (scalar registers) plus the lane's byte offset, and advances by one
+  // row of blocks (codes) or one row of the [G][Mp] / [G][Np] scale arrays
+  // from one group to the next.
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
-  // per copy slot: source of group 0 and the byte stride from one group to
-  // the next (A and B panels advance by a row of blocks, the scales by a row
-  // of the [G][Mp] / [G][Np] arrays)
-  const uint8_t *src0[MAX_LOADS];
+  const uint8_t *sbase[MAX_LOADS];
   int64_t sstride[MAX_LOADS];
 #pragma unroll
   for (int r = 0; r < MAX_LOADS; ++r) {
-    const int u = 64 * (wu + NWAVES * r) + lane;
-    const int off = u * 16;
-    if (u >= UNITS || off < A_BYTES) {
-      src0[r] = p.qa + (int64_t)(bm / kTile) * kBlockBytes + (u < UNITS ? off : 0);
+    const int L = wu + NWAVES * r;               // load index within the stage
+    if (L < A_BYTES / 1024) {
+      sbase[r] = p.qa + (int64_t)(bm / kTile) * kBlockBytes + 1024 * L;
       sstride[r] = (int64_t)Ta * kBlockBytes;
-    } else if (off < A_BYTES + B_BYTES) {
-      src0[r] = p.qw + (int64_t)(bn / kTile) * kBlockBytes + (off - A_BYTES);
+    } else if (L < (A_BYTES + B_BYTES) / 1024) {
+      sbase[r] = p.qw + (int64_t)(bn / kTile) * kBlockBytes + 1024 * (L - A_BYTES / 1024);
       sstride[r] = (int64_t)Tw * kBlockBytes;
-    } else if (off < A_BYTES + B_BYTES + SA_BYTES) {
-      src0[r] = reinterpret_cast<const uint8_t *>(p.sa + bm) + (off - A_BYTES - B_BYTES);
-      sstride[r] = (int64_t)p.Mp * 4;
-    } else {
-      src0[r] = reinterpret_cast<const uint8_t *>(p.sw + bn) + (off - A_BYTES - B_BYTES - SA_BYTES);
+    } else if (L < (A_BYTES + B_BYTES + SW_BYTES) / 1024) {
+      sbase[r] = reinterpret_cast<const uint8_t *>(p.sw + bn) + 1024 * (L - (A_BYTES + B_BYTES) / 1024);
       sstride[r] = (int64_t)p.Np * 4;
+    } else {
+      sbase[r] = reinterpret_cast<const uint8_t *>(p.sa + bm);
+      sstride[r] = (int64_t)p.Mp * 4;
     }
   }
+  const uint32_t voff = 16u * lane;
+  const uint32_t voff_sa = 16u * (lane & 31);     // sA is half a load
   auto fetch = [&](int g) {
     const uint32_t buf = smem_lds + (uint32_t)((g % NBUF) * STAGE) + (uint32_t)(wu * 64 * 16);
 #pragma unroll
-    for (int r = 0; r < MAX_LOADS; ++r)
-      if (r < nload) lds_dma16(src0[r] + g * sstride[r], buf + (uint32_t)(r * NWAVES * 64 * 16));
-  };
-  // wait until at most `later` stages issued after the ones needed are in flight
-  auto wait_stage = [&](int later) {
-    if (MODE == MODE_SUMS) { vmcnt_wait0(); return; }   // P stores also count
-    if (nload == 4) {
-      if (later >= 4) vmcnt_wait<16>(); else if (later == 3) vmcnt_wait<12>();
-      else if (later == 2) vmcnt_wait<8>(); else if (later == 1) vmcnt_wait<4>(); else vmcnt_wait0();
-    } else {
-      if (later >= 4) vmcnt_wait<12>(); else if (later == 3) vmcnt_wait<9>();
-      else if (later == 2) vmcnt_wait<6>(); else if (later == 1) vmcnt_wait<3>(); else vmcnt_wait0();
+    for (int r = 0; r < MAX_LOADS; ++r) {
+      const int L = wu + NWAVES * r;
+      lds_dma16_s(sbase[r] + g * sstride[r], L == WAVE_LOADS - 1 ? voff_sa : voff,
+                  buf + (uint32_t)(r * NWAVES * 64 * 16));
     }
   };
 
   // Operands of one group as a wavefront holds them in registers: the fp6
-  // codes of its two row tiles and two column tiles, the activation scales
-  // of the 16 rows each lane's accumulator elements belong to (per row tile:
-  // rows 8 q + 4 (lane / 32) + [0, 4), q = 0..3, four float4 reads), and the
+  // codes of its row tiles and column tiles, the activation scales of the
+  // 16 rows each lane's accumulator elements belong to (per row tile: rows
+  // 8 q + 4 (lane / 32) + [0, 4), q = 0..3, four float4 reads), and the
   // weight scale of the lane's column in each column tile.
-  struct Frags { v8i a[2], b[2]; float4 sa[2][4]; float sw[2]; };
+  struct Frags { v8i a[WTM], b[WTN]; float4 sa[4]; float sw[WTN]; };
   Frags F;
   auto stage_of = [&](int g) { return smem + (g % NBUF) * STAGE; };
-  auto load_a = [&](int g, int i) { F.a[i] = k2_frag(stage_of(g) + (2 * wmi + i) * kBlockBytes, lane); };
-  auto load_b = [&](int g, int j) {
-    F.b[j] = k2_frag(stage_of(g) + A_BYTES + (2 * wni + j) * kBlockBytes, lane);
+  auto load_a = [&](int g, int i) {
+    F.a[i] = k2_frag(stage_of(g) + (WTM * wmi + i) * kBlockBytes, lane);
   };
-  auto load_sa = [&](int g, int i) {
-    const float4 *lsa = reinterpret_cast<const float4 *>(stage_of(g) + A_BYTES + B_BYTES) +
-                        (64 * wmi + 32 * i + 4 * hl) / 4;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) F.sa[i][q] = lsa[2 * q];
+  auto load_b = [&](int g, int j) {
+    F.b[j] = k2_frag(stage_of(g) + A_BYTES + (WTN * wni + j) * kBlockBytes, lane);
+  };
+  auto sa_src = [&](int g, int i) {
+    return reinterpret_cast<const float4 *>(stage_of(g) + A_BYTES + B_BYTES + SW_BYTES) +
+           (WROWS * wmi + 32 * i + 4 * hl) / 4;
   };
   auto load_sw = [&](int g, int j) {
-    F.sw[j] = reinterpret_cast<const float *>(stage_of(g) + A_BYTES + B_BYTES + SA_BYTES)[64 * wni + 32 * j + ln];
+    F.sw[j] = reinterpret_cast<const float *>(stage_of(g) + A_BYTES + B_BYTES)
+        [WCOLS * wni + 32 * j + ln];
   };
-  // Per group the wavefront's four 32 x 32 tiles t = (i, j) = (t / 2, t % 2)
-  // each take one fp6 product; its elements are then scaled by the fp32
-  // product sA[m] sW[n] (one rounding) and accumulated with one FMA.
+  // Per group each of the wavefront's 32 x 32 tiles t = (i, j) =
+  // (t / WTN, t % WTN) takes one fp6 product; its elements are then scaled
+  // by the fp32 product sA[m] sW[n] (one rounding) and accumulated with one
+  // FMA.
   auto mm = [&](int t, v16f &P) {
-    const int i = t >> 1, j = t & 1;
+    const int i = t / WTN, j = t % WTN;
     P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[i], F.b[j], v16f{}, 2, 2, 0, 127, 0, 127);
   };
-  auto consume = [&](int t, int g, const v16f &P) {
-    const int i = t >> 1, j = t & 1;
+  auto consume_impl = [&](int t, int g, const v16f &P, const float4 *next, auto swap) {
+    const int i = t / WTN, j = t % WTN;
     if constexpr (MODE == MODE_SUMS) {
       const int n = wn + 32 * j + ln;
 #pragma unroll
@@ -464,86 +483,116 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (m >= p.m0 && m < p.m0 + p.mcount && n >= p.n0 && n < p.n0 + p.ncount)
           p.P[((int64_t)(m - p.m0) * p.ncount + (n - p.n0)) * G + g] = (int32_t)P[e];
       }
+      if constexpr (decltype(swap)::value) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) F.sa[q] = next[2 * q];
+      }
     } else {
       const float swj = F.sw[j];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 sa4 = F.sa[i][q];
+        const float4 sa4 = F.sa[q];
         const float sv[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int e = 4 * q + k;
           acc[i][j][e] = __builtin_fmaf(P[e], __fmul_rn(sv[k], swj), acc[i][j][e]);
         }
+        if constexpr (decltype(swap)::value) F.sa[q] = next[2 * q];
       }
     }
+  };
+  // consume(t): scale and accumulate tile t.  consume_swap(t, next): the
+  // same, and each float4 of activation scales is replaced by the one at
+  // `next` (the next row tile's) as soon as its last FMA has read it.
+  auto consume = [&](int t, int g, const v16f &P) {
+    consume_impl(t, g, P, nullptr, std::false_type{});
+  };
+  auto consume_swap = [&](int t, int g, const v16f &P, const float4 *next) {
+    consume_impl(t, g, P, next, std::true_type{});
+  };
+  auto mm_hi = [&](int t, v16f &P) {
+    __builtin_amdgcn_s_setprio(1);
+    mm(t, P);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Software pipeline over (group, tile): while the FMAs of tile t run on
   // the vector ALU, the matrix core works on tile t + 1 (the next group's
-  // first tile after t = 3).  Each operand of group g + 1 is read from LDS
-  // into its registers right after the last instruction of group g that
-  // uses them, one to three tiles before it is needed.  The matrix
-  // instructions are issued at raised wave priority so the SIMD's other
-  // wavefront does not delay them.  A barrier every third group: at
-  // g = 0 mod 3 every wave waits for its copies of stages g+1..g+3, meets
-  // the others, and requests stages g+4..g+6 (the buffers of stages g-2..g,
-  // which every wave has read before this barrier); the six buffers hold
-  // stages g+1..g+6.  The scheduling fences keep each step's products from
-  // being hoisted above the FMAs that still read the registers they
-  // overwrite.  After the last group the loads and the first product still
-  // run, on a stale but in-bounds LDS buffer, and their results are never
-  // used: branch-free code keeps the operands and products in fixed
-  // registers.
+  // first tile after the last).  Each operand of group g + 1 is read from
+  // LDS into its registers right after the last instruction of group g that
+  // uses it; the activation scales are held for one row tile at a time and
+  // swapped float4 by float4 inside the last tile that reads them.  The
+  // matrix instructions are issued at raised wave priority so the SIMD's
+  // other wavefront does not delay them.  One barrier per group; three of
+  // the four buffers hold stages g, g + 1, g + 2 while stage g + 3 is being
+  // requested.  The scheduling fences keep each step's products from being
+  // hoisted above the FMAs that still read the registers they overwrite.
+  // After the last group the loads and the first product still run, on a
+  // stale but in-bounds LDS buffer, and their results are never used:
+  // branch-free code keeps the operands and products in fixed registers.
   v16f Pa, Pb;
-  for (int g = 0; g < 4 && g < G; ++g) fetch(g);
-  wait_stage(min(3, G - 1));
+  for (int g = 0; g < 3 && g < G; ++g) fetch(g);
+  if (G > 2) vmcnt_wait<MAX_LOADS>(); else vmcnt_wait0();
   __syncthreads();
-  load_a(0, 0); load_a(0, 1); load_b(0, 0); load_b(0, 1);
-  load_sa(0, 0); load_sa(0, 1); load_sw(0, 0); load_sw(0, 1);
+  load_a(0, 0); load_a(0, 1);
+#pragma unroll
+  for (int j = 0; j < WTN; ++j) { load_b(0, j); load_sw(0, j); }
+  {
+    const float4 *s0 = sa_src(0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) F.sa[q] = s0[2 * q];
+  }
   mm(0, Pa);
   for (int g = 0; g < G; ++g) {
-    const bool nx = g + 1 < G;
-    if ((g % 3) == 0 && nx) {
-      wait_stage(0);
+    // Every wavefront waits for its copies of stage g + 1 (stage g + 2 may
+    // still be in flight) and meets the others; stage g - 1 has then been
+    // read by all of them, so its buffer takes stage g + 3.
+    if (g + 1 < G) {
+      if (MODE == MODE_FWD && g + 2 < G) vmcnt_wait<MAX_LOADS>(); else vmcnt_wait0();
       __syncthreads();
-      if (g + 4 < G) fetch(g + 4);
-      if (g + 5 < G) fetch(g + 5);
-      if (g + 6 < G) fetch(g + 6);
+      if (g + 3 < G) fetch(g + 3);
     }
-    __builtin_amdgcn_s_setprio(1);
-    mm(1, Pb);                                      // tile (0,1): last use of a0
-    __builtin_amdgcn_s_setprio(0);
-    load_a(g + 1, 0);
+    mm_hi(1, Pb);                         // tile (0,1)
     consume(0, g, Pa);
+    k2_order<0, 0>();
+    mm_hi(2, Pa);                         // tile (0,2)
+    consume(1, g, Pb);
+    k2_order<0, 0>();
+    mm_hi(3, Pb);                         // tile (0,3): last use of a0
+    load_a(g + 1, 0);
+    consume(2, g, Pa);
     k2_order<3, 0>();
-    __builtin_amdgcn_s_setprio(1);
-    mm(2, Pa);                                      // tile (1,0): last use of b0
-    __builtin_amdgcn_s_setprio(0);
+    mm_hi(4, Pa);                         // tile (1,0): last use of b0
     load_b(g + 1, 0);
-    consume(1, g, Pb);                              // last use of sa0
-    load_sa(g + 1, 0);
-    k2_order<3, 4>();
-    __builtin_amdgcn_s_setprio(1);
-    mm(3, Pb);                                      // tile (1,1): last use of a1, b1
-    __builtin_amdgcn_s_setprio(0);
-    load_a(g + 1, 1); load_b(g + 1, 1);
-    consume(2, g, Pa);                              // last use of sw0
+    consume_swap(3, g, Pb, sa_src(g, 1));      // row-0 scales give way to row 1
+    k2_order_r<3>();
+    mm_hi(5, Pb);                         // tile (1,1): last use of b1
+    load_b(g + 1, 1);
+    consume(4, g, Pa);           // last use of sw0
     load_sw(g + 1, 0);
+    k2_order<3, 1>();
+    mm_hi(6, Pa);                         // tile (1,2): last use of b2
+    load_b(g + 1, 2);
+    consume(5, g, Pb);           // last use of sw1
+    load_sw(g + 1, 1);
+    k2_order<3, 1>();
+    mm_hi(7, Pb);                         // tile (1,3): last use of a1, b3
+    load_a(g + 1, 1); load_b(g + 1, 3);
+    consume(6, g, Pa);           // last use of sw2
+    load_sw(g + 1, 2);
     k2_order<6, 1>();
-    __builtin_amdgcn_s_setprio(1);
-    mm(0, Pa);                                      // next group's tile (0,0)
-    __builtin_amdgcn_s_setprio(0);
-    consume(3, g, Pb);                              // last use of sa1, sw1
-    load_sa(g + 1, 1); load_sw(g + 1, 1);
-    k2_order<0, 5>();
+    mm_hi(0, Pa);                         // next group's tile (0,0)
+    consume_swap(7, g, Pb, sa_src(g + 1, 0));  // row-1 scales give way to the next group's row 0
+    load_sw(g + 1, 3);
+    k2_order_r<0, 1>();
   }
 
   if constexpr (MODE == MODE_FWD) {
     // low-rank up-projection: acc += D L2, D summed over the K1 splits
     for (int c = 0; c < p.rp / 16; ++c) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < WTM; ++i) {
         const int r = wm + 32 * i + ln;
         float d[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         for (int s = 0; s < p.S; ++s) {
@@ -565,7 +614,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const v8bf ah = as_v8bf(make_uint4(hi[0], hi[1], hi[2], hi[3]));
         const v8bf al = as_v8bf(make_uint4(lo[0], lo[1], lo[2], lo[3]));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < WTN; ++j) {
           const uint4 bw = *reinterpret_cast<const uint4 *>(
               p.l2t + (int64_t)(wn + 32 * j + ln) * p.rp + 16 * c + 8 * hl);
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, as_v8bf(bw), acc[i][j], 0, 0, 0);
@@ -573,19 +622,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     }
-    // Bias (+ GELU), then the wavefront's 64 x 64 tile goes out through its
-    // own 8 KB of LDS one 32-row half at a time, so global stores are whole
-    // 16-byte vectors along a row instead of 2- or 4-byte scattered stores.
+    // Bias (+ GELU), then the wavefront's tile goes out through its own LDS
+    // one 32-row half at a time, so global stores are whole 16-byte vectors
+    // along a row instead of 2- or 4-byte scattered stores.
     __syncthreads();                    // every wavefront is done with the stages
-    uint8_t *wbuf = smem + w * 8192;
+    uint8_t *wbuf = smem + w * EPI_WAVE_BYTES;
     constexpr int ES = OUT_F32 ? 4 : 2;          // bytes per output element
     constexpr int VE = 16 / ES;                  // elements per 16-byte vector
-    constexpr int LPR = 64 / VE;                 // lanes per 64-wide row
+    constexpr int LPR = WCOLS / VE;              // lanes per row of the wavefront tile
     const bool vec_ok = (p.N % VE) == 0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < WTM; ++i) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < WTN; ++j) {
         const float bj = p.bias[wn + 32 * j + ln];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -593,9 +642,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           float y = acc[i][j][e] + bj;
           if constexpr (EPI == SVDQ_EPILOGUE_GELU_TANH) y = gelu_tanh_f32(y);
           if constexpr (OUT_F32)
-            reinterpret_cast<float *>(wbuf)[r * 64 + 32 * j + ln] = y;
+            reinterpret_cast<float *>(wbuf)[r * WCOLS + 32 * j + ln] = y;
           else
-            reinterpret_cast<uint16_t *>(wbuf)[r * 64 + 32 * j + ln] = (uint16_t)f32_to_bf16_rne(y);
+            reinterpret_cast<uint16_t *>(wbuf)[r * WCOLS + 32 * j + ln] = (uint16_t)f32_to_bf16_rne(y);
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -606,7 +655,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int r = q * (64 / LPR) + lane / LPR;
         const int c = (lane % LPR) * VE;
         const int m = wm + 32 * i + r, n = wn + c;
-        const uint4 v = *reinterpret_cast<const uint4 *>(wbuf + (r * 64 + c) * ES);
+        const uint4 v = *reinterpret_cast<const uint4 *>(wbuf + (r * WCOLS + c) * ES);
         if (m < p.M) {
           uint8_t *dst = reinterpret_cast<uint8_t *>(p.Y) + ((int64_t)m * p.N + n) * ES;
           if (vec_ok && n + VE <= p.N) {
