@@ -48,14 +48,15 @@ __device__ __forceinline__ v8bf as_v8bf(uint4 u) { return __builtin_bit_cast(v8b
 
 // tanh-form GELU, 0.5 y (1 + tanh u) with u = sqrt(2/pi) (y + 0.044715 y^3),
 // evaluated as y / (1 + exp(-2u)) (the same function) so that large negative
-// y keep their relative accuracy instead of cancelling in 1 + tanh(u).  The
-// hardware exp2 and reciprocal (about 1 ulp of fp32 each) are far inside the
-// half-ulp of the bf16 result; exp overflow gives 1/inf = 0, the right limit.
+// y keep their relative accuracy instead of cancelling in 1 + tanh(u).  With
+// -2u log2(e) = y (c0 + c1 y^2) the exponential is one hardware exp2; exp2
+// and the reciprocal (about 1 ulp of fp32 each) are far inside the half-ulp
+// of the bf16 result; exp overflow gives 1/inf = 0, the right limit.
 __device__ __forceinline__ float gelu_tanh_f32(float y) {
-  const float k0 = 0.7978845608028654f;   // sqrt(2/pi)
-  const float k1 = 0.044715f;
-  const float u = k0 * (y + k1 * y * y * y);
-  return y * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
+  constexpr float c0 = (float)(-2.0 * 0.7978845608028654 * 1.4426950408889634);
+  constexpr float c1 = (float)(-2.0 * 0.7978845608028654 * 1.4426950408889634 * 0.044715);
+  const float t = y * __builtin_fmaf(c1, y * y, c0);
+  return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
 // Global -> LDS copy of 16 bytes per lane by the load unit
@@ -287,8 +288,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
 //   P  = v_mfma_scale_f32_32x32x64_f8f6f4 on fp6 codes (unit block scales):
 //        the exact int32 group sums, delivered as fp32 (|P| <= 3136)
 //   acc = fma(P, fl32(sA[m] sW[n]), acc)        (two VALU ops per element)
-// The epilogue adds the low-rank up-projection D L2 on bf16 MFMA (D split
-// into a bf16 high part and a bf16 remainder), the bias, the optional GELU,
+// The accumulators start from the low-rank up-projection D L2 (bf16 MFMA,
+// D split into a bf16 high part and a bf16 remainder), computed while the
+// first stages are copied; the epilogue adds the bias, the optional GELU,
 // and stores bf16 or fp32.  MODE_SUMS stores P for a window instead.
 //
 // Tile order: workgroups are dealt round-robin to the 8 XCDs, so block id b
@@ -438,7 +440,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int r = 0; r < MAX_LOADS; ++r) {
       const int L = wu + NWAVES * r;
-      lds_dma16_s(sbase[r] + g * sstride[r], L == WAVE_LOADS - 1 ? voff_sa : voff,
+      lds_dma16_s(sbase[r] + g * sstride[r], (r == MAX_LOADS - 1 && L == WAVE_LOADS - 1) ? voff_sa : voff,
                   buf + (uint32_t)(r * NWAVES * 64 * 16));
     }
   };
@@ -533,6 +535,81 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // branch-free code keeps the operands and products in fixed registers.
   v16f Pa, Pb;
   for (int g = 0; g < 3 && g < G; ++g) fetch(g);
+  if constexpr (MODE == MODE_FWD) {
+    // Low-rank up-projection first, while the first stages are in flight:
+    // acc = D L2 on bf16 matrix cores, D entered as a bf16 high part plus a
+    // bf16 remainder.  D of the workgroup's 128 rows is assembled once, in
+    // the fourth stage buffer (free until the main loop starts), 32 ranks at
+    // a time: wavefront w sums the K1 splits' partials of rows 32 w .. 32 w
+    // + 31 in split order (lane l: row l / 2, ranks 16 (l % 2) + [0, 16);
+    // loads issued four splits at a time, indices clamped, surplus ones not
+    // added) and stores the two bf16 parts; every wavefront then reads its
+    // operands from there.
+    uint16_t *dhi = reinterpret_cast<uint16_t *>(smem + 3 * STAGE);   // [BM][32]
+    uint16_t *dlo = dhi + BM * 32;                                     // [BM][32]
+    static_assert(BM * 32 * 2 * 2 <= STAGE, "low-rank staging fits one stage buffer");
+    const int rloc = 32 * wu + (lane >> 1), k0 = 16 * (lane & 1);
+    for (int c2 = 0; c2 < p.rp / 32; ++c2) {
+      float d[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) d[e] = 0.f;
+      const float *dp0 = p.dpart + (int64_t)(bm + rloc) * p.rp + 32 * c2 + k0;
+      for (int s0 = 0; s0 < p.S; s0 += 4) {
+        float4 v[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float4 *q = reinterpret_cast<const float4 *>(dp0 + (int64_t)min(s0 + u, p.S - 1) * p.Mp * p.rp);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) v[u][x] = q[x];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (s0 + u < p.S) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              d[4 * x + 0] += v[u][x].x; d[4 * x + 1] += v[u][x].y;
+              d[4 * x + 2] += v[u][x].z; d[4 * x + 3] += v[u][x].w;
+            }
+          }
+        }
+      }
+      uint32_t hw[8], lw[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t h0 = f32_to_bf16_rne(d[2 * e]), h1 = f32_to_bf16_rne(d[2 * e + 1]);
+        const uint32_t l0 = f32_to_bf16_rne(d[2 * e] - __uint_as_float(h0 << 16));
+        const uint32_t l1 = f32_to_bf16_rne(d[2 * e + 1] - __uint_as_float(h1 << 16));
+        hw[e] = h0 | (h1 << 16);
+        lw[e] = l0 | (l1 << 16);
+      }
+      uint4 *hp = reinterpret_cast<uint4 *>(dhi + rloc * 32 + k0);
+      uint4 *lp = reinterpret_cast<uint4 *>(dlo + rloc * 32 + k0);
+      hp[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]); hp[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+      lp[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]); lp[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+      uint4 bw[2][WTN];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int j = 0; j < WTN; ++j)
+          bw[cc][j] = *reinterpret_cast<const uint4 *>(p.l2t + (int64_t)(wn + 32 * j + ln) * p.rp + 32 * c2 + 16 * cc + 8 * hl);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) {
+        const int r = WROWS * wmi + 32 * i + ln;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const v8bf ah = as_v8bf(*reinterpret_cast<const uint4 *>(dhi + r * 32 + 16 * cc + 8 * hl));
+          const v8bf al = as_v8bf(*reinterpret_cast<const uint4 *>(dlo + r * 32 + 16 * cc + 8 * hl));
+#pragma unroll
+          for (int j = 0; j < WTN; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, as_v8bf(bw[cc][j]), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, as_v8bf(bw[cc][j]), acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+      __syncthreads();                   // staging free for the next 32 ranks
+    }
+  }
   if (G > 2) vmcnt_wait<MAX_LOADS>(); else vmcnt_wait0();
   __syncthreads();
   load_a(0, 0); load_a(0, 1);
@@ -589,39 +666,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   if constexpr (MODE == MODE_FWD) {
-    // low-rank up-projection: acc += D L2, D summed over the K1 splits
-    for (int c = 0; c < p.rp / 16; ++c) {
-#pragma unroll
-      for (int i = 0; i < WTM; ++i) {
-        const int r = wm + 32 * i + ln;
-        float d[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int s = 0; s < p.S; ++s) {
-          const float *dp = p.dpart + ((int64_t)s * p.Mp + r) * p.rp + 16 * c + 8 * hl;
-          const float4 d0 = *reinterpret_cast<const float4 *>(dp);
-          const float4 d1 = *reinterpret_cast<const float4 *>(dp + 4);
-          d[0] += d0.x; d[1] += d0.y; d[2] += d0.z; d[3] += d0.w;
-          d[4] += d1.x; d[5] += d1.y; d[6] += d1.z; d[7] += d1.w;
-        }
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t h0 = f32_to_bf16_rne(d[2 * e]), h1 = f32_to_bf16_rne(d[2 * e + 1]);
-          const uint32_t l0 = f32_to_bf16_rne(d[2 * e] - __uint_as_float(h0 << 16));
-          const uint32_t l1 = f32_to_bf16_rne(d[2 * e + 1] - __uint_as_float(h1 << 16));
-          hi[e] = h0 | (h1 << 16);
-          lo[e] = l0 | (l1 << 16);
-        }
-        const v8bf ah = as_v8bf(make_uint4(hi[0], hi[1], hi[2], hi[3]));
-        const v8bf al = as_v8bf(make_uint4(lo[0], lo[1], lo[2], lo[3]));
-#pragma unroll
-        for (int j = 0; j < WTN; ++j) {
-          const uint4 bw = *reinterpret_cast<const uint4 *>(
-              p.l2t + (int64_t)(wn + 32 * j + ln) * p.rp + 16 * c + 8 * hl);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, as_v8bf(bw), acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, as_v8bf(bw), acc[i][j], 0, 0, 0);
-        }
-      }
-    }
     // Bias (+ GELU), then the wavefront's tile goes out through its own LDS
     // one 32-row half at a time, so global stores are whole 16-byte vectors
     // along a row instead of 2- or 4-byte scattered stores.
@@ -644,7 +688,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           if constexpr (OUT_F32)
             reinterpret_cast<float *>(wbuf)[r * WCOLS + 32 * j + ln] = y;
           else
-            reinterpret_cast<uint16_t *>(wbuf)[r * WCOLS + 32 * j + ln] = (uint16_t)f32_to_bf16_rne(y);
+            reinterpret_cast<__bf16 *>(wbuf)[r * WCOLS + 32 * j + ln] = (__bf16)y;
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
