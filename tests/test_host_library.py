@@ -271,8 +271,19 @@ def test_host_weights_accept_fortran_ordered_arrays():
     Np, rp, K = 256, 32, 128
     off_l2t = Np * K * 3 // 4 + 2 * Np * 4
     off_l1t = off_l2t + Np * rp * 2
-    l1t = blob[off_l1t: off_l1t + rp * K * 2].view(np.uint16).reshape(rp, K)
-    assert np.array_equal(l1t[:6].T, O.bf16_bits_of(ref["L1s"]))
+    # L1s in the quantiser's fragment order: [group][32-rank block][16-channel
+    # step j][lane][8 channels]; lane l is rank l % 32 of the block, channels
+    # 16 j + 8 (l // 32) + [0, 8) of the group
+    frag = blob[off_l1t: off_l1t + rp * K * 2].view(np.uint16).reshape(K // 64, rp // 32, 4, 64, 8)
+    l1 = np.zeros((K, rp), np.uint16)
+    for g in range(K // 64):
+        for b in range(rp // 32):
+            for j in range(4):
+                for lane in range(64):
+                    k0 = 64 * g + 16 * j + 8 * (lane // 32)
+                    l1[k0:k0 + 8, 32 * b + lane % 32] = frag[g, b, j, lane]
+    assert np.array_equal(l1[:, :6], O.bf16_bits_of(ref["L1s"]))
+    assert not l1[:, 6:].any()
     l2t = blob[off_l2t: off_l2t + Np * rp * 2].view(np.uint16).reshape(Np, rp)
     assert np.array_equal(l2t[:96, :6].T, O.bf16_bits_of(ref["L2b"]))
     assert L == len(blob)

@@ -107,7 +107,7 @@ __device__ __forceinline__ void vmcnt_wait_dyn(int n) { vmcnt_wait_le<63>(min(n,
 //   x_hat = fl32(x * iota);  a = max |x_hat| over 64 (two lanes);
 //   s = a / 7, inv = 7 / a (correctly rounded), q = rint(x_hat inv),
 // stored as fp6 E2M3 (exact for these integers).  The raw bf16 values also
-// feed a 32x32x16 bf16 MFMA against L1s^T for the low-rank down-projection;
+// feed a 32x32x16 bf16 MFMA against L1s for the low-rank down-projection;
 // the four wavefronts' partial products are summed through LDS and written
 // as this split's partial D.
 constexpr int kK1Chunk = 4;                        // groups per chunk = wavefronts
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
   const int row = t * kTile + rr;
   const int nch = (Gs + kK1Chunk - 1) / kK1Chunk;
   constexpr int NB = TB > 0 ? TB : 1;
-  constexpr int L1N = 4 * TB;                      // L1s^T loads per wave and chunk
+  constexpr int L1N = 4 * TB;                      // L1s loads per wave and chunk
   const int ncopy = wu == 0 ? 5 : 4;               // copy instructions per wave and chunk
   // Copy of chunk c: wave w issues X instructions i = 4w .. 4w+3; instruction
   // i, lane l moves piece (l % 32) ^ (r % 16) of row r = 2i + l / 32.  Wave 0
@@ -154,7 +154,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
       lds_dma16(iota + (int64_t)gq * kGroup + (lane & 15) * 4, dst + (uint32_t)kK1XBytes);
     }
   };
-  // L1s^T operand of this wavefront's group in chunk c (clamped; unused past the split)
+  // L1s operand of this wavefront's group in chunk c, 1 KB contiguous per
+  // load (clamped; unused past the split)
   uint4 lring[kK1Bufs][4 * NB];
   auto load_l1 = [&](int c, uint4 (&d)[4 * NB]) {
     if constexpr (TB > 0) {
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
 #pragma unroll
         for (int b = 0; b < TB; ++b)
           d[j * NB + b] = *reinterpret_cast<const uint4 *>(
-              l1t + (int64_t)(b * 32 + rr) * K + g * kGroup + 16 * j + 8 * h);
+              l1t + ((((int64_t)g * TB + b) * 4 + j) * 64 + lane) * 8);
     }
   };
   v16f dacc[NB];

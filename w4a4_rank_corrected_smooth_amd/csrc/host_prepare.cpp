@@ -209,7 +209,7 @@ svdq_status_t pack_device_weights(const svdq_host_weights_t *in, void *host_blob
   uint16_t *l1t = reinterpret_cast<uint16_t *>(b + L.l1t);
   for (int64_t t = 0; t < r; ++t) {
     for (int64_t n = 0; n < N; ++n) l2t[n * L.rp + t] = in->l2[t * N + n];
-    for (int64_t k = 0; k < K; ++k) l1t[t * K + k] = in->l1s[k * r + t];
+    for (int64_t k = 0; k < K; ++k) l1t[l1_frag_index(k, t, L.rp)] = in->l1s[k * r + t];
   }
   std::memcpy(b + L.iota, in->inv_lambda, sizeof(float) * K);
   std::memcpy(b + L.bias, in->bias, sizeof(float) * N);

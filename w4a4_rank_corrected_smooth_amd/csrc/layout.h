@@ -61,6 +61,17 @@ constexpr int int_of_e2m3(uint32_t v) {
   return (v & 0x20u) ? -mag : mag;
 }
 
+// The down-projection factor L1s [K][rp] is stored in the order in which the
+// quantiser's matrix instruction consumes it (B operand of a 32x32x16 bf16
+// product, one 32-rank block b at a time): for group g, block b and 16-channel
+// step j, 64 lanes x 8 bf16 form one contiguous 1 KB piece; lane l holds rank
+// 32 b + l % 32 at channels 64 g + 16 j + 8 (l / 32) + [0, 8).  Element index
+// (in bf16 units) of (channel k, rank t):
+constexpr int64_t l1_frag_index(int64_t k, int64_t t, int64_t rp) {
+  return ((((k / kGroup) * (rp / 32) + t / 32) * 4 + (k % kGroup) / 16) * 64 + t % 32 +
+          32 * ((k % 16) / 8)) * 8 + k % 8;
+}
+
 // Device weight blob of one prepared layer.
 struct WeightLayout {
   int64_t N = 0, K = 0, rank = 0, Np = 0, rp = 0, G = 0;
@@ -72,7 +83,7 @@ struct WeightLayout {
     q = o;    o = round_up(o + Np * K * 3 / 4, kAlign);  // fp6 codes, tiled
     s = o;    o = round_up(o + G * Np * 4, kAlign);      // fp32 scales [G][Np]
     l2t = o;  o = round_up(o + Np * rp * 2, kAlign);     // bf16 L2^T [Np][rp]
-    l1t = o;  o = round_up(o + rp * K * 2, kAlign);      // bf16 L1s^T [rp][K]
+    l1t = o;  o = round_up(o + rp * K * 2, kAlign);      // bf16 L1s, MFMA fragment order (l1_frag_index)
     iota = o; o = round_up(o + K * 4, kAlign);           // fp32 1/lambda [K]
     bias = o; o = round_up(o + Np * 4, kAlign);          // fp32 [Np]
     total = o;
