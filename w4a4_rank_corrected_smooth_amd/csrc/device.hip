@@ -727,14 +727,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // ======================================================================= K3
 // AWQ W4A16.  A workgroup of 4 wavefronts owns a tile of 16 output channels;
-// wavefront w takes a contiguous quarter of the groups of 64 input channels.
-// It issues all its activation loads (a few kilobytes shared by every
-// workgroup, so cache hits) and then all its code and scale loads (the HBM
-// stream), up to kAwqChunk groups at once, and waits once: every load is
-// unconditional (indices clamped) so the completion count is exact.  For each
-// group, lane l (channel l % 16, quarter q = l / 16) turns its 16 codes into
-// fp16 (q - z) with the 1024-offset trick (0x6400 | code is the fp16 value
-// 1024 + code; subtracting 1024 + z is exact), the activations [16, 64] are
+// wavefront w takes a contiguous quarter of the groups of 64 input channels,
+// kAwqChunk groups at a time.  Per chunk it first copies the chunk's
+// activations (M rows, a few kilobytes shared by every workgroup, so cache
+// hits) into its own LDS with the global->LDS path, then issues all its code
+// and scale loads (the HBM stream) and waits only for the copies; each
+// group's compute then waits for its own loads alone, in issue order.  Every
+// load is unconditional (indices clamped; groups past the range weigh 0), so
+// the completion counts are exact.  For each group, lane l (channel l % 16,
+// quarter q = l / 16) turns its 16 codes into fp16 (q - z) with the
+// 1024-offset trick (0x6400 | code is the fp16 value 1024 + code;
+// subtracting 1024 + z is exact), the activations [16, 64] read from LDS are
 // the A operand, and two v_mfma_f32_16x16x32_f16 give the group's inner
 // sums; acc += s * sum in fp32.  Rows m >= M repeat row M - 1 and are never
 // stored.  The four partial sums meet in LDS, in a fixed order.
@@ -753,30 +756,52 @@ __global__ __launch_bounds__(256) void k3_awq_w4a16(const uint8_t *__restrict__ 
   const int m = lane & 15, qtr = lane >> 4;
   const int n = tile * kAwqTile + (lane & 15);
   const uint8_t *qbase = qd + (int64_t)tile * G * kAwqBlockBytes + lane * 8;
-  const uint16_t *xrow = x + (int64_t)min(m, M - 1) * K + 16 * qtr;
+  extern __shared__ __attribute__((aligned(16))) uint8_t awq_lds[];
   v4f acc = v4f{};
+  // this wavefront's copy of the chunk's activations, rows 0..M-1, one
+  // 16-byte piece per lane and copy (global->LDS path)
+  const int xw_bytes = (M * kAwqChunk * (kGroup / 8) + 63) / 64 * 1024;
+  const uint32_t xl_u32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)awq_lds +
+                          (uint32_t)(__builtin_amdgcn_readfirstlane(w) * xw_bytes);
+  const uint16_t *xl = reinterpret_cast<const uint16_t *>(awq_lds + w * xw_bytes);
   for (int gc = g0; gc < g1; gc += kAwqChunk) {
-    uint4 xa[kAwqChunk][2];
+    const int nG = min(kAwqChunk, g1 - gc);
+    const int npr = nG * (kGroup / 8);                  // pieces per row
+    const int npc = M * npr;
+    // activations first (cache hits), then the code and scale stream; every
+    // load after the copies is unconditional, so the copies are complete
+    // once at most 2 kAwqChunk loads remain
+    for (int c0 = 0; c0 < npc; c0 += 64) {
+      const int pc = min(c0 + lane, npc - 1);
+      const int mr = pc / npr, o = pc - mr * npr;
+      lds_dma16(x + (int64_t)mr * K + gc * kGroup + o * 8, xl_u32 + (uint32_t)(c0 * 16));
+    }
+    // The code and scale loads must follow the copies in issue order (the
+    // wait below counts them); their addresses take an offset from an empty
+    // asm placed after the copies, so the compiler cannot hoist them above.
+    int zero = 0;
+    asm volatile("" : "+s"(zero));
+    const uint8_t *qb = qbase + zero;
+    const uint32_t *szb = sz + n + zero;
     uint2 cw[kAwqChunk];
     uint32_t szw[kAwqChunk];
 #pragma unroll
     for (int i = 0; i < kAwqChunk; ++i) {
       const int gg = min(gc + i, g1 - 1);
-      xa[i][0] = *reinterpret_cast<const uint4 *>(xrow + gg * kGroup);
-      xa[i][1] = *reinterpret_cast<const uint4 *>(xrow + gg * kGroup + 8);
+      cw[i] = *reinterpret_cast<const uint2 *>(qb + (int64_t)gg * kAwqBlockBytes);
+      szw[i] = szb[(int64_t)gg * Np];
     }
+    vmcnt_wait<2 * kAwqChunk>();
+    const uint16_t *xm = xl + min(m, M - 1) * (npr * 8) + 16 * qtr;
 #pragma unroll
     for (int i = 0; i < kAwqChunk; ++i) {
-      const int gg = min(gc + i, g1 - 1);
-      cw[i] = *reinterpret_cast<const uint2 *>(qbase + (int64_t)gg * kAwqBlockBytes);
-      szw[i] = sz[(int64_t)gg * Np + n];
-    }
-    __builtin_amdgcn_sched_barrier(0);         // keep every load ahead of the math
-#pragma unroll
-    for (int i = 0; i < kAwqChunk; ++i) {
-      if (gc + i < g1) {                       // uniform across the wavefront
+      {
+      const uint4 xa0 = *reinterpret_cast<const uint4 *>(xm + i * kGroup);
+      const uint4 xa1 = *reinterpret_cast<const uint4 *>(xm + i * kGroup + 8);
       const _Float16 zf = __builtin_bit_cast(_Float16, (uint16_t)(szw[i] >> 16));
-      const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)(szw[i] & 0xFFFF));
+      // groups past the wavefront's range repeat its last one and weigh 0,
+      // so every load above is used and none is moved below the wait
+      const float sf = gc + i < g1 ? (float)__builtin_bit_cast(_Float16, (uint16_t)(szw[i] & 0xFFFF)) : 0.0f;
       const _Float16 off = -((_Float16)1024.0f + zf);
       const v2h off2 = v2h{off, off};
       v8h bop[2];
@@ -791,9 +816,9 @@ __global__ __launch_bounds__(256) void k3_awq_w4a16(const uint8_t *__restrict__ 
           bop[half][2 * j + 1] = v.y;
         }
       }
-      v4f part = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, xa[i][0]), bop[0],
+      v4f part = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, xa0), bop[0],
                                                        v4f{}, 0, 0, 0);
-      part = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, xa[i][1]), bop[1], part,
+      part = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, xa1), bop[1], part,
                                                    0, 0, 0);
       // output layout: lane holds rows 4 * (lane / 16) + e, column lane % 16
 #pragma unroll
@@ -1164,7 +1189,9 @@ svdq_status_t awq_w4a16_forward(const void *blob, int N, int K, const void *x, i
   if (st != SVDQ_OK) return st;
   const AwqLayout L(N, K);
   const uint8_t *b = static_cast<const uint8_t *>(blob);
-  hipLaunchKernelGGL(k3_awq_w4a16, dim3((unsigned)(L.Np / kAwqTile)), dim3(256), 0,
+  // per wavefront: M rows of a chunk, in whole 1 KB copies
+  const size_t lds = (size_t)4 * ((M * kAwqChunk * (kGroup / 8) + 63) / 64 * 1024);
+  hipLaunchKernelGGL(k3_awq_w4a16, dim3((unsigned)(L.Np / kAwqTile)), dim3(256), lds,
                      static_cast<hipStream_t>(hip_stream), b + L.q,
                      reinterpret_cast<const uint32_t *>(b + L.sz), static_cast<const uint16_t *>(x), M,
                      N, (int)L.Np, K, static_cast<const uint16_t *>(bias), static_cast<uint16_t *>(y));
