@@ -159,7 +159,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
   uint4 lring[kK1Bufs][4 * NB];
   auto load_l1 = [&](int c, uint4 (&d)[4 * NB]) {
     if constexpr (TB > 0) {
-      const int g = s * Gs + min(c * kK1Chunk + wu, Gs - 1);
+      // The loads must follow the chunk's copies in issue order (the waits
+      // count them); their address takes an offset from an empty asm, which
+      // stays after the copy asm, so the compiler cannot hoist them above.
+      int zero = 0;
+      asm volatile("" : "+s"(zero));
+      const int g = s * Gs + min(c * kK1Chunk + wu, Gs - 1) + zero;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll

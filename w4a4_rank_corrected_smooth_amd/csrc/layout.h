@@ -90,18 +90,18 @@ struct WeightLayout {
   }
 };
 
-// Groups of 64 handled by one quantiser workgroup: the K range is split
-// S ways so that enough workgroups exist to keep every CU streaming, with at
-// most kK1MaxGroups groups per split (the split's smoothing factors are held
-// in LDS) and, where possible, at least 4 (one per wavefront).
-constexpr int64_t kK1MaxGroups = 64;
+// Groups of 64 handled by one quantiser workgroup: the K range is split S
+// ways so that enough workgroups exist to keep every CU streaming (about 384:
+// more, shorter splits lose more to each workgroup's start-up than they gain),
+// with, where possible, at least 4 groups per split (one per wavefront).
+// Every split adds a partial low-rank product the GEMM has to sum.
 constexpr int64_t k1_splits(int64_t Mp, int64_t G) {
   const int64_t T = Mp / kTile;
-  int64_t best = 0;
+  int64_t best = 1;
   for (int64_t s = 1; s <= G; ++s) {
-    if (G % s != 0 || G / s > kK1MaxGroups) continue;
-    if (best == 0 || G / s >= 4) best = s;
-    if (G / s >= 4 && T * s >= 512) return s;
+    if (G % s != 0) continue;
+    if (s == 1 || G / s >= 4) best = s;
+    if (G / s >= 4 && T * s >= 384) return s;
   }
   return best;
 }
