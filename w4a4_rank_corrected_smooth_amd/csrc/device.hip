@@ -98,7 +98,7 @@ __device__ __forceinline__ void vmcnt_wait_dyn(int n) { vmcnt_wait_le<63>(min(n,
 // chunk's 32 rows x 512 bytes of X, and the chunk's 256 smoothing factors,
 // into LDS with the load unit's global->LDS path, each X copy instruction
 // moving two whole 512-byte row segments (long contiguous bursts for HBM);
-// wavefront w then quantises group w of the chunk.  Three chunk buffers are
+// wavefront w then quantises group w of the chunk.  kK1Bufs chunk buffers are
 // in flight.  Inside a row segment the 16-byte pieces are permuted (piece p
 // stored at slot p ^ (row % 16)) so that the reads below, one row per lane,
 // hit 16 different bank quads.
@@ -178,10 +178,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
   for (int b = 0; b < NB; ++b) dacc[b] = v16f{};
 
   // Vector-memory operations of one wavefront in issue order: copy(0)
-  // l1(0) copy(1) l1(1) copy(2) l1(2), then per chunk c: stores(c) [4],
-  // copy(c+3) l1(c+3).  Before chunk c it waits until copy(c) and l1(c) are
-  // done, leaving everything issued after them in flight, then the
-  // workgroup meets.
+  // l1(0) ... copy(B-1) l1(B-1) (B = kK1Bufs), then per chunk c: stores(c)
+  // [4], copy(c+B) l1(c+B).  Before chunk c it waits until copy(c) and l1(c)
+  // are done, leaving in flight everything issued after them: the stores of
+  // the min(c, B-1) chunks before it and the fetches of chunks c+1 .. c+B-1
+  // that exist; then the workgroup meets.
 #pragma unroll
   for (int c = 0; c < kK1Bufs; ++c) {
     if (c < nch) { copy_chunk(c); load_l1(c, lring[c]); }
@@ -191,9 +192,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
   for (int u = 0; u < kK1Bufs; ++u) {
     const int c = c0 + u;
     if (c >= nch) break;
-    int later = (c >= 2 ? 4 : 0) + (c >= 1 ? 4 : 0);
-    if (c + 1 < nch) later += ncopy + L1N;
-    if (c + 2 < nch) later += ncopy + L1N;
+    const int later = 4 * min(c, kK1Bufs - 1) + (ncopy + L1N) * (min(nch - 1, c + kK1Bufs - 1) - c);
     vmcnt_wait_dyn(later);
     __syncthreads();
     const uint8_t *buf = k1_lds + u * kK1BufBytes;
