@@ -172,6 +172,36 @@ svdq_status_t svdq_linear_gemm(const svdq_weights_t *w, int M, void *Y, svdq_dty
                                svdq_epilogue_t epilogue, const void *workspace,
                                size_t ws_bytes, void *hip_stream);
 
+/* MLP pair with the GELU/MLP fusion the pages credit to the original engine
+ * (VI, section "Giới thiệu Nunchaku Lite"): Y = linear2(bf16(epilogue(
+ * linear1(X)))) where linear1's GEMM applies bias (+ GELU), rounds to bf16
+ * and quantises the result for linear2 in its epilogue (codes, scales and the
+ * low-rank down-projection D, the last as a 64-bit fixed-point sum so the
+ * result does not depend on the order of the GEMM's workgroups); the
+ * intermediate activations never go to memory.  w2->K must equal w1->N.
+ * ws1 / ws2 are the two layers' own workspaces (svdq_workspace_bytes with
+ * each layer's shape, same M), distinct and caller-owned.  epilogue applies
+ * to linear1 (NONE or GELU_TANH); linear2 adds its bias only.  Y [M, N2] of
+ * y_dtype (SVDQ_BF16 or SVDQ_FP32), row-major.  Three kernels on
+ * `hip_stream`, also callable apart: svdq_mlp_quantize (linear1's quantiser,
+ * which also clears linear2's D), svdq_mlp_gemm1 (linear1's GEMM with the
+ * quantising epilogue), svdq_mlp_gemm2 (linear2's GEMM); each must follow
+ * the previous on the stream.  Errors as for svdq_linear_forward, plus
+ * SVDQ_ERR_UNSUPPORTED_SHAPE when the shapes do not chain and
+ * SVDQ_ERR_INVALID_ARGUMENT when ws1 == ws2. */
+svdq_status_t svdq_mlp_forward(const svdq_weights_t *w1, const svdq_weights_t *w2,
+                               const void *X, int M, void *Y, svdq_dtype_t y_dtype,
+                               svdq_epilogue_t epilogue, void *ws1, size_t ws1_bytes,
+                               void *ws2, size_t ws2_bytes, void *hip_stream);
+svdq_status_t svdq_mlp_quantize(const svdq_weights_t *w1, const svdq_weights_t *w2,
+                                const void *X, int M, void *ws1, size_t ws1_bytes,
+                                void *ws2, size_t ws2_bytes, void *hip_stream);
+svdq_status_t svdq_mlp_gemm1(const svdq_weights_t *w1, const svdq_weights_t *w2, int M,
+                             svdq_epilogue_t epilogue, const void *ws1, size_t ws1_bytes,
+                             void *ws2, size_t ws2_bytes, void *hip_stream);
+svdq_status_t svdq_mlp_gemm2(const svdq_weights_t *w2, int M, void *Y, svdq_dtype_t y_dtype,
+                             const void *ws2, size_t ws2_bytes, void *hip_stream);
+
 /* Elementwise bf16 -> bf16 tanh-GELU (the unfused glue between the MLP's
  * projections; same reading as SVDQ_EPILOGUE_GELU_TANH), n elements. */
 svdq_status_t svdq_gelu_tanh_bf16(const void *in, void *out, size_t n,

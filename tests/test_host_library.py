@@ -248,6 +248,24 @@ def test_forward_validation_errors():
     assert S._lib.svdq_device_weights_bytes(128, 100, 4) == 0
 
 
+def test_mlp_pair_argument_errors():
+    """The fused MLP pair's entry points reject shapes that do not chain, a
+    shared workspace and undersized workspaces before any HIP call."""
+    lib = S._lib
+    w1, w2 = _dw(N=256, K=128), _dw(N=128, K=256)
+    ws1 = S.workspace_bytes(64, 256, 128, 4)
+    ws2 = S.workspace_bytes(64, 128, 256, 4)
+    bad = _dw(N=128, K=192)
+    B1, B2 = FAKE, FAKE + (1 << 24)
+    assert lib.svdq_mlp_forward(ctypes.byref(w1), ctypes.byref(bad), FAKE, 64, FAKE, S.BF16, 1,
+                                B1, ws1, B2, S.workspace_bytes(64, 128, 192, 4), None) == SHAPE
+    assert lib.svdq_mlp_gemm1(ctypes.byref(w1), ctypes.byref(w2), 64, 1, B1, ws1, B1, ws2, None) == INV
+    assert lib.svdq_mlp_gemm1(ctypes.byref(w1), ctypes.byref(w2), 64, 1, B1, ws1, B2, ws2 - 256, None) == WS
+    assert lib.svdq_mlp_gemm1(ctypes.byref(w1), ctypes.byref(w2), 64, 7, B1, ws1, B2, ws2, None) in (INV, NODEV)
+    assert lib.svdq_mlp_quantize(ctypes.byref(w1), ctypes.byref(w2), None, 64, B1, ws1, B2, ws2, None) in (INV, NODEV)
+    assert lib.svdq_mlp_gemm2(ctypes.byref(w2), 64, None, S.BF16, B2, ws2, None) == INV
+
+
 @pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="checks the no-device path")
 def test_no_device_is_reported():
     assert S._lib.svdq_device_check() == NODEV
@@ -255,6 +273,10 @@ def test_no_device_is_reported():
     ws = S.workspace_bytes(64, 128, 128, 4)
     assert S._lib.svdq_linear_forward(ctypes.byref(w), FAKE, 64, FAKE, S.BF16, 0, FAKE, ws, None) == NODEV
     assert S._lib.svdq_gelu_tanh_bf16(FAKE, FAKE, 16, None) == NODEV
+    w1, w2 = _dw(N=256, K=128), _dw(N=128, K=256)
+    assert S._lib.svdq_mlp_forward(ctypes.byref(w1), ctypes.byref(w2), FAKE, 64, FAKE, S.BF16, 1,
+                                   FAKE, S.workspace_bytes(64, 256, 128, 4), FAKE + (1 << 24),
+                                   S.workspace_bytes(64, 128, 256, 4), None) == NODEV
 
 
 def test_host_weights_accept_fortran_ordered_arrays():

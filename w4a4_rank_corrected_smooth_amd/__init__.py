@@ -40,7 +40,9 @@ EXPORTS = [
     "svdq_abi_version", "svdq_status_string", "svdq_last_error", "svdq_device_check",
     "svdq_host_weights_sizes", "svdq_calibration_absmax", "svdq_prepare_weights",
     "svdq_device_weights_bytes", "svdq_pack_device_weights", "svdq_workspace_bytes",
-    "svdq_linear_forward", "svdq_linear_quantize", "svdq_linear_gemm", "svdq_gelu_tanh_bf16", "svdq_quantize_activations",
+    "svdq_linear_forward", "svdq_linear_quantize", "svdq_linear_gemm", "svdq_mlp_forward",
+    "svdq_mlp_quantize", "svdq_mlp_gemm1", "svdq_mlp_gemm2", "svdq_gelu_tanh_bf16",
+    "svdq_quantize_activations",
     "svdq_debug_group_sums", "awq_quantize_weights", "awq_device_weights_bytes",
     "awq_pack_device_weights", "awq_w4a16_forward",
 ]
@@ -77,6 +79,11 @@ _sig("svdq_linear_forward", _i, [ctypes.POINTER(DeviceWeights), _vp, _i, _vp, _i
 _sig("svdq_linear_quantize", _i, [ctypes.POINTER(DeviceWeights), _vp, _i, _vp, _sz, _vp])
 _sig("svdq_linear_gemm", _i, [ctypes.POINTER(DeviceWeights), _i, _vp, _i, _i, _vp, _sz, _vp])
 _sig("svdq_gelu_tanh_bf16", _i, [_vp, _vp, _sz, _vp])
+_W = ctypes.POINTER(DeviceWeights)
+_sig("svdq_mlp_forward", _i, [_W, _W, _vp, _i, _vp, _i, _i, _vp, _sz, _vp, _sz, _vp])
+_sig("svdq_mlp_quantize", _i, [_W, _W, _vp, _i, _vp, _sz, _vp, _sz, _vp])
+_sig("svdq_mlp_gemm1", _i, [_W, _W, _i, _i, _vp, _sz, _vp, _sz, _vp])
+_sig("svdq_mlp_gemm2", _i, [_W, _i, _vp, _i, _vp, _sz, _vp])
 _sig("svdq_quantize_activations", _i, [ctypes.POINTER(DeviceWeights), _vp, _i, _vp, _vp, _vp,
                                        _vp, _sz, _vp])
 _sig("svdq_debug_group_sums", _i, [ctypes.POINTER(DeviceWeights), _i, _i, _i, _i, _i, _vp, _vp,
@@ -246,6 +253,51 @@ def linear_gemm(layer: Linear, M: int, out: torch.Tensor, workspace: torch.Tenso
                                  EPILOGUE_GELU_TANH if gelu else EPILOGUE_NONE,
                                  workspace.data_ptr(), workspace.numel(), _stream(out.device)),
            "svdq_linear_gemm")
+    return out
+
+
+def mlp_forward(l1: Linear, l2: Linear, X: torch.Tensor, out: Optional[torch.Tensor] = None,
+                out_dtype=torch.bfloat16, gelu: bool = True,
+                ws1: Optional[torch.Tensor] = None, ws2: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = l2(bf16(gelu_tanh(l1(X)))) with l1's GEMM quantising l2's input in
+    its epilogue (the intermediate never goes to memory)."""
+    assert X.dtype == torch.bfloat16 and X.is_contiguous() and X.shape[1] == l1.K
+    M = X.shape[0]
+    if out is None:
+        out = torch.empty((M, l2.N), dtype=out_dtype, device=X.device)
+    ws1 = l1.new_workspace(M) if ws1 is None else ws1
+    ws2 = l2.new_workspace(M) if ws2 is None else ws2
+    dt = FP32 if out.dtype == torch.float32 else BF16
+    _check(_lib.svdq_mlp_forward(ctypes.byref(l1._w), ctypes.byref(l2._w), X.data_ptr(), M,
+                                 out.data_ptr(), dt, EPILOGUE_GELU_TANH if gelu else EPILOGUE_NONE,
+                                 ws1.data_ptr(), ws1.numel(), ws2.data_ptr(), ws2.numel(),
+                                 _stream(X.device)), "svdq_mlp_forward")
+    return out
+
+
+def mlp_quantize(l1: Linear, l2: Linear, X: torch.Tensor, ws1: torch.Tensor,
+                 ws2: torch.Tensor) -> None:
+    """First kernel of mlp_forward: l1's quantiser (and clearing l2's D)."""
+    assert X.dtype == torch.bfloat16 and X.is_contiguous() and X.shape[1] == l1.K
+    _check(_lib.svdq_mlp_quantize(ctypes.byref(l1._w), ctypes.byref(l2._w), X.data_ptr(), X.shape[0],
+                                  ws1.data_ptr(), ws1.numel(), ws2.data_ptr(), ws2.numel(),
+                                  _stream(X.device)), "svdq_mlp_quantize")
+
+
+def mlp_gemm1(l1: Linear, l2: Linear, M: int, ws1: torch.Tensor, ws2: torch.Tensor,
+              gelu: bool = True) -> None:
+    """Second kernel of mlp_forward: l1's GEMM, writing l2's codes, scales and D."""
+    _check(_lib.svdq_mlp_gemm1(ctypes.byref(l1._w), ctypes.byref(l2._w), M,
+                               EPILOGUE_GELU_TANH if gelu else EPILOGUE_NONE,
+                               ws1.data_ptr(), ws1.numel(), ws2.data_ptr(), ws2.numel(),
+                               _stream(ws1.device)), "svdq_mlp_gemm1")
+
+
+def mlp_gemm2(l2: Linear, M: int, out: torch.Tensor, ws2: torch.Tensor) -> torch.Tensor:
+    """Third kernel of mlp_forward: l2's GEMM from the workspace mlp_gemm1 filled."""
+    dt = FP32 if out.dtype == torch.float32 else BF16
+    _check(_lib.svdq_mlp_gemm2(ctypes.byref(l2._w), M, out.data_ptr(), dt, ws2.data_ptr(),
+                               ws2.numel(), _stream(out.device)), "svdq_mlp_gemm2")
     return out
 
 

@@ -92,6 +92,54 @@ __device__ __forceinline__ void vmcnt_wait_le(int n) {
 }
 __device__ __forceinline__ void vmcnt_wait_dyn(int n) { vmcnt_wait_le<63>(min(n, 63)); }
 
+// One lane's share of a group's quantisation (the reading of the pages'
+// quantiser used throughout): lane l holds half l / 32 of a row's 64 values,
+// channels 16 j + 8 h + [0, 8) in xr[j] (bf16 pairs) with their factors
+// 1/lambda in io[2 j], io[2 j + 1].
+//   x_hat = fl32(x * iota);  a = max |x_hat| over 64 (two lanes);
+//   s = a / 7, inv = 7 / a (correctly rounded), q = rint(x_hat inv),
+// returned as s and the 32 codes packed as fp6 E2M3 (exact for these
+// integers).  The hardware packer interleaves its two 16-value inputs (field
+// 2i from the first, 2i+1 from the second), so even and odd elements go in to
+// get element order 0..31 at bits 6c.  No clamp to [-7, 7] is needed:
+// |x_hat| <= a and inv <= (7/a)(1 + 2^-24) give |fl32(x_hat inv)| <
+// 7.0000009, which rounds to at most 7.
+__device__ __forceinline__ float quantize_lane(const uint4 (&xr)[4], const float4 (&io)[8],
+                                               v6u &packed) {
+  float xh[32];
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t wv[4] = {xr[j].x, xr[j].y, xr[j].z, xr[j].w};
+    const float iv[8] = {io[2 * j].x, io[2 * j].y, io[2 * j].z, io[2 * j].w,
+                         io[2 * j + 1].x, io[2 * j + 1].y, io[2 * j + 1].z, io[2 * j + 1].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = (e & 1) ? bf16_hi(wv[e >> 1]) : bf16_lo(wv[e >> 1]);
+      const float v = __fmul_rn(x, iv[e]);
+      xh[8 * j + e] = v;
+      a = fmaxf(a, fabsf(v));
+    }
+  }
+  a = fmaxf(a, __shfl_xor(a, 32));
+  float sc = 0.0f, inv = 0.0f;
+  if (a >= 0x1p-100f) {
+    sc = a / 7.0f;
+    inv = 7.0f / a;
+  }
+  v16f ev, od;
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc) {
+    ev[cc] = rintf(__fmul_rn(xh[2 * cc], inv));
+    od[cc] = rintf(__fmul_rn(xh[2 * cc + 1], inv));
+  }
+  // The packer's result must not share registers with its inputs (it writes
+  // output dwords while later inputs are still to be read), which the
+  // builtin does not guarantee: written as asm with an early-clobber output.
+  asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, 1.0" : "=&v"(packed) : "v"(ev), "v"(od));
+  return sc;
+}
+
 // ======================================================================= K1
 // One workgroup (4 wavefronts) per (tile of 32 token rows, K split).  The
 // split's groups are taken kK1Chunk = 4 at a time: the workgroup copies the
@@ -103,9 +151,7 @@ __device__ __forceinline__ void vmcnt_wait_dyn(int n) { vmcnt_wait_le<63>(min(n,
 // stored at slot p ^ (row % 16)) so that the reads below, one row per lane,
 // hit 16 different bank quads.
 // Per group, lane l owns row l % 32 and half h = l / 32: its 32 values are
-// channels 16 j + 8 h + [0, 8) (j = 0..3).
-//   x_hat = fl32(x * iota);  a = max |x_hat| over 64 (two lanes);
-//   s = a / 7, inv = 7 / a (correctly rounded), q = rint(x_hat inv),
+// channels 16 j + 8 h + [0, 8) (j = 0..3), quantised by quantize_lane and
 // stored as fp6 E2M3 (exact for these integers).  The raw bf16 values also
 // feed a 32x32x16 bf16 MFMA against L1s for the low-rank down-projection;
 // the four wavefronts' partial products are summed through LDS and written
@@ -120,7 +166,8 @@ template <int TB>   // rank_pad / 32
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3 : 1))) void k1_quantize_lowrank_down(
     const uint16_t *__restrict__ X, int M, int K, int Mp, int S,
     const float *__restrict__ iota, const uint16_t *__restrict__ l1t,
-    uint8_t *__restrict__ qa, float *__restrict__ sa, float *__restrict__ dpart) {
+    uint8_t *__restrict__ qa, float *__restrict__ sa, float *__restrict__ dpart,
+    int64_t *__restrict__ dzero, int rpz) {
   __shared__ __attribute__((aligned(16))) uint8_t k1_lds[kK1LdsBytes];
   const uint32_t lds_u32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)k1_lds;
   const int t = blockIdx.x, s = blockIdx.y;
@@ -207,40 +254,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
       const int piece = wu * 8 + 2 * j + h;
       xr[j] = *reinterpret_cast<const uint4 *>(xb + ((piece ^ (rr & 15)) << 4));
     }
-    float xh[32];
-    float a = 0.0f;
+    float4 io[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float4 i0 = iota_c[4 * j + 2 * h];
-      const float4 i1 = iota_c[4 * j + 2 * h + 1];
-      const uint32_t wv[4] = {xr[j].x, xr[j].y, xr[j].z, xr[j].w};
-      const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = (e & 1) ? bf16_hi(wv[e >> 1]) : bf16_lo(wv[e >> 1]);
-        const float v = __fmul_rn(x, iv[e]);
-        xh[8 * j + e] = v;
-        a = fmaxf(a, fabsf(v));
-      }
+      io[2 * j] = iota_c[4 * j + 2 * h];
+      io[2 * j + 1] = iota_c[4 * j + 2 * h + 1];
     }
-    a = fmaxf(a, __shfl_xor(a, 32));
-    float sc = 0.0f, inv = 0.0f;
-    if (a >= 0x1p-100f) {
-      sc = a / 7.0f;
-      inv = 7.0f / a;
-    }
-    // codes as fp6 E2M3: the hardware packer interleaves its two 16-value
-    // inputs (field 2i from the first, 2i+1 from the second), so even and odd
-    // elements go in to get element order 0..31 at bits 6c.  No clamp to
-    // [-7, 7] is needed: |x_hat| <= a and inv <= (7/a)(1 + 2^-24) give
-    // |fl32(x_hat inv)| < 7.0000009, which rounds to at most 7.
-    v16f ev, od;
-#pragma unroll
-    for (int cc = 0; cc < 16; ++cc) {
-      ev[cc] = rintf(__fmul_rn(xh[2 * cc], inv));
-      od[cc] = rintf(__fmul_rn(xh[2 * cc + 1], inv));
-    }
-    const v6u packed = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+    v6u packed;
+    const float sc = quantize_lane(xr, io, packed);
     uint8_t *qp = qa + pair_offset(g, t, T, lane, 0);
 #pragma unroll
     for (int j = 0; j < 3; ++j)
@@ -277,6 +298,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
       __syncthreads();
     }
   }
+  // For a fused MLP pair: clear this row tile's rows of the next layer's
+  // fixed-point D, which the GEMM that follows accumulates into.
+  if (dzero != nullptr && s == 0) {
+    int64_t *dz = dzero + (int64_t)t * kTile * rpz;
+    for (int i = threadIdx.x; i < kTile * rpz / 2; i += 256)
+      reinterpret_cast<int4 *>(dz)[i] = make_int4(0, 0, 0, 0);
+  }
 }
 
 // ======================================================================= K2
@@ -311,6 +339,13 @@ struct K2Args {
   void *Y;
   int32_t *P; int m0, mcount, n0, ncount;
   int tile_m0, tile_n0, TM, TN;     // tile grid (units of the workgroup tile)
+  // D as one int64 fixed-point sum [Mp][rp] (input quantised by the previous
+  // layer's GEMM) instead of fp32 partials
+  const int64_t *dfix;
+  // quantisation of the next layer's input in the epilogue (MLP pair): its
+  // 1/lambda [N], L1s in fragment order, codes, scales and fixed-point D
+  const float *iota2; const uint16_t *l1f2; uint8_t *qa2; float *sa2; int64_t *d2;
+  int G2, rp2;
 };
 
 namespace k2c {
@@ -381,7 +416,7 @@ __device__ __forceinline__ void k2_order_r() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int MODE, int EPI, bool OUT_F32>
+template <int MODE, int EPI, bool OUT_F32, bool DFIX = false, bool QNEXT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_w4a4_gemm(K2Args p) {
   using namespace k2c;
   // ---- tile of this workgroup (XCD-aware, grouped)
@@ -558,8 +593,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       float d[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) d[e] = 0.f;
+      if constexpr (DFIX) {
+        // one fixed-point sum: 16 int64 per lane, converted with one rounding
+        const int4 *q = reinterpret_cast<const int4 *>(p.dfix + (int64_t)(bm + rloc) * p.rp + 32 * c2 + k0);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int4 v = q[x];
+          const int64_t a0 = (int64_t)(((uint64_t)(uint32_t)v.y << 32) | (uint32_t)v.x);
+          const int64_t a1 = (int64_t)(((uint64_t)(uint32_t)v.w << 32) | (uint32_t)v.z);
+          d[2 * x] = (float)((double)a0 * (1.0 / kDFixScale));
+          d[2 * x + 1] = (float)((double)a1 * (1.0 / kDFixScale));
+        }
+      }
       const float *dp0 = p.dpart + (int64_t)(bm + rloc) * p.rp + 32 * c2 + k0;
-      for (int s0 = 0; s0 < p.S; s0 += 4) {
+      for (int s0 = 0; s0 < (DFIX ? 0 : p.S); s0 += 4) {
         float4 v[4][4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -670,7 +717,113 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     k2_order_r<0, 1>();
   }
 
-  if constexpr (MODE == MODE_FWD) {
+  if constexpr (MODE == MODE_FWD && QNEXT) {
+    // MLP pair: this layer's output never goes to memory.  Bias (+ GELU),
+    // rounded to bf16 (exactly the values the unfused path stores), then the
+    // next layer's quantiser runs on the tile: every (32-row tile, group of 64
+    // columns) block of the wavefront's 64 x 128 tile lies wholly inside it.
+    // The tile is staged row-major in the wavefront's own LDS, 16-byte chunks
+    // XOR-permuted by row so the one-row-per-lane reads spread over the banks.
+    __syncthreads();                    // every wavefront is done with the stages
+    uint8_t *xs = smem + w * EPI_WAVE_BYTES;   // 64 rows x 256 bytes
+    static_assert(WROWS * WCOLS * 2 <= EPI_WAVE_BYTES, "bf16 tile fits the wavefront's staging");
+#pragma unroll
+    for (int i = 0; i < WTM; ++i)
+#pragma unroll
+      for (int j = 0; j < WTN; ++j) {
+        const float bj = p.bias[wn + 32 * j + ln];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = 32 * i + 8 * (e >> 2) + 4 * hl + (e & 3), c = 32 * j + ln;
+          float y = acc[i][j][e] + bj;
+          if constexpr (EPI == SVDQ_EPILOGUE_GELU_TANH) y = gelu_tanh_f32(y);
+          *reinterpret_cast<__bf16 *>(xs + r * (WCOLS * 2) + ((((c >> 3) ^ (r & 15))) << 4) + (c & 7) * 2) =
+              (__bf16)y;
+        }
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int rr = lane & 31, h = lane >> 5;
+    const int T2 = p.Mp / kTile;
+    // block (i, gl): lane's 32 values, row 32 i + rr, channels 16 j + 8 h + [0, 8)
+    auto load_block = [&](int i, int gl, uint4 (&xr)[4]) {
+      const int r = 32 * i + rr;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xr[j] = *reinterpret_cast<const uint4 *>(xs + r * (WCOLS * 2) + (((8 * gl + 2 * j + h) ^ (r & 15)) << 4));
+    };
+#pragma unroll
+    for (int gl = 0; gl < WCOLS / kGroup; ++gl) {
+      const int g2 = (wn + kGroup * gl) / kGroup;
+      if (g2 >= p.G2) continue;                  // padding columns past the layer's N
+      float4 io[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 *ip = reinterpret_cast<const float4 *>(p.iota2 + (int64_t)g2 * kGroup + 16 * j + 8 * h);
+        io[2 * j] = ip[0];
+        io[2 * j + 1] = ip[1];
+      }
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) {
+        uint4 xr[4];
+        load_block(i, gl, xr);
+        v6u packed;
+        const float sc = quantize_lane(xr, io, packed);
+        uint8_t *qp = p.qa2 + pair_offset(g2, (wm + 32 * i) / kTile, T2, lane, 0);
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+          *reinterpret_cast<uint2 *>(qp + 512 * j) = make_uint2(packed[2 * j], packed[2 * j + 1]);
+        p.sa2[(int64_t)g2 * p.Mp + wm + 32 * i + rr] = sc;   // both halves hold the same scale
+      }
+    }
+    // The next layer's low-rank down-projection over this tile's channels,
+    // 32 ranks at a time: bf16 MFMA of the tile's raw bf16 values against
+    // L1s; the two wavefronts sharing rows add their halves through LDS in a
+    // fixed order, and the sum goes into the next layer's D as 64-bit fixed
+    // point (units of 2^-32; integer addition, so the result does not depend
+    // on the order in which workgroups arrive).  Partial sums are clamped to
+    // +-2^56 so no sum of the column tiles can overflow.
+    float *exch = reinterpret_cast<float *>(smem + NWAVES * EPI_WAVE_BYTES);   // [4][16][64]
+    static_assert(NWAVES * EPI_WAVE_BYTES + NWAVES * 16 * 64 * 4 <= NBUF * STAGE, "exchange fits");
+    for (int b = 0; b < p.rp2 / 32; ++b) {
+      v16f dacc[WTM];
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) dacc[i] = v16f{};
+#pragma unroll
+      for (int gl = 0; gl < WCOLS / kGroup; ++gl) {
+        const int g2 = (wn + kGroup * gl) / kGroup;
+        if (g2 >= p.G2) continue;
+        uint4 lf[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          lf[j] = *reinterpret_cast<const uint4 *>(
+              p.l1f2 + ((((int64_t)g2 * (p.rp2 / 32) + b) * 4 + j) * 64 + lane) * 8);
+#pragma unroll
+        for (int i = 0; i < WTM; ++i) {
+          uint4 xr[4];
+          load_block(i, gl, xr);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            dacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8bf(xr[j]), as_v8bf(lf[j]), dacc[i], 0, 0, 0);
+        }
+      }
+      // wavefront (wmi, wni) finishes row tile wni of its pair's rows
+#pragma unroll
+      for (int e = 0; e < 16; ++e) exch[(w * 16 + e) * 64 + lane] = wni == 0 ? dacc[1][e] : dacc[0][e];
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float other = exch[((w ^ 1) * 16 + e) * 64 + lane];
+        const float v = wni == 0 ? dacc[0][e] + other : other + dacc[1][e];
+        const double q = fmin(fmax(rint((double)v * kDFixScale), -0x1p56), 0x1p56);
+        const int m = wm + 32 * wni + 8 * (e >> 2) + 4 * hl + (e & 3);
+        atomicAdd(reinterpret_cast<unsigned long long *>(p.d2 + (int64_t)m * p.rp2 + 32 * b + ln),
+                  (unsigned long long)(long long)q);
+      }
+      __syncthreads();                   // the exchange buffer is reused
+    }
+  } else if constexpr (MODE == MODE_FWD) {
     // Bias (+ GELU), then the wavefront's tile goes out through its own LDS
     // one 32-row half at a time, so global stores are whole 16-byte vectors
     // along a row instead of 2- or 4-byte scattered stores.
@@ -965,7 +1118,8 @@ svdq_status_t validate_weights(const svdq_weights_t *w, const char *who) {
 }
 
 svdq_status_t launch_k1(const WeightLayout &L, const WorkLayout &Wl, const svdq_weights_t *w,
-                        const void *X, int M, uint8_t *ws, hipStream_t st) {
+                        const void *X, int M, uint8_t *ws, hipStream_t st,
+                        int64_t *dzero = nullptr, int rpz = 0) {
   const uint8_t *blob = static_cast<const uint8_t *>(w->blob);
   const dim3 grid((unsigned)(Wl.Mp / kTile), (unsigned)Wl.S);
   const uint16_t *x = static_cast<const uint16_t *>(X);
@@ -980,7 +1134,7 @@ svdq_status_t launch_k1(const WeightLayout &L, const WorkLayout &Wl, const svdq_
 #define K1_CASE(TB)                                                                       \
   case TB:                                                                                \
     hipLaunchKernelGGL(k1_quantize_lowrank_down<TB>, grid, dim3(256), lds, st, x, M, K, Mp, \
-                       S, iota, l1t, qa, sa, dp);                                         \
+                       S, iota, l1t, qa, sa, dp, dzero, rpz);                             \
     break;
     K1_CASE(0) K1_CASE(1) K1_CASE(2) K1_CASE(3) K1_CASE(4) K1_CASE(5) K1_CASE(6) K1_CASE(7)
     K1_CASE(8)
@@ -1043,26 +1197,55 @@ static svdq_status_t validate_output(void *Y, svdq_dtype_t y_dtype, svdq_epilogu
   return SVDQ_OK;
 }
 
+// Input D of the GEMM: fp32 partials from the quantiser, or one fixed-point
+// sum written by the previous layer's fused epilogue.  Output: Y, or (w2 set)
+// the next layer's codes, scales and D in ws2.
+enum K2In { K2_D_PARTIALS = 0, K2_D_FIXED = 1 };
 static svdq_status_t launch_k2(const svdq_weights_t *w, int M, void *Y, svdq_dtype_t y_dtype,
-                               svdq_epilogue_t epilogue, const void *workspace, hipStream_t stream) {
+                               svdq_epilogue_t epilogue, const void *workspace, hipStream_t stream,
+                               K2In din = K2_D_PARTIALS, const svdq_weights_t *w2 = nullptr,
+                               void *ws2 = nullptr) {
   const WeightLayout L(w->N, w->K, w->rank);
   const WorkLayout Wl(M, w->K, w->rank);
   K2Args a = make_k2_args(L, Wl, w, M, static_cast<const uint8_t *>(workspace));
   a.Y = Y;
   a.TM = (M + k2c::BM - 1) / k2c::BM;
   a.TN = (w->N + k2c::BN - 1) / k2c::BN;
+  a.dfix = reinterpret_cast<const int64_t *>(static_cast<const uint8_t *>(workspace) + Wl.d);
+  if (w2) {
+    const WeightLayout L2(w2->N, w2->K, w2->rank);
+    const WorkLayout W2(M, w2->K, w2->rank);
+    const uint8_t *b2 = static_cast<const uint8_t *>(w2->blob);
+    uint8_t *s2 = static_cast<uint8_t *>(ws2);
+    a.iota2 = reinterpret_cast<const float *>(b2 + L2.iota);
+    a.l1f2 = reinterpret_cast<const uint16_t *>(b2 + L2.l1t);
+    a.qa2 = s2 + W2.qa;
+    a.sa2 = reinterpret_cast<float *>(s2 + W2.sa);
+    a.d2 = reinterpret_cast<int64_t *>(s2 + W2.d);
+    a.G2 = (int)W2.G;
+    a.rp2 = (int)W2.rp;
+  }
   const dim3 grid((unsigned)round_up((int64_t)a.TM * a.TN, 8));
   const dim3 block(k2c::THREADS);
   const bool f32 = y_dtype == SVDQ_FP32;
   const bool gelu = epilogue == SVDQ_EPILOGUE_GELU_TANH;
-  if (!gelu && f32)
-    hipLaunchKernelGGL((k2_w4a4_gemm<MODE_FWD, SVDQ_EPILOGUE_NONE, true>), grid, block, 0, stream, a);
-  else if (!gelu)
-    hipLaunchKernelGGL((k2_w4a4_gemm<MODE_FWD, SVDQ_EPILOGUE_NONE, false>), grid, block, 0, stream, a);
-  else if (f32)
-    hipLaunchKernelGGL((k2_w4a4_gemm<MODE_FWD, SVDQ_EPILOGUE_GELU_TANH, true>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((k2_w4a4_gemm<MODE_FWD, SVDQ_EPILOGUE_GELU_TANH, false>), grid, block, 0, stream, a);
+  constexpr int NONE = SVDQ_EPILOGUE_NONE, GELU = SVDQ_EPILOGUE_GELU_TANH;
+#define K2_GO(E, F, DF, QN) hipLaunchKernelGGL((k2_w4a4_gemm<MODE_FWD, E, F, DF, QN>), grid, block, 0, stream, a)
+  if (w2) {
+    if (din == K2_D_FIXED) return fail(SVDQ_ERR_INVALID_ARGUMENT, "chained fused epilogues are not supported");
+    if (gelu) K2_GO(GELU, false, false, true); else K2_GO(NONE, false, false, true);
+  } else if (din == K2_D_FIXED) {
+    if (!gelu && f32) K2_GO(NONE, true, true, false);
+    else if (!gelu) K2_GO(NONE, false, true, false);
+    else if (f32) K2_GO(GELU, true, true, false);
+    else K2_GO(GELU, false, true, false);
+  } else {
+    if (!gelu && f32) K2_GO(NONE, true, false, false);
+    else if (!gelu) K2_GO(NONE, false, false, false);
+    else if (f32) K2_GO(GELU, true, false, false);
+    else K2_GO(GELU, false, false, false);
+  }
+#undef K2_GO
   return launch_status("GEMM kernel launch");
 }
 
@@ -1104,6 +1287,68 @@ svdq_status_t svdq_linear_forward(const svdq_weights_t *w, const void *X, int M,
   if ((st = launch_k1(L, Wl, w, X, M, static_cast<uint8_t *>(workspace), stream)) != SVDQ_OK)
     return st;
   return launch_k2(w, M, Y, y_dtype, epilogue, workspace, stream);
+}
+
+static svdq_status_t validate_pair(const svdq_weights_t *w1, const svdq_weights_t *w2, int M,
+                                   size_t ws1_bytes, const void *ws1, size_t ws2_bytes,
+                                   const void *ws2, const char *who) {
+  svdq_status_t st = validate_forward(w1, M, ws1_bytes, ws1, who);
+  if (st != SVDQ_OK) return st;
+  if ((st = validate_forward(w2, M, ws2_bytes, ws2, who)) != SVDQ_OK) return st;
+  if (w2->K != w1->N)
+    return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "%s: second layer's K=%d != first layer's N=%d", who,
+                w2->K, w1->N);
+  if (ws1 == ws2) return fail(SVDQ_ERR_INVALID_ARGUMENT, "%s: the two workspaces must differ", who);
+  return check_device();
+}
+
+svdq_status_t svdq_mlp_quantize(const svdq_weights_t *w1, const svdq_weights_t *w2, const void *X,
+                                int M, void *ws1, size_t ws1_bytes, void *ws2, size_t ws2_bytes,
+                                void *hip_stream) {
+  svdq_status_t st = validate_pair(w1, w2, M, ws1_bytes, ws1, ws2_bytes, ws2, "svdq_mlp_quantize");
+  if (st != SVDQ_OK) return st;
+  if (!X) return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_mlp_quantize: NULL X");
+  if (!aligned16(X)) return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_mlp_quantize: misaligned X");
+  const WeightLayout L(w1->N, w1->K, w1->rank);
+  const WorkLayout Wl(M, w1->K, w1->rank);
+  const WorkLayout W2(M, w2->K, w2->rank);
+  int64_t *dz = W2.rp > 0 ? reinterpret_cast<int64_t *>(static_cast<uint8_t *>(ws2) + W2.d) : nullptr;
+  return launch_k1(L, Wl, w1, X, M, static_cast<uint8_t *>(ws1), static_cast<hipStream_t>(hip_stream),
+                   dz, (int)W2.rp);
+}
+
+svdq_status_t svdq_mlp_gemm1(const svdq_weights_t *w1, const svdq_weights_t *w2, int M,
+                             svdq_epilogue_t epilogue, const void *ws1, size_t ws1_bytes,
+                             void *ws2, size_t ws2_bytes, void *hip_stream) {
+  svdq_status_t st = validate_pair(w1, w2, M, ws1_bytes, ws1, ws2_bytes, ws2, "svdq_mlp_gemm1");
+  if (st != SVDQ_OK) return st;
+  if (epilogue != SVDQ_EPILOGUE_NONE && epilogue != SVDQ_EPILOGUE_GELU_TANH)
+    return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_mlp_gemm1: unknown epilogue %d", (int)epilogue);
+  return launch_k2(w1, M, nullptr, SVDQ_BF16, epilogue, ws1, static_cast<hipStream_t>(hip_stream),
+                   K2_D_PARTIALS, w2, ws2);
+}
+
+svdq_status_t svdq_mlp_gemm2(const svdq_weights_t *w2, int M, void *Y, svdq_dtype_t y_dtype,
+                             const void *ws2, size_t ws2_bytes, void *hip_stream) {
+  svdq_status_t st = validate_forward(w2, M, ws2_bytes, ws2, "svdq_mlp_gemm2");
+  if (st != SVDQ_OK) return st;
+  if ((st = validate_output(Y, y_dtype, SVDQ_EPILOGUE_NONE, "svdq_mlp_gemm2")) != SVDQ_OK) return st;
+  if ((st = check_device()) != SVDQ_OK) return st;
+  return launch_k2(w2, M, Y, y_dtype, SVDQ_EPILOGUE_NONE, ws2, static_cast<hipStream_t>(hip_stream),
+                   K2_D_FIXED);
+}
+
+svdq_status_t svdq_mlp_forward(const svdq_weights_t *w1, const svdq_weights_t *w2, const void *X,
+                               int M, void *Y, svdq_dtype_t y_dtype, svdq_epilogue_t epilogue,
+                               void *ws1, size_t ws1_bytes, void *ws2, size_t ws2_bytes,
+                               void *hip_stream) {
+  svdq_status_t st = validate_output(Y, y_dtype, epilogue, "svdq_mlp_forward");
+  if (st != SVDQ_OK) return st;
+  if ((st = svdq_mlp_quantize(w1, w2, X, M, ws1, ws1_bytes, ws2, ws2_bytes, hip_stream)) != SVDQ_OK)
+    return st;
+  if ((st = svdq_mlp_gemm1(w1, w2, M, epilogue, ws1, ws1_bytes, ws2, ws2_bytes, hip_stream)) != SVDQ_OK)
+    return st;
+  return svdq_mlp_gemm2(w2, M, Y, y_dtype, ws2, ws2_bytes, hip_stream);
 }
 
 svdq_status_t svdq_gelu_tanh_bf16(const void *in, void *out, size_t n, void *hip_stream) {

@@ -28,6 +28,7 @@ constexpr int kPad = 256;                // M and N are padded to multiples of t
 constexpr int kLaneBytes = 24;           // 32 fp6 codes per lane
 constexpr int kBlockBytes = 64 * kLaneBytes;
 constexpr int64_t kAlign = 256;
+constexpr double kDFixScale = 4294967296.0;   // 2^32: fixed-point unit of a fused D sum
 
 constexpr int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 constexpr int rank_pad(int rank) { return rank <= 0 ? 0 : (int)round_up(rank, 32); }
@@ -116,7 +117,10 @@ struct WorkLayout {
     int64_t o = 0;
     qa = o; o = round_up(o + Mp * K * 3 / 4, kAlign);    // fp6 codes, tiled
     sa = o; o = round_up(o + G * Mp * 4, kAlign);        // fp32 scales [G][Mp]
-    d = o;  o = round_up(o + S * Mp * rp * 4, kAlign);   // fp32 partial X L1s [S][Mp][rp]
+    // D = X L1s: either fp32 partials [S][Mp][rp] from the quantiser, or,
+    // when the previous layer's GEMM quantised this layer's input in its
+    // epilogue, one int64 fixed-point sum [Mp][rp] (units of 2^-32)
+    d = o;  o = round_up(o + (S > 2 ? S : 2) * Mp * rp * 4, kAlign);
     total = o;
   }
 };
