@@ -4,9 +4,12 @@
 One step is one pass of the whole runtime path over one batch of synthetic
 input already resident in HBM:
     fc1  4608 x 3072 -> 12288, rank 32: quantise + low-rank down (kernel 1),
-         INT4 GEMM + low-rank up + bias + fused tanh-GELU (kernel 2)
-    fc2  4608 x 12288 -> 3072, rank 32: kernel 1, kernel 2
+         INT4 GEMM + low-rank up + bias + tanh-GELU, whose epilogue rounds to
+         bf16 and quantises fc2's input (codes, scales, low-rank down) (kernel 2)
+    fc2  4608 x 12288 -> 3072, rank 32: kernel 2 on that input
     AWQ  W4A16 modulation projection 1 x 3072 -> 18432 (kernel 3)
+The same step with fc1's output stored and fc2 quantised by its own kernel 1
+is timed too (`unfused_pair`).
 The offline steps (smoothing, SVD split, residual quantisation, AWQ
 quantisation) run once before timing, through the library's host code.
 
@@ -175,6 +178,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--sets", type=int, default=3, help="rotating copies of inputs and weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-unfused", action="store_true",
+                    help="do not time the unfused pair (profiling runs: only the step's own kernels)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run an elementwise copy of known size (for HBM counter calibration)")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -182,7 +187,7 @@ def main():
     args = ap.parse_args()
     if args.summarize_profile:
         t, fe, wr = args.summarize_profile
-        base = "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --calibration-copy"
+        base = "python3 bench.py --steps 5 --warmup 20 --no-cpu-baseline --calibration-copy --skip-unfused"
         cmd = {"trace": f"rocprofv3 --kernel-trace --stats -f csv -d {t} -- {base}",
                "fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d {fe} -- {base}",
                "write": f"rocprofv3 --pmc WRITE_SIZE -f csv -d {wr} -- {base}"}
@@ -245,21 +250,33 @@ def main():
         del src, dst
 
     stream = torch.cuda.current_stream(dev)
-    NEV = 6
+    NEV = 5
 
-    def step(i, ev=None):
+    def step(i, ev=None, fused=True):
         k = i % R
-        if ev: ev[0].record(stream)
-        S.linear_quantize(L1[k], X[k], ws1[k])
-        if ev: ev[1].record(stream)
-        S.linear_gemm(L1[k], M, Y1[k], ws1[k], gelu=True)
-        if ev: ev[2].record(stream)
-        S.linear_quantize(L2[k], Y1[k], ws2[k])
-        if ev: ev[3].record(stream)
-        S.linear_gemm(L2[k], M, Y2[k], ws2[k])
-        if ev: ev[4].record(stream)
+
+        def mark(j):
+            if ev:
+                ev[j].record(stream)
+        mark(0)
+        if fused:
+            # fc1's GEMM quantises fc2's input in its epilogue (no fc1 output)
+            S.mlp_quantize(L1[k], L2[k], X[k], ws1[k], ws2[k])
+            mark(1)
+            S.mlp_gemm1(L1[k], L2[k], M, ws1[k], ws2[k], gelu=True)
+            mark(2)
+            S.mlp_gemm2(L2[k], M, Y2[k], ws2[k])
+            mark(3)
+        else:
+            S.linear_quantize(L1[k], X[k], ws1[k])
+            mark(1)
+            S.linear_gemm(L1[k], M, Y1[k], ws1[k], gelu=True)
+            mark(2)
+            S.linear_quantize(L2[k], Y1[k], ws2[k])
+            S.linear_gemm(L2[k], M, Y2[k], ws2[k])
+            mark(3)
         S.awq_forward(A[k], xm[k], out=ym[k])
-        if ev: ev[5].record(stream)
+        mark(4)
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
@@ -273,13 +290,26 @@ def main():
         step(args.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    wall_unfused = None
+    if not args.skip_unfused:
+        log(f"timing {args.steps} steps of the unfused pair (fc1 output stored, fc2 quantised apart)")
+        for i in range(args.warmup // 4):
+            step(i, fused=False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(args.warmup + i, fused=False)
+        torch.cuda.synchronize()
+        wall_unfused = time.perf_counter() - t0
     log(f"timing {args.steps} steps with per-kernel events")
+    for i in range(args.warmup // 4):
+        step(i)
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(args.warmup + args.steps + i, events[i])
     torch.cuda.synchronize()
 
-    names = ["fc1_quantize", "fc1_gemm_gelu", "fc2_quantize", "fc2_gemm", "awq_m1"]
+    names = ["fc1_quantize", "fc1_gemm_gelu_quantize_fc2", "fc2_gemm", "awq_m1"]
     dur = {n: [] for n in names}
     span = []
     for ev in events:
@@ -291,7 +321,7 @@ def main():
     ops_layer = 2.0 * M * N1 * K1            # = 2 * M * N2 * K2
     value = 2 * ops_layer / (ms_per_step * 1e-3) / 1e12
 
-    k2_us = 0.5 * (avg["fc1_gemm_gelu"] + avg["fc2_gemm"])
+    k2_us = 0.5 * (avg["fc1_gemm_gelu_quantize_fc2"] + avg["fc2_gemm"])
     achieved = ops_layer / (k2_us * 1e-6) / 1e12
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "k2_traffic.json")
@@ -302,7 +332,6 @@ def main():
             traffic = tj.get("bytes_per_launch")
     r = 32
     k1_bytes_fc1 = M * K1 * 2 + K1 * 4 + K1 * r * 2 + M * K1 // 2 + M * (K1 // 64) * 4 + M * r * 4
-    k1_bytes_fc2 = M * K2 * 2 + K2 * 4 + K2 * r * 2 + M * K2 // 2 + M * (K2 // 64) * 4 + M * r * 4
     awq_bytes = a.N * a.K // 2 + a.N * (a.K // 64) * 4 + a.K * 2 + a.N * 2
     out = {
         "metric": "W4A4+low-rank linear TOPS at Flux MLP shape; % of MI355X int8 MFMA peak",
@@ -326,8 +355,10 @@ def main():
                      "ops_per_launch": ops_layer, "avg_launch_us": round(k2_us, 2)},
         "kernels_us": {n: round(v, 2) for n, v in avg.items()},
         "event_step_us": round(float(np.mean(span)), 2),
-        "k1_gbs": {"fc1": round(k1_bytes_fc1 / avg["fc1_quantize"] / 1e3, 1),
-                   "fc2": round(k1_bytes_fc2 / avg["fc2_quantize"] / 1e3, 1)},
+        "k1_gbs": {"fc1": round(k1_bytes_fc1 / avg["fc1_quantize"] / 1e3, 1)},
+        "unfused_pair": (None if wall_unfused is None else
+                         {"ms_per_step": round(wall_unfused / args.steps * 1e3, 4),
+                          "value": round(2 * ops_layer / (wall_unfused / args.steps) / 1e12, 2)}),
         "awq_gbs": round(awq_bytes / avg["awq_m1"] / 1e3, 1),
         "prepare_s": {"fc1": round(prep1, 2), "fc2": round(prep2, 2)},
         "source_hash": source_hash(),
