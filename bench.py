@@ -108,7 +108,7 @@ def _short(name):
     return name.split("(")[0].replace("void ", "")
 
 
-def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir, command):
+def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir, command, run_log=None):
     """CPU-only: turn rocprofv3 output (one --kernel-trace --stats run, one
     FETCH_SIZE pass, one WRITE_SIZE pass, all of ``bench.py
     --calibration-copy``) into the text summaries kept under profiles/ and
@@ -123,6 +123,32 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir, command):
         lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | "
                      f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                      f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    # The per-launch trace: the last `last` launches of each kernel are the
+    # bench's instrumented pass, whose event-timed mean the JSON reports
+    # (earlier launches include the warm-up while clocks settle).
+    last = 50
+    trace = _read_csv(_find(trace_dir, "kernel_trace.csv"))
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dur = {}
+    for r in trace:
+        dur.setdefault(_short(r["Kernel_Name"]), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines += ["", f"Mean over each kernel's last {last} launches (the bench's instrumented pass):", "",
+              "| kernel | launches | mean us (last) |", "|---|---:|---:|"]
+    for k, v in dur.items():
+        if len(v) >= last:
+            lines.append(f"| `{k}` | {len(v)} | {float(np.mean(v[-last:])):.2f} |")
+    k2_last = [float(np.mean(v[-last:])) for k, v in dur.items() if K2_NAME in k and len(v) >= last]
+    if k2_last:
+        lines += ["", f"{K2_NAME}: mean of its kernels' last-{last} means {float(np.mean(k2_last)):.2f} us "
+                  "(compare `roofline.avg_launch_us` of the same run)."]
+    if run_log:
+        # the JSON line the profiled bench run printed
+        js = [ln for ln in open(run_log) if ln.startswith("{")]
+        if js:
+            d = json.loads(js[-1])
+            lines += [f"The profiled run's own JSON: `roofline.avg_launch_us` = {d['roofline']['avg_launch_us']} us, "
+                      f"`kernels_us` = {d['kernels_us']}."]
     with open(os.path.join(out_dir, "kernels_flux_mlp_pair.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -182,16 +208,18 @@ def main():
                     help="do not time the unfused pair (profiling runs: only the step's own kernels)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run an elementwise copy of known size (for HBM counter calibration)")
+    ap.add_argument("--profiled-log", default=None,
+                    help="with --summarize-profile: stdout of the traced bench run (its JSON line)")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="CPU only: summarise rocprofv3 output into profiles/ and exit")
     args = ap.parse_args()
     if args.summarize_profile:
         t, fe, wr = args.summarize_profile
-        base = "python3 bench.py --steps 5 --warmup 20 --no-cpu-baseline --calibration-copy --skip-unfused"
+        base = "python3 bench.py --no-cpu-baseline --calibration-copy --skip-unfused"
         cmd = {"trace": f"rocprofv3 --kernel-trace --stats -f csv -d {t} -- {base}",
                "fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d {fe} -- {base}",
                "write": f"rocprofv3 --pmc WRITE_SIZE -f csv -d {wr} -- {base}"}
-        summarize_profiles(t, fe, wr, os.path.join(ROOT, "profiles"), cmd)
+        summarize_profiles(t, fe, wr, os.path.join(ROOT, "profiles"), cmd, args.profiled_log)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this library runs the layer on a single MI355X and "
