@@ -132,6 +132,38 @@ def test_mlp_fc2(S, mlp):
     assert rel_max_err(Yf, Yref) <= TOL_F32
 
 
+def test_mlp_pair_fused_as_benchmarked(S, mlp):
+    """The benchmarked step's MLP: fc1's GEMM quantises fc2's input in its
+    epilogue.  fc2's codes and scales equal the unfused quantiser's on the
+    same bf16 intermediate (the device's own GELU(fc1) output), bit for bit;
+    fc2's output on sampled rows matches the oracle run on that intermediate;
+    the fixed-point down-projection matches the oracle's."""
+    fc1, ref1, _, ref2 = mlp
+    M = fc1.M
+    announce("mlp fused pair: device")
+    l1, l2 = layer_from_oracle(ref1), layer_from_oracle(ref2)
+    X = bf16_to_device(fc1.X)
+    Y1 = S.linear_forward(l1, X, out_dtype=torch.bfloat16, gelu=True)
+    ws1, ws2, ws2u = l1.new_workspace(M), l2.new_workspace(M), l2.new_workspace(M)
+    Y2 = S.mlp_forward(l1, l2, X, out_dtype=torch.bfloat16, ws1=ws1, ws2=ws2)
+    S.linear_quantize(l2, Y1, ws2u)
+    torch.cuda.synchronize()
+    K2, G2, Mp, rp = ref2["K"], ref2["K"] // 64, -(-M // 256) * 256, 32
+    qa_bytes = Mp * K2 * 3 // 4
+    sa_off = -(-qa_bytes // 256) * 256
+    d_off = -(-(sa_off + G2 * Mp * 4) // 256) * 256
+    assert torch.equal(ws2[:qa_bytes], ws2u[:qa_bytes]), "fc2 codes"
+    assert torch.equal(ws2[sa_off:sa_off + G2 * Mp * 4], ws2u[sa_off:sa_off + G2 * Mp * 4]), "fc2 scales"
+    X2 = Y1.cpu().view(torch.int16).numpy().view(np.uint16)
+    rows = sample_rows(M, 5)
+    f = O.forward(ref2, X2, rows=rows)
+    err = rel_max_err(to_f64(Y2)[rows], f["Y"])
+    announce(f"mlp fused pair bf16 max rel err {err:.3e}")
+    assert err <= TOL_BF16
+    d = ws2[d_off:d_off + Mp * rp * 8].cpu().numpy().view(np.int64).reshape(Mp, rp)[rows, :32] / 2.0 ** 32
+    assert rel_max_err(d, f["D"]) <= 1e-5, "fixed-point down-projection"
+
+
 # -------------------------------------------------------------- low-res
 def test_lowres_high_rank_full(S):
     c = synth.lowres_case()

@@ -753,61 +753,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int j = 0; j < 4; ++j)
         xr[j] = *reinterpret_cast<const uint4 *>(xs + r * (WCOLS * 2) + (((8 * gl + 2 * j + h) ^ (r & 15)) << 4));
     };
-#pragma unroll
-    for (int gl = 0; gl < WCOLS / kGroup; ++gl) {
-      const int g2 = (wn + kGroup * gl) / kGroup;
-      if (g2 >= p.G2) continue;                  // padding columns past the layer's N
-      float4 io[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 *ip = reinterpret_cast<const float4 *>(p.iota2 + (int64_t)g2 * kGroup + 16 * j + 8 * h);
-        io[2 * j] = ip[0];
-        io[2 * j + 1] = ip[1];
-      }
-#pragma unroll
-      for (int i = 0; i < WTM; ++i) {
-        uint4 xr[4];
-        load_block(i, gl, xr);
-        v6u packed;
-        const float sc = quantize_lane(xr, io, packed);
-        uint8_t *qp = p.qa2 + pair_offset(g2, (wm + 32 * i) / kTile, T2, lane, 0);
-#pragma unroll
-        for (int j = 0; j < 3; ++j)
-          *reinterpret_cast<uint2 *>(qp + 512 * j) = make_uint2(packed[2 * j], packed[2 * j + 1]);
-        p.sa2[(int64_t)g2 * p.Mp + wm + 32 * i + rr] = sc;   // both halves hold the same scale
-      }
-    }
     // The next layer's low-rank down-projection over this tile's channels,
     // 32 ranks at a time: bf16 MFMA of the tile's raw bf16 values against
-    // L1s; the two wavefronts sharing rows add their halves through LDS in a
-    // fixed order, and the sum goes into the next layer's D as 64-bit fixed
-    // point (units of 2^-32; integer addition, so the result does not depend
-    // on the order in which workgroups arrive).  Partial sums are clamped to
-    // +-2^56 so no sum of the column tiles can overflow.
+    // L1s (the first 32 ranks in the same pass as the quantisation); the two
+    // wavefronts sharing rows add their halves through LDS in a fixed order,
+    // and the sum goes into the next layer's D as 64-bit fixed point (units
+    // of 2^-32; integer addition, so the result does not depend on the order
+    // in which workgroups arrive).  Partial sums are clamped to +-2^56 so no
+    // sum of the column tiles can overflow.
+    const int TB2 = p.rp2 / 32;
+    auto load_l1f = [&](int g2, int b, uint4 (&lf)[4]) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        lf[j] = *reinterpret_cast<const uint4 *>(p.l1f2 + ((((int64_t)g2 * TB2 + b) * 4 + j) * 64 + lane) * 8);
+    };
     float *exch = reinterpret_cast<float *>(smem + NWAVES * EPI_WAVE_BYTES);   // [4][16][64]
     static_assert(NWAVES * EPI_WAVE_BYTES + NWAVES * 16 * 64 * 4 <= NBUF * STAGE, "exchange fits");
-    for (int b = 0; b < p.rp2 / 32; ++b) {
-      v16f dacc[WTM];
-#pragma unroll
-      for (int i = 0; i < WTM; ++i) dacc[i] = v16f{};
-#pragma unroll
-      for (int gl = 0; gl < WCOLS / kGroup; ++gl) {
-        const int g2 = (wn + kGroup * gl) / kGroup;
-        if (g2 >= p.G2) continue;
-        uint4 lf[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          lf[j] = *reinterpret_cast<const uint4 *>(
-              p.l1f2 + ((((int64_t)g2 * (p.rp2 / 32) + b) * 4 + j) * 64 + lane) * 8);
-#pragma unroll
-        for (int i = 0; i < WTM; ++i) {
-          uint4 xr[4];
-          load_block(i, gl, xr);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            dacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8bf(xr[j]), as_v8bf(lf[j]), dacc[i], 0, 0, 0);
-        }
-      }
+    auto finish = [&](int b, const v16f (&dacc)[WTM]) {
       // wavefront (wmi, wni) finishes row tile wni of its pair's rows
 #pragma unroll
       for (int e = 0; e < 16; ++e) exch[(w * 16 + e) * 64 + lane] = wni == 0 ? dacc[1][e] : dacc[0][e];
@@ -822,6 +784,61 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                   (unsigned long long)(long long)q);
       }
       __syncthreads();                   // the exchange buffer is reused
+    };
+    v16f dacc[WTM];
+#pragma unroll
+    for (int i = 0; i < WTM; ++i) dacc[i] = v16f{};
+#pragma unroll
+    for (int gl = 0; gl < WCOLS / kGroup; ++gl) {
+      const int g2 = (wn + kGroup * gl) / kGroup;
+      if (g2 >= p.G2) continue;                  // padding columns past the layer's N
+      float4 io[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 *ip = reinterpret_cast<const float4 *>(p.iota2 + (int64_t)g2 * kGroup + 16 * j + 8 * h);
+        io[2 * j] = ip[0];
+        io[2 * j + 1] = ip[1];
+      }
+      uint4 lf[4];
+      if (TB2 > 0) load_l1f(g2, 0, lf);
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) {
+        uint4 xr[4];
+        load_block(i, gl, xr);
+        v6u packed;
+        const float sc = quantize_lane(xr, io, packed);
+        uint8_t *qp = p.qa2 + pair_offset(g2, (wm + 32 * i) / kTile, T2, lane, 0);
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+          *reinterpret_cast<uint2 *>(qp + 512 * j) = make_uint2(packed[2 * j], packed[2 * j + 1]);
+        p.sa2[(int64_t)g2 * p.Mp + wm + 32 * i + rr] = sc;   // both halves hold the same scale
+        if (TB2 > 0) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            dacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8bf(xr[j]), as_v8bf(lf[j]), dacc[i], 0, 0, 0);
+        }
+      }
+    }
+    if (TB2 > 0) finish(0, dacc);
+    for (int b = 1; b < TB2; ++b) {
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) dacc[i] = v16f{};
+#pragma unroll
+      for (int gl = 0; gl < WCOLS / kGroup; ++gl) {
+        const int g2 = (wn + kGroup * gl) / kGroup;
+        if (g2 >= p.G2) continue;
+        uint4 lf[4];
+        load_l1f(g2, b, lf);
+#pragma unroll
+        for (int i = 0; i < WTM; ++i) {
+          uint4 xr[4];
+          load_block(i, gl, xr);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            dacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8bf(xr[j]), as_v8bf(lf[j]), dacc[i], 0, 0, 0);
+        }
+      }
+      finish(b, dacc);
     }
   } else if constexpr (MODE == MODE_FWD) {
     // Bias (+ GELU), then the wavefront's tile goes out through its own LDS
