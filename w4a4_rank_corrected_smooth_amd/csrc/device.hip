@@ -2,8 +2,11 @@
 //
 //  K1  k1_quantize_lowrank_down  smoothing, per-group INT4 activation codes
 //                                and scales, low-rank down-projection D = X L1s
-//  K2  k2_w4a4_gemm              INT4 x INT4 group GEMM on int8 MFMA, fp32
-//                                per-group scaling, + D L2 + bias (+ GELU)
+//  K2  k2_w4a4_gemm              INT4 x INT4 group GEMM on the fp6 matrix
+//                                instruction (codes -7..7 held exactly), fp32
+//                                per-group scaling, + D L2 + bias (+ GELU);
+//                                for an MLP pair, the epilogue quantises the
+//                                next layer's input instead of storing Y
 //  K3  k3_awq_w4a16              AWQ W4A16 GEMV/GEMM on fp16 MFMA
 //  +   GELU glue kernel and canonical-layout inspection kernels.
 //
@@ -22,8 +25,6 @@
 
 using namespace svdq;
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -31,7 +32,6 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef unsigned v6u __attribute__((ext_vector_type(6)));
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v32f __attribute__((ext_vector_type(32)));
 
 // ------------------------------------------------------------ small helpers
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
