@@ -190,6 +190,47 @@ def test_awq_quantizer_bit_exact_and_packer():
     assert np.array_equal(z.view(np.uint16), rz.view(np.uint16))
 
 
+def test_awq_blob_layout():
+    """AWQ codes and scale words sit where the documented layout says: tiles
+    of 16 output channels; per (tile, pair of groups) a 1024-byte block where
+    lane = column + 16 * quarter holds 16 bytes (first group of the pair, then
+    the second); in each 32-bit word the even channels fill the low half,
+    nibble j = channel 2 j, the odd ones the high half.  Scale words
+    (s | z << 16) follow as [Np][G rounded up to 4].  Padding is zero."""
+    rng = np.random.default_rng(7)
+    N, K = 40, 320                       # 3 tiles (last one ragged), G = 5: odd
+    G, T, P, G4 = 5, 3, 3, 8
+    q = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    s = rng.integers(0x3000, 0x4000, size=(N, G), dtype=np.uint16)
+    z = rng.integers(0x4000, 0x4b00, size=(N, G), dtype=np.uint16)
+    n_bytes = S._lib.awq_device_weights_bytes(N, K)
+    qbytes = T * P * 1024
+    s_off = (qbytes + 255) // 256 * 256
+    assert n_bytes == (s_off + T * 16 * G4 * 4 + 255) // 256 * 256
+    blob = np.empty(n_bytes, np.uint8)
+    assert S._lib.awq_pack_device_weights(q.ctypes.data, s.ctypes.data, z.ctypes.data, N, K,
+                                          blob.ctypes.data, n_bytes) == 0
+    codes = np.empty((N, K), np.int64)
+    codes[:, 0::2] = q & 15
+    codes[:, 1::2] = q >> 4
+    qdev = blob[:qbytes]
+    seen = np.zeros(qbytes, bool)
+    for n in range(N):
+        for k in range(K):
+            g, kk = divmod(k, 64)
+            lane = n % 16 + 16 * (kk // 16)
+            word_at = ((n // 16) * P + g // 2) * 1024 + lane * 16 + 8 * (g % 2) + 4 * ((kk % 16) // 8)
+            word = int.from_bytes(bytes(qdev[word_at: word_at + 4]), "little")
+            c = kk % 8
+            shift = 4 * (c // 2) + (16 if c % 2 else 0)
+            assert (word >> shift) & 15 == codes[n, k], (n, k)
+            seen[word_at: word_at + 4] = True
+    assert not np.any(qdev[~seen])       # padded columns, the missing sixth group
+    sz = blob[s_off: s_off + T * 16 * G4 * 4].view(np.uint32).reshape(T * 16, G4)
+    assert np.array_equal(sz[:N, :G], s.astype(np.uint32) | (z.astype(np.uint32) << 16))
+    assert not np.any(sz[N:]) and not np.any(sz[:, G:])
+
+
 # ---------------------------------------------------------------- errors
 INV, SHAPE, NODEV, WS, NUM = 1, 2, 3, 5, 6
 FAKE = 1 << 20          # aligned, never dereferenced: validation fails first

@@ -901,54 +901,61 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // ======================================================================= K3
 // AWQ W4A16.  A workgroup of 4 wavefronts owns a tile of 16 output channels;
-// wavefront w takes a contiguous quarter of the groups of 64 input channels,
-// kAwqChunk groups at a time.  Per chunk it first copies the chunk's
-// activations (M rows, a few kilobytes shared by every workgroup, so cache
-// hits) into its own LDS with the global->LDS path, then issues all its code
-// and scale loads (the HBM stream) and waits only for the copies; each
-// group's compute then waits for its own loads alone, in issue order.  Every
-// load is unconditional (indices clamped; groups past the range weigh 0), so
-// the completion counts are exact.  For each group, lane l (channel l % 16,
-// quarter q = l / 16) turns its 16 codes into fp16 (q - z) with the
-// 1024-offset trick (0x6400 | code is the fp16 value 1024 + code;
-// subtracting 1024 + z is exact), the activations [16, 64] read from LDS are
-// the A operand, and two v_mfma_f32_16x16x32_f16 give the group's inner
-// sums; acc += s * sum in fp32.  Rows m >= M repeat row M - 1 and are never
-// stored.  The four partial sums meet in LDS, in a fixed order.
-constexpr int kAwqChunk = 12;
+// wavefront w takes a contiguous quarter of the groups of 64 input channels
+// (rounded up to a multiple of 4, so its range starts on a pair of code
+// blocks and on a 16-byte quad of scale words), kAwqChunk groups at a time.
+// Per chunk it first copies the chunk's activations (M rows, a few kilobytes
+// shared by every workgroup, so cache hits) into its own LDS with the
+// global->LDS path, then issues its code loads (16 bytes per lane: two
+// groups) and scale loads (16 bytes: four groups), the HBM stream, and waits
+// only for the copies; each group's compute then waits for its own loads
+// alone, in issue order.  Every load is unconditional (indices clamped;
+// groups past the range weigh 0, and every value they touch is finite: the
+// copies fill whole rows of kAwqChunk groups, repeating the last group of
+// the range, and the blob's padding words are zero), so the completion
+// counts are exact.  For each group, lane l (channel l % 16, quarter
+// q = l / 16) turns its 16 codes into fp16 (q - z) with the 1024-offset
+// trick (0x6400 | code is the fp16 value 1024 + code; subtracting 1024 + z
+// is exact), the activations [16, 64] read from LDS are the A operand, and
+// two v_mfma_f32_16x16x32_f16 give the group's inner sums; acc += s * sum in
+// fp32.  Rows m >= M repeat row M - 1 and are never stored.  The four
+// partial sums meet in LDS, in a fixed order.
+constexpr int kAwqChunk = 12;                          // a multiple of 4
 __global__ __launch_bounds__(256) void k3_awq_w4a16(const uint8_t *__restrict__ qd,
                                                      const uint32_t *__restrict__ sz,
                                                      const uint16_t *__restrict__ x, int M,
-                                                     int N, int Np, int K,
+                                                     int N, int K,
                                                      const uint16_t *__restrict__ bias,
                                                      uint16_t *__restrict__ y) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int tile = blockIdx.x;
   const int G = K / kGroup;
-  const int Gq = (G + 3) / 4;
+  const int G4 = (G + 3) & ~3;
+  const int Gq = ((G + 3) / 4 + 3) & ~3;
   const int g0 = min(G, w * Gq), g1 = min(G, g0 + Gq);
   const int m = lane & 15, qtr = lane >> 4;
   const int n = tile * kAwqTile + (lane & 15);
-  const uint8_t *qbase = qd + (int64_t)tile * G * kAwqBlockBytes + lane * 8;
+  const uint8_t *qbase = qd + (int64_t)tile * ((G + 1) / 2) * kAwqBlockBytes + lane * 16;
   extern __shared__ __attribute__((aligned(16))) uint8_t awq_lds[];
   v4f acc = v4f{};
-  // this wavefront's copy of the chunk's activations, rows 0..M-1, one
-  // 16-byte piece per lane and copy (global->LDS path)
-  const int xw_bytes = (M * kAwqChunk * (kGroup / 8) + 63) / 64 * 1024;
+  // this wavefront's copy of the chunk's activations: rows 0..M-1 of
+  // kAwqChunk groups each, one 16-byte piece per lane and copy
+  constexpr int npr = kAwqChunk * (kGroup / 8);         // pieces per row
+  const int npc = M * npr;
+  const int xw_bytes = (npc + 63) / 64 * 1024;
   const uint32_t xl_u32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)awq_lds +
                           (uint32_t)(__builtin_amdgcn_readfirstlane(w) * xw_bytes);
   const uint16_t *xl = reinterpret_cast<const uint16_t *>(awq_lds + w * xw_bytes);
+  const uint16_t *xm = xl + min(m, M - 1) * (npr * 8) + 16 * qtr;
   for (int gc = g0; gc < g1; gc += kAwqChunk) {
-    const int nG = min(kAwqChunk, g1 - gc);
-    const int npr = nG * (kGroup / 8);                  // pieces per row
-    const int npc = M * npr;
     // activations first (cache hits), then the code and scale stream; every
     // load after the copies is unconditional, so the copies are complete
-    // once at most 2 kAwqChunk loads remain
+    // once at most kAwqChunk / 2 + kAwqChunk / 4 loads remain
     for (int c0 = 0; c0 < npc; c0 += 64) {
       const int pc = min(c0 + lane, npc - 1);
       const int mr = pc / npr, o = pc - mr * npr;
-      lds_dma16(x + (int64_t)mr * K + gc * kGroup + o * 8, xl_u32 + (uint32_t)(c0 * 16));
+      const int gi = min(gc + o / 8, g1 - 1);
+      lds_dma16(x + (int64_t)mr * K + gi * kGroup + (o % 8) * 8, xl_u32 + (uint32_t)(c0 * 16));
     }
     // The code and scale loads must follow the copies in issue order (the
     // wait below counts them); their addresses take an offset from an empty
@@ -956,32 +963,37 @@ __global__ __launch_bounds__(256) void k3_awq_w4a16(const uint8_t *__restrict__ 
     int zero = 0;
     asm volatile("" : "+s"(zero));
     const uint8_t *qb = qbase + zero;
-    const uint32_t *szb = sz + n + zero;
-    uint2 cw[kAwqChunk];
-    uint32_t szw[kAwqChunk];
+    const uint32_t *szb = sz + (int64_t)n * G4 + zero;
+    uint4 cw[kAwqChunk / 2];
+    uint4 szw[kAwqChunk / 4];
 #pragma unroll
-    for (int i = 0; i < kAwqChunk; ++i) {
-      const int gg = min(gc + i, g1 - 1);
-      cw[i] = *reinterpret_cast<const uint2 *>(qb + (int64_t)gg * kAwqBlockBytes);
-      szw[i] = szb[(int64_t)gg * Np];
+    for (int j = 0; j < kAwqChunk / 2; ++j) {
+      const int pr = min(gc / 2 + j, (g1 - 1) / 2);
+      cw[j] = *reinterpret_cast<const uint4 *>(qb + (int64_t)pr * kAwqBlockBytes);
     }
-    vmcnt_wait<2 * kAwqChunk>();
-    const uint16_t *xm = xl + min(m, M - 1) * (npr * 8) + 16 * qtr;
+#pragma unroll
+    for (int j = 0; j < kAwqChunk / 4; ++j) {
+      const int qd4 = min(gc / 4 + j, (g1 - 1) / 4);
+      szw[j] = *reinterpret_cast<const uint4 *>(szb + 4 * qd4);
+    }
+    vmcnt_wait<kAwqChunk / 2 + kAwqChunk / 4>();
 #pragma unroll
     for (int i = 0; i < kAwqChunk; ++i) {
-      {
       const uint4 xa0 = *reinterpret_cast<const uint4 *>(xm + i * kGroup);
       const uint4 xa1 = *reinterpret_cast<const uint4 *>(xm + i * kGroup + 8);
-      const _Float16 zf = __builtin_bit_cast(_Float16, (uint16_t)(szw[i] >> 16));
-      // groups past the wavefront's range repeat its last one and weigh 0,
-      // so every load above is used and none is moved below the wait
-      const float sf = gc + i < g1 ? (float)__builtin_bit_cast(_Float16, (uint16_t)(szw[i] & 0xFFFF)) : 0.0f;
+      const uint4 q4 = szw[i / 4];
+      const uint32_t szv = (i % 4 == 0) ? q4.x : (i % 4 == 1) ? q4.y : (i % 4 == 2) ? q4.z : q4.w;
+      const _Float16 zf = __builtin_bit_cast(_Float16, (uint16_t)(szv >> 16));
+      // groups past the wavefront's range weigh 0, so every load above is
+      // used and none is moved below the wait
+      const float sf = gc + i < g1 ? (float)__builtin_bit_cast(_Float16, (uint16_t)(szv & 0xFFFF)) : 0.0f;
       const _Float16 off = -((_Float16)1024.0f + zf);
       const v2h off2 = v2h{off, off};
       v8h bop[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const uint32_t word = half ? cw[i].y : cw[i].x;
+        const uint4 c = cw[i / 2];
+        const uint32_t word = (i % 2 == 0) ? (half ? c.y : c.x) : (half ? c.w : c.z);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint32_t pr = ((word >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
@@ -997,7 +1009,6 @@ __global__ __launch_bounds__(256) void k3_awq_w4a16(const uint8_t *__restrict__ 
       // output layout: lane holds rows 4 * (lane / 16) + e, column lane % 16
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(part[e], sf, acc[e]);
-      }
     }
   }
   __shared__ v4f red[4][64];
@@ -1460,7 +1471,7 @@ svdq_status_t awq_w4a16_forward(const void *blob, int N, int K, const void *x, i
   hipLaunchKernelGGL(k3_awq_w4a16, dim3((unsigned)(L.Np / kAwqTile)), dim3(256), lds,
                      static_cast<hipStream_t>(hip_stream), b + L.q,
                      reinterpret_cast<const uint32_t *>(b + L.sz), static_cast<const uint16_t *>(x), M,
-                     N, (int)L.Np, K, static_cast<const uint16_t *>(bias), static_cast<uint16_t *>(y));
+                     N, K, static_cast<const uint16_t *>(bias), static_cast<uint16_t *>(y));
   return launch_status("AWQ kernel launch");
 }
 

@@ -268,7 +268,7 @@ svdq_status_t awq_pack(const uint8_t *q, const uint16_t *s, const uint16_t *z, i
   uint32_t *sz = reinterpret_cast<uint32_t *>(b + L.sz);
   for (int64_t n = 0; n < N; ++n)
     for (int64_t g = 0; g < L.G; ++g)
-      sz[g * L.Np + n] = (uint32_t)s[n * L.G + g] | ((uint32_t)z[n * L.G + g] << 16);
+      sz[n * awq_g4(L.G) + g] = (uint32_t)s[n * L.G + g] | ((uint32_t)z[n * L.G + g] << 16);
   return SVDQ_OK;
 }
 

@@ -126,21 +126,27 @@ struct WorkLayout {
 };
 
 // AWQ W4A16 device blob.  Output channels are cut into tiles of 16; for each
-// (tile, group of 64) there is a 512-byte block: lane l (column l % 16 of the
-// tile, quarter q = l / 16 of the group) holds the 16 codes of input channels
-// 64 g + 16 q + [0, 16) in 8 bytes.  Within each 4-byte word the low 16 bits
-// hold the codes of the even channels (nibble j = channel 2j) and the high
-// 16 bits those of the odd channels, so one shift and one mask turn a word
-// into pairs of fp16 operands.  Scales and zero points follow as one
-// 32-bit word per (group, column): fp16 scale | fp16 zero << 16, [G][N16].
+// (tile, pair of groups of 64) there is a 1024-byte block: lane l (column
+// l % 16 of the tile, quarter q = l / 16 of a group) holds, in 16 bytes, the
+// 16 codes of input channels 64 g + 16 q + [0, 16) of the pair's first group
+// and then those of its second (zero past the last group), so one 16-byte
+// load brings two groups.  Within each 4-byte word the low 16 bits hold the
+// codes of the even channels (nibble j = channel 2j) and the high 16 bits
+// those of the odd channels, so one shift and one mask turn a word into pairs
+// of fp16 operands.  Scales and zero points follow as one 32-bit word per
+// (column, group): fp16 scale | fp16 zero << 16, [Np][G4] with G4 = G rounded
+// up to 4, so one 16-byte load brings a column's words for four groups.
 constexpr int kAwqTile = 16;
-constexpr int kAwqBlockBytes = 512;
+constexpr int kAwqBlockBytes = 1024;   // a pair of groups
+
+constexpr int64_t awq_pairs(int64_t G) { return (G + 1) / 2; }
+constexpr int64_t awq_g4(int64_t G) { return round_up(G, 4); }
 
 // byte offset and nibble shift of the code for (n, k)
 constexpr int64_t awq_code_byte(int64_t n, int64_t k, int64_t G) {
-  return ((n / kAwqTile) * G + k / kGroup) * kAwqBlockBytes +
-         ((n % kAwqTile) + 16 * ((k % kGroup) / 16)) * 8 + 4 * ((k % 16) / 8) +
-         (((k % 8) / 2) / 2) + 2 * (k % 2);
+  return ((n / kAwqTile) * awq_pairs(G) + k / kGroup / 2) * kAwqBlockBytes +
+         ((n % kAwqTile) + 16 * ((k % kGroup) / 16)) * 16 + 8 * ((k / kGroup) % 2) +
+         4 * ((k % 16) / 8) + (((k % 8) / 2) / 2) + 2 * (k % 2);
 }
 constexpr int awq_code_shift(int64_t k) { return 4 * (((k % 8) / 2) % 2); }
 
@@ -150,8 +156,8 @@ struct AwqLayout {
   constexpr AwqLayout(int64_t N_, int64_t K_)
       : N(N_), K(K_), G(K_ / kGroup), Np(round_up(N_, kAwqTile)) {
     int64_t o = 0;
-    q = o;  o = round_up(o + Np * K / 2, kAlign);
-    sz = o; o = round_up(o + G * Np * 4, kAlign);
+    q = o;  o = round_up(o + Np / kAwqTile * awq_pairs(G) * kAwqBlockBytes, kAlign);
+    sz = o; o = round_up(o + Np * awq_g4(G) * 4, kAlign);
     total = o;
   }
 };
