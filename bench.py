@@ -195,6 +195,191 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir, command, run_lo
 CALIBRATION_BYTES = 256 << 20
 
 
+def summarize_configs(trace_dir, sweep_jsonl, out_path, command):
+    """Exact per-configuration kernel durations from a rocprofv3 kernel trace
+    of ``bench.py --configs``: the sweep launches each timed kernel 8 + steps
+    + 5 x 24 times in a row, in a fixed order of configurations, so the
+    trace's runs of one kernel split into those series; the last 120 launches
+    of each are the back-to-back ones."""
+    import csv
+    import glob
+    import numpy as np
+    cfgs = [json.loads(l) for l in open(sweep_jsonl) if l.startswith("{")]
+    path = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)[0]
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    runs = []
+    for r in rows:
+        name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if runs and runs[-1][0] == name:
+            runs[-1][1].append(d)
+        else:
+            runs.append((name, [d]))
+    per = 8 + 50 + 5 * 24
+    series = []      # (kernel, durations of one timed series)
+    for name, ds in runs:
+        if not any(k in name for k in ("k1_quantize", "k2_w4a4", "k3_awq")) or len(ds) < per:
+            continue
+        n = len(ds) // per
+        for i in range(n):
+            series.append((name, ds[len(ds) - (n - i) * per: len(ds) - (n - i - 1) * per]))
+    lines = ["# Kernel durations per configuration (rocprofv3 kernel trace)", "",
+             "Command:", "", "```", command, "```", "",
+             "Each kernel runs as its own series (8 warm-up launches, 50 launches between events, "
+             "then 5 x 24 back to back) over rotating buffer sets; durations below are the trace's "
+             "own, over the 120 back-to-back launches. Rates use the algorithmic work of each "
+             "kernel (K2: 2MNK int ops; K1: X + 1/lambda + L1s + codes + scales + D bytes; "
+             "K3: codes + scales/zeros + x + y bytes).", "",
+             "| configuration | kernel | median us | p10 us | p90 us | rate | fraction of peak |",
+             "|---|---|---:|---:|---:|---:|---:|"]
+    si = 0
+    for c in cfgs:
+        if "k3" in c:
+            kinds = [("K3", "k3_awq")]
+        else:
+            kinds = [("K1", "k1_quantize"), ("K2", "k2_w4a4")]
+        for label, key in kinds:
+            while si < len(series) and key not in series[si][0]:
+                si += 1
+            if si >= len(series):
+                break
+            name, ds = series[si]
+            si += 1
+            b2b = np.array(ds[-120:])
+            med = float(np.median(b2b))
+            M, N, K = c["M"], c["N"], c["K"]
+            if label == "K2":
+                rate = 2.0 * M * N * K / med / 1e6
+                txt, frac = f"{rate:.0f} TOPS", rate / PEAK_INT8_TOPS
+            elif label == "K1":
+                r = c["rank"]
+                b = 2 * M * K + 4 * K + 2 * K * r + M * K // 2 + 4 * M * (K // 64) + 4 * M * r
+                rate = b / med / 1e3
+                txt, frac = f"{rate:.0f} GB/s", rate / PEAK_HBM_GBS
+            else:
+                b = N * K // 2 + N * (K // 64) * 4 + M * K * 2 + M * N * 2
+                rate = b / med / 1e3
+                txt, frac = f"{rate:.0f} GB/s", rate / PEAK_HBM_GBS
+            lines.append(f"| {c['config']} ({M}x{K}->{N}) | `{name}` | {med:.2f} | "
+                         f"{np.percentile(b2b, 10):.2f} | {np.percentile(b2b, 90):.2f} | {txt} | {frac:.1%} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def config_sweep(args):
+    """Per-configuration kernel timings (not the one-line contract): for each
+    W4A4 configuration, the quantiser (kernel 1) and the GEMM (kernel 2) are
+    timed apart, and the AWQ kernel at M = 1, 2, 4, 8, 16.  Each kernel is
+    timed two ways over rotating buffer sets (enough copies that a series
+    touches more than the 256 MB Infinity Cache): per launch between HIP
+    events (median, p10, p90; each includes a few microseconds of event
+    overhead), and as the mean of 24 launches back to back between two
+    events.  One JSON line per configuration; a rocprofv3 kernel trace of
+    this mode gives the exact durations."""
+    import numpy as np
+    import torch
+    import synth
+    import w4a4_rank_corrected_smooth_amd as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    S.device_check()
+    stream = torch.cuda.current_stream(dev)
+    reps, batch = args.steps, 24
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def nsets(bytes_per_set):
+        return int(min(32, max(3, -(-640e6 // bytes_per_set))))
+
+    def timed(fn, R):
+        for i in range(8):
+            fn(i % R)
+        torch.cuda.synchronize()
+        per = []
+        for i in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(i % R)
+            e1.record(stream)
+            per.append((e0, e1))
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) * 1e3 for a, b in per])
+        b2b = []
+        for r in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(batch):
+                fn(i % R)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            b2b.append(e0.elapsed_time(e1) * 1e3 / batch)
+        return {"median_us": round(float(np.median(t)), 2), "p10_us": round(float(np.percentile(t, 10)), 2),
+                "p90_us": round(float(np.percentile(t, 90)), 2),
+                "back_to_back_us": round(float(np.median(b2b)), 2)}
+
+    def w4a4(name, M, N, K, r, hw, Xbits, gelu):
+        R = nsets(2 * M * K + M * N * 2 + N * K // 2 + S.workspace_bytes(M, N, K, r))
+        log(f"{name}: {R} buffer sets")
+        Ls = [S.Linear(hw, dev) for _ in range(R)]
+        Xs = [dev_bf16(Xbits) if isinstance(Xbits, np.ndarray) else Xbits.clone() for _ in range(R)]
+        ws = [Ls[0].new_workspace(M) for _ in range(R)]
+        Ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        for k in range(R):
+            S.linear_quantize(Ls[k], Xs[k], ws[k])
+        k1 = timed(lambda k: S.linear_quantize(Ls[k], Xs[k], ws[k]), R)
+        k2 = timed(lambda k: S.linear_gemm(Ls[k], M, Ys[k], ws[k], gelu=gelu), R)
+        ops = 2.0 * M * N * K
+        k1_bytes = 2 * M * K + 4 * K + 2 * K * r + M * K // 2 + 4 * M * (K // 64) + 4 * M * r
+        t1, t2 = k1["back_to_back_us"], k2["back_to_back_us"]
+        out = {"config": name, "M": M, "N": N, "K": K, "rank": r, "gelu": gelu, "sets": R,
+               "k1": k1, "k2": k2,
+               "k2_tops": round(ops / t2 / 1e6, 1), "k2_frac_int8": round(ops / t2 / 1e6 / PEAK_INT8_TOPS, 4),
+               "k1_gbs": round(k1_bytes / t1 / 1e3, 1), "k1_frac_hbm": round(k1_bytes / t1 / 1e3 / PEAK_HBM_GBS, 4),
+               "layer_tops": round(ops / (t1 + t2) / 1e6, 1),
+               "lowrank_gflop": round(2.0 * M * (K + N) * r / 1e9, 2)}
+        print(json.dumps(out), flush=True)
+        del Ls, Xs, ws, Ys
+        torch.cuda.empty_cache()
+
+    c = synth.tiny_case()
+    w4a4("tiny", c.M, c.N, c.K, 16, S.prepare_weights(c.W, c.calib_absmax(), c.bias, 16), c.X, False)
+    c = synth.qkv_case()
+    log("preparing QKV on the host")
+    w4a4("qkv", c.M, c.N, c.K, 32, S.prepare_weights(c.W, c.calib_absmax(), c.bias, 32), c.X, False)
+    fc1, W2, b2 = synth.mlp_cases()
+    log("preparing fc1 on the host")
+    hw1 = S.prepare_weights(fc1.W, fc1.calib_absmax(), fc1.bias, 32)
+    w4a4("mlp_fc1_gelu", fc1.M, fc1.N, fc1.K, 32, hw1, fc1.X, True)
+    L1 = S.Linear(hw1, dev)
+    Y1 = S.linear_forward(L1, dev_bf16(fc1.X), out_dtype=torch.bfloat16, gelu=True)
+    torch.cuda.synchronize()
+    ax2 = S.calibration_absmax(Y1[:64].cpu().view(torch.int16).numpy().view(np.uint16))
+    log("preparing fc2 on the host")
+    hw2 = S.prepare_weights(W2, ax2, b2, 32)
+    del L1
+    w4a4("mlp_fc2", fc1.M, fc1.K, fc1.N, 32, hw2, Y1, False)
+    del Y1
+    c = synth.lowres_case()
+    log("preparing the low-resolution layer on the host")
+    w4a4("lowres_r128", c.M, c.N, c.K, 128, S.prepare_weights(c.W, c.calib_absmax(), c.bias, 128), c.X, False)
+    a = synth.awq_case()
+    q, sc, z = S.awq_quantize_weights(a.W)
+    R = nsets(a.N * a.K // 2 + a.N * (a.K // 64) * 4)
+    A = [S.AwqLinear(q, sc, z, dev) for _ in range(R)]
+    for M in (1, 2, 4, 8, 16):
+        xs = [torch.from_numpy(np.ascontiguousarray(a.x[:M])).to(dev) for _ in range(R)]
+        ys = [torch.empty((M, a.N), dtype=torch.float16, device=dev) for _ in range(R)]
+        k3 = timed(lambda k: S.awq_forward(A[k], xs[k], out=ys[k]), R)
+        nbytes = a.N * a.K // 2 + a.N * (a.K // 64) * 4 + M * a.K * 2 + M * a.N * 2
+        t3 = k3["back_to_back_us"]
+        print(json.dumps({"config": f"awq_m{M}", "M": M, "N": a.N, "K": a.K, "sets": R, "k3": k3,
+                          "k3_gbs": round(nbytes / t3 / 1e3, 1),
+                          "k3_frac_hbm": round(nbytes / t3 / 1e3 / PEAK_HBM_GBS, 4)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,7 +397,16 @@ def main():
                     help="with --summarize-profile: stdout of the traced bench run (its JSON line)")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="CPU only: summarise rocprofv3 output into profiles/ and exit")
+    ap.add_argument("--configs", action="store_true",
+                    help="per-configuration kernel timings (one JSON line each) instead of the step")
+    ap.add_argument("--summarize-configs", nargs=2, metavar=("TRACE_DIR", "SWEEP_JSONL"),
+                    help="CPU only: summarise a rocprofv3 trace of --configs into profiles/ and exit")
     args = ap.parse_args()
+    if args.summarize_configs:
+        t, j = args.summarize_configs
+        summarize_configs(t, j, os.path.join(ROOT, "profiles", "kernels_all_configs.md"),
+                          f"rocprofv3 --kernel-trace --stats -f csv -d {t} -- python3 bench.py --configs")
+        return
     if args.summarize_profile:
         t, fe, wr = args.summarize_profile
         base = "python3 bench.py --no-cpu-baseline --calibration-copy --skip-unfused"
@@ -225,6 +419,10 @@ def main():
         print(f"bench.py measures one GPU: this library runs the layer on a single MI355X and "
               f"has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+
+    if args.configs:
+        config_sweep(args)
+        return
 
     import numpy as np
     import torch
