@@ -197,11 +197,19 @@ def test_awq_full(S, awq, M):
     assert rel_max_err(y, yref) <= 2e-3 + 2.0 ** -11
 
 
-def test_awq_ragged_with_bias(S):
-    a = synth.awq_case(m_max=5, N=100, K=192, seed=44)
+@pytest.mark.parametrize("M,N,K", [(5, 100, 192), (16, 250, 1600), (4, 100, 1600), (9, 48, 768),
+                                   (7, 17, 832), (1, 33, 64), (12, 4100, 3072), (10, 40, 64),
+                                   (13, 272, 4160)])
+def test_awq_ragged_with_bias(S, M, N, K):
+    """Both AWQ kernels (one private activation copy per wavefront up to 9
+    rows, copies shared by two wavefronts from 10): ragged column tiles,
+    spare wavefronts, odd group counts, one chunk, several chunks, a last
+    chunk past the groups, a half with no groups of its own."""
+    announce(f"awq ragged M={M} N={N} K={K}")
+    a = synth.awq_case(m_max=M, N=N, K=K, seed=44 + M)
     q, s, z = OA.quantize(a.W)
     layer = S.AwqLinear(OA.pack(q), s, z, "cuda")
-    bias = (np.random.default_rng(1).standard_normal(100) * 0.01).astype(np.float16)
+    bias = (np.random.default_rng(1).standard_normal(N) * 0.01).astype(np.float16)
     y = to_f64(S.awq_forward(layer, torch.from_numpy(a.x).to("cuda"),
                              bias=torch.from_numpy(bias).to("cuda")))
     yref = OA.forward(a.x, q, s, z, bias.astype(np.float64))
