@@ -207,6 +207,73 @@ svdq_status_t svdq_mlp_gemm2(const svdq_weights_t *w2, int M, void *Y, svdq_dtyp
 svdq_status_t svdq_gelu_tanh_bf16(const void *in, void *out, size_t n,
                                   void *hip_stream);
 
+/* ===================================================== FP4 (MXFP4) variant
+ * The 4-bit path in the FP4 form the pages name beside INT4 ("Bringing
+ * Nunchaku 4-bit diffusion inference to Diffusers", Vietnamese edition,
+ * section "Giới thiệu Nunchaku Lite"; Korean edition, section "Diffusers 내
+ * Nunchaku Lite 통합": an NVFP4 path for Blackwell, whose numerics the pages
+ * do not give).  Everything of the INT4 method is kept (smoothing, low-rank
+ * split, residual, 16-bit branch); the residual weights and the smoothed
+ * activations are encoded in OCP Microscaling MXFP4 instead, the
+ * block-scaled format gfx950's matrix instructions take natively:
+ *   - blocks of 32 consecutive values along K share one power-of-two scale
+ *     2^e, e = floor(log2(max |v|)) - 2 clamped to [-127, 127] (-127 for an
+ *     all-zero block), stored as the E8M0 byte e + 127;
+ *   - each value v / 2^e becomes an FP4 E2M1 code (sign bit 3; magnitudes
+ *     0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes 0..7), nearest value, ties to the
+ *     even mantissa bit, saturating at 6, zero stored as +0.
+ * The matrix instruction applies both scales, so the GEMM needs no
+ * per-element scaling work.  K must be a multiple of 64. */
+
+/* Host-side prepared MXFP4 weights; sizes from svdq_mx_host_weights_sizes
+ * (order: inv_lambda, l1s, l2, qweight, wscales, bias). */
+typedef struct {
+  int32_t N, K, rank;
+  float *inv_lambda;   /* [K]       as in svdq_host_weights_t */
+  uint16_t *l1s;       /* [K, rank] as in svdq_host_weights_t */
+  uint16_t *l2;        /* [rank, N] as in svdq_host_weights_t */
+  uint8_t *qweight;    /* [N, K/2]  E2M1 codes, byte j = code 2j | code 2j+1 << 4 */
+  uint8_t *wscales;    /* [N, K/32] E8M0 block scales (biased exponents) */
+  float *bias;         /* [N]       fp32 */
+} svdq_mx_host_weights_t;
+
+svdq_status_t svdq_mx_host_weights_sizes(int N, int K, int rank, size_t sizes_out[6]);
+
+/* Steps 1 and 2 of svdq_prepare_weights, then the residual rows in MXFP4.
+ * Same arguments and errors (no group size: blocks are 32). */
+svdq_status_t svdq_mx_prepare_weights(const uint16_t *W_bf16, int N, int K,
+                                      const float *act_absmax,
+                                      const uint16_t *bias_bf16, int rank,
+                                      svdq_mx_host_weights_t *out);
+
+size_t svdq_mx_device_weights_bytes(int N, int K, int rank);
+svdq_status_t svdq_mx_pack_device_weights(const svdq_mx_host_weights_t *in,
+                                          void *host_blob, size_t bytes);
+size_t svdq_mx_workspace_bytes(int M, int N, int K, int rank);
+
+/* Y = linear(X) [+ epilogue] through the MXFP4 path, with the conventions of
+ * svdq_linear_forward; `w` describes a blob packed by
+ * svdq_mx_pack_device_weights.  Two kernels: (1) smoothing + MXFP4 encoding
+ * of X + low-rank down-projection; (2) the block-scaled FP4 GEMM with the
+ * low-rank up-projection, bias (+ GELU) in its epilogue.  The quantize and
+ * GEMM halves are also callable apart, as for the INT4 path. */
+svdq_status_t svdq_mx_linear_forward(const svdq_weights_t *w, const void *X, int M,
+                                     void *Y, svdq_dtype_t y_dtype,
+                                     svdq_epilogue_t epilogue, void *workspace,
+                                     size_t ws_bytes, void *hip_stream);
+svdq_status_t svdq_mx_linear_quantize(const svdq_weights_t *w, const void *X, int M,
+                                      void *workspace, size_t ws_bytes, void *hip_stream);
+svdq_status_t svdq_mx_linear_gemm(const svdq_weights_t *w, int M, void *Y,
+                                  svdq_dtype_t y_dtype, svdq_epilogue_t epilogue,
+                                  const void *workspace, size_t ws_bytes, void *hip_stream);
+
+/* Canonical export of kernel (1): qact [M, K/2] packed E2M1 codes, ascales
+ * [M, K/32] E8M0 bytes, lowrank_down [M, rank] fp32.  Device pointers. */
+svdq_status_t svdq_mx_quantize_activations(const svdq_weights_t *w, const void *X, int M,
+                                           uint8_t *qact, uint8_t *ascales,
+                                           float *lowrank_down, void *workspace,
+                                           size_t ws_bytes, void *hip_stream);
+
 /* ------------------------------------------- test / inspection exports
  * Same device kernels as the forward, writing canonical layouts. */
 

@@ -231,6 +231,91 @@ def test_awq_blob_layout():
     assert not np.any(sz[N:]) and not np.any(sz[:, G:])
 
 
+# ----------------------------------------------------------- MXFP4 form
+from oracle import mxfp4 as MXO  # noqa: E402
+
+
+@pytest.mark.parametrize("smooth", [False, True])
+def test_mx_rank0_codes_and_scales_bit_exact(smooth):
+    c = synth.linear_case("mxr0", 90, 64, 96, 320, 0, x_outlier_n=3, x_outlier_scale=40.0,
+                          w_outlier_n=4, w_outlier_scale=8.0)
+    ax = c.calib_absmax() if smooth else None
+    hw = S.mx_prepare_weights(c.W, ax, c.bias, 0)
+    ref = MXO.prepare(c.W, ax, c.bias, 0)
+    assert np.array_equal(hw.inv_lambda, ref["iota"])
+    assert np.array_equal(hw.qweight, MXO.pack_fp4(ref["qW"]))
+    assert np.array_equal(hw.wscales.astype(np.int32) - 127, ref["eW"])
+    assert np.array_equal(hw.bias, ref["bias"].astype(np.float32))
+
+
+def test_mx_quantiser_edge_values_bit_exact():
+    """Rows built to hit every rounding boundary (ties on both sides, values
+    just off them), saturation above 6, all-zero and subnormal blocks, mixed
+    signs and negative zero: with rank 0 and no smoothing the residual is W
+    itself, so the host encoder must match the oracle's bit for bit."""
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, 7.5, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0])
+    rows = []
+    for k in (-20, -3, 0, 4):
+        b = np.concatenate([ties, -ties]) * 2.0 ** k
+        b[0] = 4.0 * 2.0 ** k                           # keeps the block exponent at k
+        rows.append(b)
+        rows.append(b * (1 + 2.0 ** -7))                # just above every boundary
+        rows.append(b * (1 - 2.0 ** -7))                # just below
+    rows.append(np.zeros(32))
+    rows.append(np.concatenate([[2.0 ** -130, -2.0 ** -131], np.zeros(30)]))
+    z = np.zeros(32)
+    z[3] = -0.0
+    z[5] = 3.0
+    rows.append(z)
+    W = np.stack([np.concatenate([r, r[::-1]]) for r in rows])   # K = 64
+    Wb = O.bf16_bits_of(O.round_to_bf16(W))
+    hw = S.mx_prepare_weights(Wb, None, None, 0)
+    ref = MXO.prepare(Wb, None, None, 0)
+    assert np.array_equal(hw.qweight, MXO.pack_fp4(ref["qW"]))
+    assert np.array_equal(hw.wscales.astype(np.int32) - 127, ref["eW"])
+
+
+def test_mx_residual_within_half_a_step():
+    c = synth.linear_case("mxres", 91, 64, 128, 256, 12, x_outlier_n=4, x_outlier_scale=40.0)
+    ax = c.calib_absmax()
+    hw = S.mx_prepare_weights(c.W, ax, c.bias, 12)
+    lam, _ = O.smoothing_factors(ax, O.bf16_values(c.W))
+    W_hat = O.smooth_weight(O.bf16_values(c.W), lam)
+    R = W_hat - _cpp_branch(hw, lam)
+    e = hw.wscales.astype(np.int32) - 127
+    deq = MXO.dequantize(MXO.unpack_fp4(hw.qweight), e)
+    scale = np.repeat(np.exp2(e.astype(np.float64)), 32, axis=1)
+    # the grid step is at most 2 x scale (between 4 and 6); saturation only
+    # clips values in (6, 8) x scale, and the block max is below 8 x scale
+    assert np.all(np.abs(R - deq) <= 2.0 * scale * (1 + 2.0 ** -20) + 2.0 ** -24 * np.abs(R))
+
+
+def test_mx_blob_layout():
+    """Codes and scales sit where the documented MXFP4 tiling says: for
+    K-step s and tile t, lane l = row % 32 + 32 h holds the row's canonical
+    bytes 32 s + 16 h + [0, 16) at ((s T + t) 64 + l) 16, and the E8M0 scale
+    of MX block 2 s + h at (s T + t) 64 + l of the scale array."""
+    c = synth.linear_case("mxpk", 92, 8, 100, 192, 5, x_outlier_n=2, x_outlier_scale=20.0)
+    hw = S.mx_prepare_weights(c.W, c.calib_absmax(), c.bias, 5)
+    blob = S.mx_pack_device_weights(hw)
+    N, K, G, Np = 100, 192, 3, 256
+    T = Np // 32
+    qbytes = Np * K // 2
+    q = blob[:qbytes]
+    s_off = (qbytes + 255) // 256 * 256
+    sc = blob[s_off: s_off + Np * (K // 32)]
+    for n in range(N):
+        for s_ in range(G):
+            for h in range(2):
+                lane = n % 32 + 32 * h
+                base = ((s_ * T + n // 32) * 64 + lane) * 16
+                assert np.array_equal(q[base: base + 16], hw.qweight[n, 32 * s_ + 16 * h: 32 * s_ + 16 * h + 16])
+                assert sc[(s_ * T + n // 32) * 64 + lane] == hw.wscales[n, 2 * s_ + h]
+    # padded rows: +0 codes and the smallest scale byte (0)
+    assert not np.any(q.reshape(G, T, 64, 16)[:, 3, 4:32]) and not np.any(q.reshape(G, T, 64, 16)[:, 4:])
+    assert not np.any(sc.reshape(G, T, 64)[:, 4:])
+
+
 # ---------------------------------------------------------------- errors
 INV, SHAPE, NODEV, WS, NUM = 1, 2, 3, 5, 6
 FAKE = 1 << 20          # aligned, never dereferenced: validation fails first

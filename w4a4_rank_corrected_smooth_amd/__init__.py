@@ -45,6 +45,9 @@ EXPORTS = [
     "svdq_quantize_activations",
     "svdq_debug_group_sums", "awq_quantize_weights", "awq_device_weights_bytes",
     "awq_pack_device_weights", "awq_w4a16_forward",
+    "svdq_mx_host_weights_sizes", "svdq_mx_prepare_weights", "svdq_mx_device_weights_bytes",
+    "svdq_mx_pack_device_weights", "svdq_mx_workspace_bytes", "svdq_mx_linear_forward",
+    "svdq_mx_linear_quantize", "svdq_mx_linear_gemm", "svdq_mx_quantize_activations",
 ]
 
 
@@ -52,6 +55,12 @@ class HostWeights(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int32), ("K", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("group_size", ctypes.c_int32), ("inv_lambda", _vp), ("l1s", _vp), ("l2", _vp),
                 ("qweight", _vp), ("wscales", _vp), ("bias", _vp)]
+
+
+class MxHostWeights(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("K", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("inv_lambda", _vp), ("l1s", _vp), ("l2", _vp), ("qweight", _vp),
+                ("wscales", _vp), ("bias", _vp)]
 
 
 class DeviceWeights(ctypes.Structure):
@@ -92,6 +101,15 @@ _sig("awq_quantize_weights", _i, [_vp, _i, _i, _i, _vp, _vp, _vp])
 _sig("awq_device_weights_bytes", _sz, [_i, _i])
 _sig("awq_pack_device_weights", _i, [_vp, _vp, _vp, _i, _i, _vp, _sz])
 _sig("awq_w4a16_forward", _i, [_vp, _i, _i, _vp, _i, _vp, _vp, _vp])
+_sig("svdq_mx_host_weights_sizes", _i, [_i, _i, _i, ctypes.POINTER(_sz)])
+_sig("svdq_mx_prepare_weights", _i, [_vp, _i, _i, _vp, _vp, _i, ctypes.POINTER(MxHostWeights)])
+_sig("svdq_mx_device_weights_bytes", _sz, [_i, _i, _i])
+_sig("svdq_mx_pack_device_weights", _i, [ctypes.POINTER(MxHostWeights), _vp, _sz])
+_sig("svdq_mx_workspace_bytes", _sz, [_i, _i, _i, _i])
+_sig("svdq_mx_linear_forward", _i, [_W, _vp, _i, _vp, _i, _i, _vp, _sz, _vp])
+_sig("svdq_mx_linear_quantize", _i, [_W, _vp, _i, _vp, _sz, _vp])
+_sig("svdq_mx_linear_gemm", _i, [_W, _i, _vp, _i, _i, _vp, _sz, _vp])
+_sig("svdq_mx_quantize_activations", _i, [_W, _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp])
 
 
 class SvdqError(RuntimeError):
@@ -334,6 +352,134 @@ def debug_group_sums(layer: Linear, M: int, m0: int, mcount: int, n0: int, ncoun
                                       P.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                       _stream(workspace.device)), "svdq_debug_group_sums")
     return P
+
+
+# ------------------------------------------------------------ MXFP4 variant
+@dataclass
+class PreparedHostMx:
+    """Output of svdq_mx_prepare_weights (host numpy arrays, canonical layouts)."""
+    N: int
+    K: int
+    rank: int
+    inv_lambda: np.ndarray   # float32 [K]
+    l1s: np.ndarray          # uint16 (bf16) [K, rank]
+    l2: np.ndarray           # uint16 (bf16) [rank, N]
+    qweight: np.ndarray      # uint8 [N, K/2] E2M1 codes
+    wscales: np.ndarray      # uint8 [N, K/32] E8M0
+    bias: np.ndarray         # float32 [N]
+
+    def __post_init__(self):
+        # the C side reads row-major buffers of exactly these types
+        self.inv_lambda = np.ascontiguousarray(self.inv_lambda, dtype=np.float32)
+        self.l1s = np.ascontiguousarray(self.l1s, dtype=np.uint16)
+        self.l2 = np.ascontiguousarray(self.l2, dtype=np.uint16)
+        self.qweight = np.ascontiguousarray(self.qweight, dtype=np.uint8)
+        self.wscales = np.ascontiguousarray(self.wscales, dtype=np.uint8)
+        self.bias = np.ascontiguousarray(self.bias, dtype=np.float32)
+
+    def as_struct(self) -> MxHostWeights:
+        return MxHostWeights(self.N, self.K, self.rank, _ptr(self.inv_lambda),
+                             _ptr(self.l1s) if self.rank else None,
+                             _ptr(self.l2) if self.rank else None, _ptr(self.qweight),
+                             _ptr(self.wscales), _ptr(self.bias))
+
+
+def mx_prepare_weights(W_bits: np.ndarray, act_absmax: Optional[np.ndarray],
+                       bias_bits: Optional[np.ndarray], rank: int) -> PreparedHostMx:
+    """Host preparation of the MXFP4 form (smoothing, SVD split, residual in MXFP4)."""
+    W_bits = np.ascontiguousarray(W_bits, dtype=np.uint16)
+    N, K = W_bits.shape
+    ax = None if act_absmax is None else np.ascontiguousarray(act_absmax, dtype=np.float32)
+    b = None if bias_bits is None else np.ascontiguousarray(bias_bits, dtype=np.uint16)
+    out = PreparedHostMx(N, K, rank, np.empty(K, np.float32), np.empty((K, rank), np.uint16),
+                         np.empty((rank, N), np.uint16), np.empty((N, max(K // 2, 1)), np.uint8),
+                         np.empty((N, max(K // 32, 1)), np.uint8), np.empty(N, np.float32))
+    hw = out.as_struct()
+    _check(_lib.svdq_mx_prepare_weights(_ptr(W_bits), N, K, _ptr(ax), _ptr(b), rank,
+                                        ctypes.byref(hw)), "svdq_mx_prepare_weights")
+    return out
+
+
+def mx_pack_device_weights(hw: PreparedHostMx) -> np.ndarray:
+    n = _lib.svdq_mx_device_weights_bytes(hw.N, hw.K, hw.rank)
+    if n == 0:
+        raise SvdqError(2, "svdq_mx_device_weights_bytes")
+    blob = np.empty(n, np.uint8)
+    s = hw.as_struct()
+    _check(_lib.svdq_mx_pack_device_weights(ctypes.byref(s), _ptr(blob), n),
+           "svdq_mx_pack_device_weights")
+    return blob
+
+
+class MxLinear:
+    """A prepared MXFP4 SVDQuant layer resident on one device."""
+
+    def __init__(self, hw: PreparedHostMx, device="cuda"):
+        self.N, self.K, self.rank = hw.N, hw.K, hw.rank
+        self.blob = torch.from_numpy(mx_pack_device_weights(hw)).to(device)
+        self.device = self.blob.device
+        self._w = DeviceWeights(self.blob.data_ptr(), self.N, self.K, self.rank)
+
+    def workspace_bytes(self, M: int) -> int:
+        n = _lib.svdq_mx_workspace_bytes(M, self.N, self.K, self.rank)
+        if n == 0:
+            raise SvdqError(2, "svdq_mx_workspace_bytes")
+        return n
+
+    def new_workspace(self, M: int) -> torch.Tensor:
+        return torch.empty(self.workspace_bytes(M), dtype=torch.uint8, device=self.device)
+
+
+def mx_linear_forward(layer: MxLinear, X: torch.Tensor, out: Optional[torch.Tensor] = None,
+                      out_dtype=torch.bfloat16, gelu: bool = False,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X W^T + b through the MXFP4 path (optionally gelu_tanh(Y))."""
+    assert X.dtype == torch.bfloat16 and X.is_contiguous() and X.shape[1] == layer.K
+    M = X.shape[0]
+    if out is None:
+        out = torch.empty((M, layer.N), dtype=out_dtype, device=X.device)
+    if workspace is None:
+        workspace = layer.new_workspace(M)
+    dt = FP32 if out.dtype == torch.float32 else BF16
+    _check(_lib.svdq_mx_linear_forward(ctypes.byref(layer._w), X.data_ptr(), M, out.data_ptr(), dt,
+                                       EPILOGUE_GELU_TANH if gelu else EPILOGUE_NONE,
+                                       workspace.data_ptr(), workspace.numel(), _stream(X.device)),
+           "svdq_mx_linear_forward")
+    return out
+
+
+def mx_linear_quantize(layer: MxLinear, X: torch.Tensor, workspace: torch.Tensor) -> None:
+    assert X.dtype == torch.bfloat16 and X.is_contiguous() and X.shape[1] == layer.K
+    _check(_lib.svdq_mx_linear_quantize(ctypes.byref(layer._w), X.data_ptr(), X.shape[0],
+                                        workspace.data_ptr(), workspace.numel(), _stream(X.device)),
+           "svdq_mx_linear_quantize")
+
+
+def mx_linear_gemm(layer: MxLinear, M: int, out: torch.Tensor, workspace: torch.Tensor,
+                   gelu: bool = False) -> torch.Tensor:
+    dt = FP32 if out.dtype == torch.float32 else BF16
+    _check(_lib.svdq_mx_linear_gemm(ctypes.byref(layer._w), M, out.data_ptr(), dt,
+                                    EPILOGUE_GELU_TANH if gelu else EPILOGUE_NONE,
+                                    workspace.data_ptr(), workspace.numel(), _stream(out.device)),
+           "svdq_mx_linear_gemm")
+    return out
+
+
+def mx_quantize_activations(layer: MxLinear, X: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+    """Canonical export of the MXFP4 quantiser: (codes uint8 [M, K/2], E8M0
+    scales uint8 [M, K/32], low-rank down float32 [M, rank])."""
+    M = X.shape[0]
+    dev = X.device
+    q = torch.empty((M, layer.K // 2), dtype=torch.uint8, device=dev)
+    e = torch.empty((M, layer.K // 32), dtype=torch.uint8, device=dev)
+    d = torch.empty((M, max(layer.rank, 1)), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = layer.new_workspace(M)
+    _check(_lib.svdq_mx_quantize_activations(ctypes.byref(layer._w), X.data_ptr(), M, q.data_ptr(),
+                                             e.data_ptr(), d.data_ptr(), workspace.data_ptr(),
+                                             workspace.numel(), _stream(dev)),
+           "svdq_mx_quantize_activations")
+    return q, e, d[:, :layer.rank]
 
 
 # ------------------------------------------------------------------- AWQ

@@ -124,6 +124,52 @@ svdq_status_t svdq_pack_device_weights(const svdq_host_weights_t *in, void *blob
   return pack_device_weights(in, blob, bytes);
 }
 
+svdq_status_t svdq_mx_host_weights_sizes(int N, int K, int rank, size_t sizes_out[6]) {
+  svdq_status_t st;
+  if (!sizes_out) return fail(SVDQ_ERR_INVALID_ARGUMENT, "sizes_out is NULL");
+  if (!shape_ok(N, K, rank, "svdq_mx_host_weights_sizes", &st)) return st;
+  sizes_out[0] = sizeof(float) * (size_t)K;
+  sizes_out[1] = 2 * (size_t)K * rank;
+  sizes_out[2] = 2 * (size_t)rank * N;
+  sizes_out[3] = (size_t)N * K / 2;
+  sizes_out[4] = (size_t)N * (K / kMxBlock);
+  sizes_out[5] = sizeof(float) * (size_t)N;
+  return SVDQ_OK;
+}
+
+svdq_status_t svdq_mx_prepare_weights(const uint16_t *W, int N, int K, const float *act_absmax,
+                                      const uint16_t *bias, int rank, svdq_mx_host_weights_t *out) {
+  svdq_status_t st;
+  if (!W || !out) return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_mx_prepare_weights: NULL pointer");
+  if (!shape_ok(N, K, rank, "svdq_mx_prepare_weights", &st)) return st;
+  if (!out->inv_lambda || !out->qweight || !out->wscales || !out->bias ||
+      (rank > 0 && (!out->l1s || !out->l2)))
+    return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_mx_prepare_weights: NULL output buffer");
+  return prepare_weights_mx(W, N, K, act_absmax, bias, rank, out);
+}
+
+size_t svdq_mx_device_weights_bytes(int N, int K, int rank) {
+  svdq_status_t st;
+  if (!shape_ok(N, K, rank, "svdq_mx_device_weights_bytes", &st)) return 0;
+  return (size_t)MxWeightLayout(N, K, rank).total;
+}
+
+svdq_status_t svdq_mx_pack_device_weights(const svdq_mx_host_weights_t *in, void *blob, size_t bytes) {
+  svdq_status_t st;
+  if (!in || !blob) return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_mx_pack_device_weights: NULL");
+  if (!shape_ok(in->N, in->K, in->rank, "svdq_mx_pack_device_weights", &st)) return st;
+  if (!in->inv_lambda || !in->qweight || !in->wscales || !in->bias ||
+      (in->rank > 0 && (!in->l1s || !in->l2)))
+    return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_mx_pack_device_weights: NULL input buffer");
+  return pack_device_weights_mx(in, blob, bytes);
+}
+
+size_t svdq_mx_workspace_bytes(int M, int N, int K, int rank) {
+  svdq_status_t st;
+  if (M < 1 || !shape_ok(N, K, rank, "svdq_mx_workspace_bytes", &st)) return 0;
+  return (size_t)MxWorkLayout(M, K, rank).total;
+}
+
 size_t svdq_workspace_bytes(int M, int N, int K, int rank) {
   svdq_status_t st;
   if (M < 1 || !shape_ok(N, K, rank, "svdq_workspace_bytes", &st)) return 0;

@@ -143,6 +143,54 @@ __device__ __forceinline__ float quantize_lane(const uint4 (&xr)[4], const float
   return sc;
 }
 
+// One lane's MXFP4 block (the FP4 form of the 4-bit path, OCP Microscaling
+// MXFP4): xm holds 32 consecutive bf16 activations (channels 32 h + [0, 32)
+// of a group), io their 1/lambda.  x_hat = fl32(x iota); a = max |x_hat|;
+// with E the biased exponent field of a, floor(log2 a) = E - 127 for a
+// normal a, so the block exponent e = floor(log2 a) - 2 is E - 129, clamped
+// at -127, which also covers a zero or subnormal a (E = 0).  Each
+// x_hat 2^-e (exact: a power of two, no overflow as |x_hat| < 2^(e+3)) is
+// rounded to the nearest FP4 E2M1 magnitude by counting the rounding
+// boundaries it passes (ties go to the even mantissa bit: 0.25 -> 0,
+// 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4; above 5 -> 6,
+// which saturates), with the sign in bit 3 unless the magnitude is 0.
+// Codes go out in canonical nibble order (code i at bits 4 (i % 8) of word
+// i / 8); returns the E8M0 byte e + 127.
+__device__ __forceinline__ uint32_t quantize_lane_mx(const uint4 (&xm)[4], const float4 (&io)[8],
+                                                     uint4 &codes) {
+  float v[32];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t wv[4] = {xm[j].x, xm[j].y, xm[j].z, xm[j].w};
+    const float4 i0 = io[2 * j], i1 = io[2 * j + 1];
+    const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v[8 * j + 2 * c] = bf16_lo(wv[c]) * iv[2 * c];
+      v[8 * j + 2 * c + 1] = bf16_hi(wv[c]) * iv[2 * c + 1];
+    }
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(v[i]));
+  const int E = (int)(__float_as_uint(a) >> 23);
+  const int e = E == 0 ? -127 : max(E - 129, -127);
+  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float r = v[i] * inv;
+    const float m = fabsf(r);
+    const uint32_t idx = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
+                         (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
+                         (uint32_t)(m > 5.0f);
+    const uint32_t code = idx | ((r < 0.0f && idx != 0u) ? 8u : 0u);
+    w[i / 8] |= code << (4 * (i % 8));
+  }
+  codes = make_uint4(w[0], w[1], w[2], w[3]);
+  return (uint32_t)(e + 127);
+}
+
 // ======================================================================= K1
 // One workgroup (4 wavefronts) per (tile of 32 token rows, K split).  The
 // split's groups are taken kK1Chunk = 4 at a time: the workgroup copies the
@@ -165,7 +213,7 @@ constexpr int kK1XBytes = kTile * kK1RowBytes;     // 16 KB of X per chunk
 constexpr int kK1BufBytes = kK1XBytes + kK1Chunk * kGroup * 4;   // + 1 KB of 1/lambda
 constexpr int kK1Bufs = 3;
 constexpr int kK1LdsBytes = kK1Bufs * kK1BufBytes;
-template <int TB>   // rank_pad / 32
+template <int TB, bool MX = false>   // rank_pad / 32; MXFP4 instead of INT4 codes
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3 : 1))) void k1_quantize_lowrank_down(
     const uint16_t *__restrict__ X, int M, int K, int Mp, int S,
     const float *__restrict__ iota, const uint16_t *__restrict__ l1t,
@@ -229,10 +277,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
 
   // Vector-memory operations of one wavefront in issue order: copy(0)
   // l1(0) ... copy(B-1) l1(B-1) (B = kK1Bufs), then per chunk c: stores(c)
-  // [4], copy(c+B) l1(c+B).  Before chunk c it waits until copy(c) and l1(c)
-  // are done, leaving in flight everything issued after them: the stores of
-  // the min(c, B-1) chunks before it and the fetches of chunks c+1 .. c+B-1
-  // that exist; then the workgroup meets.
+  // (kStores of them: INT4 three code pairs and a scale, MXFP4 one 16-byte
+  // code store and a scale byte), copy(c+B) l1(c+B).  Before chunk c it
+  // waits until copy(c) and l1(c) are done, leaving in flight everything
+  // issued after them: the stores of the min(c, B-1) chunks before it and
+  // the fetches of chunks c+1 .. c+B-1 that exist; then the workgroup meets.
 #pragma unroll
   for (int c = 0; c < kK1Bufs; ++c) {
     if (c < nch) { copy_chunk(c); load_l1(c, lring[c]); }
@@ -242,7 +291,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
   for (int u = 0; u < kK1Bufs; ++u) {
     const int c = c0 + u;
     if (c >= nch) break;
-    const int later = 4 * min(c, kK1Bufs - 1) + (ncopy + L1N) * (min(nch - 1, c + kK1Bufs - 1) - c);
+    constexpr int kStores = MX ? 2 : 4;
+    const int later = kStores * min(c, kK1Bufs - 1) + (ncopy + L1N) * (min(nch - 1, c + kK1Bufs - 1) - c);
     vmcnt_wait_dyn(later);
     __syncthreads();
     const uint8_t *buf = k1_lds + u * kK1BufBytes;
@@ -263,13 +313,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
       io[2 * j] = iota_c[4 * j + 2 * h];
       io[2 * j + 1] = iota_c[4 * j + 2 * h + 1];
     }
-    v6u packed;
-    const float sc = quantize_lane(xr, io, packed);
-    uint8_t *qp = qa + pair_offset(g, t, T, lane, 0);
+    if constexpr (MX) {
+      // the lane's MX block: channels 32 h + [0, 32) of its group
+      uint4 xm[4];
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
-      *reinterpret_cast<uint2 *>(qp + 512 * j) = make_uint2(packed[2 * j], packed[2 * j + 1]);
-    sa[(int64_t)g * Mp + row] = sc;              // both halves hold the same scale
+      for (int j = 0; j < 4; ++j) {
+        const int piece = wu * 8 + 4 * h + j;
+        xm[j] = *reinterpret_cast<const uint4 *>(xb + ((piece ^ (rr & 15)) << 4));
+      }
+      float4 iom[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) iom[q] = iota_c[8 * h + q];
+      uint4 codes;
+      const uint32_t e8 = quantize_lane_mx(xm, iom, codes);
+      *reinterpret_cast<uint4 *>(qa + mx_code_offset(g, t, T, lane)) = codes;
+      reinterpret_cast<uint8_t *>(sa)[mx_scale_offset(g, t, T, lane)] = (uint8_t)e8;
+    } else {
+      v6u packed;
+      const float sc = quantize_lane(xr, io, packed);
+      uint8_t *qp = qa + pair_offset(g, t, T, lane, 0);
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        *reinterpret_cast<uint2 *>(qp + 512 * j) = make_uint2(packed[2 * j], packed[2 * j + 1]);
+      sa[(int64_t)g * Mp + row] = sc;            // both halves hold the same scale
+    }
     if (TB > 0 && live) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -333,7 +400,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
 // runs on XCD b % 8; each XCD is given a contiguous range of tiles, walked
 // GM tile-rows at a time, so the A and B panels its CUs share stay in its
 // L2.
-enum { MODE_FWD = 0, MODE_SUMS = 1 };
+enum { MODE_FWD = 0, MODE_SUMS = 1, MODE_MX = 2 };
 
 struct K2Args {
   const uint8_t *qa; const float *sa; const float *dpart; int S, M, Mp;
@@ -349,6 +416,8 @@ struct K2Args {
   // 1/lambda [N], L1s in fragment order, codes, scales and fixed-point D
   const float *iota2; const uint16_t *l1f2; uint8_t *qa2; float *sa2; int64_t *d2;
   int G2, rp2;
+  // MXFP4 (MODE_MX): qa / qw hold E2M1 codes, these the E8M0 block scales
+  const uint8_t *sqa; const uint8_t *sqw;
 };
 
 namespace k2c {
@@ -386,6 +455,15 @@ __device__ __forceinline__ v8i k2_frag(const uint8_t *blk, int lane) {
   v8i r = __builtin_nondeterministic_value(r);
   r[0] = (int)w0.x; r[1] = (int)w0.y; r[2] = (int)w1.x;
   r[3] = (int)w1.y; r[4] = (int)w2.x; r[5] = (int)w2.y;
+  return r;
+}
+
+// The FP4 operand occupies four registers (16 bytes: the lane's 32 codes);
+// the rest of the 8-register slot is left undefined.
+__device__ __forceinline__ v8i mx_frag(const uint8_t *blk, int lane) {
+  const uint4 w = *reinterpret_cast<const uint4 *>(blk + lane * 16);
+  v8i r = __builtin_nondeterministic_value(r);
+  r[0] = (int)w.x; r[1] = (int)w.y; r[2] = (int)w.z; r[3] = (int)w.w;
   return r;
 }
 
@@ -488,6 +566,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
+  // MXFP4 stage of K-step g: A codes (4 tile blocks of 1 KB), B codes (8),
+  // and one copy of the step's E8M0 scales (lanes 0-15: A's 256 bytes,
+  // 16-47: B's 512, 48-63 repeat A's); 13 wavefront-loads, wavefront w
+  // issuing loads w, w + 4, w + 8 (and 12 for w = 0).  LDS: [A 4 KB][B 8 KB]
+  // [A scales 256 B][B scales 512 B].
+  auto fetch_mx = [&](int g) {
+    const uint32_t buf = smem_lds + (uint32_t)((g % NBUF) * STAGE);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int L = wu + NWAVES * r;
+      if (L >= 13) break;
+      if (L < 4) {
+        lds_dma16_s(p.qa + ((int64_t)g * Ta + bm / kTile + L) * 1024, voff, buf + (uint32_t)(L * 1024));
+      } else if (L < 12) {
+        lds_dma16_s(p.qw + ((int64_t)g * Tw + bn / kTile + (L - 4)) * 1024, voff, buf + (uint32_t)(L * 1024));
+      } else {
+        const uint8_t *src = lane < 16 ? p.sqa + ((int64_t)g * Ta + bm / kTile) * 64 + lane * 16
+                           : lane < 48 ? p.sqw + ((int64_t)g * Tw + bn / kTile) * 64 + (lane - 16) * 16
+                                       : p.sqa + ((int64_t)g * Ta + bm / kTile) * 64 + (lane - 48) * 16;
+        lds_dma16(src, buf + (uint32_t)(12 * 1024));
+      }
+    }
+  };
+
   // Operands of one group as a wavefront holds them in registers: the fp6
   // codes of its row tiles and column tiles, the activation scales of the
   // 16 rows each lane's accumulator elements belong to (per row tile: rows
@@ -577,8 +679,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // stale but in-bounds LDS buffer, and their results are never used:
   // branch-free code keeps the operands and products in fixed registers.
   v16f Pa, Pb;
-  for (int g = 0; g < 3 && g < G; ++g) fetch(g);
-  if constexpr (MODE == MODE_FWD) {
+  for (int g = 0; g < 3 && g < G; ++g) {
+    if constexpr (MODE == MODE_MX) fetch_mx(g); else fetch(g);
+  }
+  if constexpr (MODE == MODE_FWD || MODE == MODE_MX) {
     // Low-rank up-projection first, while the first stages are in flight:
     // acc = D L2 on bf16 matrix cores, D entered as a bf16 high part plus a
     // bf16 remainder.  D of the workgroup's 128 rows is assembled once, in
@@ -665,6 +769,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       __syncthreads();                   // staging free for the next 32 ranks
     }
   }
+  if constexpr (MODE == MODE_MX) {
+    // Block-scaled FP4 main loop.  Per K-step each wavefront issues its 8
+    // matrix instructions (2 x 4 tiles of 32 x 32), each taking the step's
+    // codes and the lanes' E8M0 block scales and accumulating into its tile:
+    // the instruction applies both scales, so no vector work is left per
+    // element.  Operands of step g + 1 are read from LDS behind the step's
+    // matrix instructions; waits and barriers as in the INT4 loop below,
+    // with this wavefront's own copy count per stage (4 for wavefront 0, 3
+    // for the others).
+    auto mx_wait = [&](bool all) {
+      if (all) vmcnt_wait0();
+      else if (wu == 0) vmcnt_wait<4>();
+      else vmcnt_wait<3>();
+    };
+    v8i xa[WTM], xb[WTN];
+    int xsa[WTM], xsb[WTN];
+    auto mx_load = [&](int g) {
+      const uint8_t *st = stage_of(g);
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) {
+        xa[i] = mx_frag(st + (WTM * wmi + i) * 1024, lane);
+        xsa[i] = st[12288 + (WTM * wmi + i) * 64 + lane];
+      }
+#pragma unroll
+      for (int j = 0; j < WTN; ++j) {
+        xb[j] = mx_frag(st + 4096 + (WTN * wni + j) * 1024, lane);
+        xsb[j] = st[12288 + 256 + (WTN * wni + j) * 64 + lane];
+      }
+    };
+    mx_wait(G <= 2);
+    __syncthreads();
+    mx_load(0);
+    for (int g = 0; g < G; ++g) {
+      if (g + 1 < G) {
+        mx_wait(g + 2 >= G);
+        __syncthreads();
+        if (g + 3 < G) fetch_mx(g + 3);
+      }
+#pragma unroll
+      for (int i = 0; i < WTM; ++i)
+#pragma unroll
+        for (int j = 0; j < WTN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa[i], xb[j], acc[i][j], 4, 4, 0,
+                                                                      xsa[i], 0, xsb[j]);
+      mx_load(g + 1);
+    }
+  } else {
   if (G > 2) vmcnt_wait<MAX_LOADS>(); else vmcnt_wait0();
   __syncthreads();
   load_a(0, 0); load_a(0, 1);
@@ -719,6 +870,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     load_sw(g + 1, 3);
     k2_order_r<0, 1>();
   }
+  }  // INT4 main loop
 
   if constexpr (MODE == MODE_FWD && QNEXT) {
     // MLP pair: this layer's output never goes to memory.  Bias (+ GELU),
@@ -843,7 +995,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       finish(b, dacc);
     }
-  } else if constexpr (MODE == MODE_FWD) {
+  } else if constexpr (MODE == MODE_FWD || MODE == MODE_MX) {
     // Bias (+ GELU), then the wavefront's tile goes out through its own LDS
     // one 32-row half at a time, so global stores are whole 16-byte vectors
     // along a row instead of 2- or 4-byte scattered stores.
@@ -1219,6 +1371,27 @@ __global__ void canon_scales_kernel(const float *__restrict__ sa, int M, int Mp,
   out[idx] = sa[g * Mp + m];
 }
 
+// MXFP4 codes and scales of the workspace -> canonical [M, K/2] bytes and
+// [M, K/32] E8M0 bytes.  Byte j of row m sits in lane (m % 32) + 32 h of
+// block (j / 32, m / 32), h = (j % 32) / 16, at byte j % 16.
+__global__ void canon_mx_codes_kernel(const uint8_t *__restrict__ qa, int M, int K, int T,
+                                      uint8_t *__restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)M * (K / 2)) return;
+  const int64_t m = idx / (K / 2), j = idx % (K / 2);
+  const int lane = (int)(m % 32) + 32 * (int)((j % 32) / 16);
+  out[idx] = qa[mx_code_offset(j / 32, m / 32, T, lane) + j % 16];
+}
+
+__global__ void canon_mx_scales_kernel(const uint8_t *__restrict__ sa, int M, int K, int T,
+                                       uint8_t *__restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int B = K / kMxBlock;
+  if (idx >= (int64_t)M * B) return;
+  const int64_t m = idx / B, b = idx % B;
+  out[idx] = sa[mx_scale_offset(b / 2, m / 32, T, (int)(m % 32) + 32 * (int)(b % 2))];
+}
+
 __global__ void canon_down_kernel(const float *__restrict__ dpart, int M, int Mp, int S, int rp,
                                   int rank, float *__restrict__ out) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1279,7 +1452,8 @@ svdq_status_t validate_weights(const svdq_weights_t *w, const char *who) {
   return SVDQ_OK;
 }
 
-svdq_status_t launch_k1(const WeightLayout &L, const WorkLayout &Wl, const svdq_weights_t *w,
+template <bool MX = false, class WL, class KL>
+svdq_status_t launch_k1(const WL &L, const KL &Wl, const svdq_weights_t *w,
                         const void *X, int M, uint8_t *ws, hipStream_t st,
                         int64_t *dzero = nullptr, int rpz = 0) {
   const uint8_t *blob = static_cast<const uint8_t *>(w->blob);
@@ -1295,7 +1469,7 @@ svdq_status_t launch_k1(const WeightLayout &L, const WorkLayout &Wl, const svdq_
   switch (L.rp / 32) {
 #define K1_CASE(TB)                                                                       \
   case TB:                                                                                \
-    hipLaunchKernelGGL(k1_quantize_lowrank_down<TB>, grid, dim3(256), lds, st, x, M, K, Mp, \
+    hipLaunchKernelGGL((k1_quantize_lowrank_down<TB, MX>), grid, dim3(256), lds, st, x, M, K, Mp, \
                        S, iota, l1t, qa, sa, dp, dzero, rpz);                             \
     break;
     K1_CASE(0) K1_CASE(1) K1_CASE(2) K1_CASE(3) K1_CASE(4) K1_CASE(5) K1_CASE(6) K1_CASE(7)
@@ -1587,6 +1761,118 @@ svdq_status_t svdq_debug_group_sums(const svdq_weights_t *w, int M, int m0, int 
   hipLaunchKernelGGL((k2_w4a4_gemm<MODE_SUMS, SVDQ_EPILOGUE_NONE, true>), grid, dim3(k2c::THREADS), 0,
                      static_cast<hipStream_t>(hip_stream), a);
   return launch_status("group-sum kernel launch");
+}
+
+// ------------------------------------------------------------- MXFP4
+static svdq_status_t validate_forward_mx(const svdq_weights_t *w, int M, size_t ws_bytes,
+                                         const void *workspace, const char *who) {
+  svdq_status_t st = validate_weights(w, who);
+  if (st != SVDQ_OK) return st;
+  if (!workspace) return fail(SVDQ_ERR_INVALID_ARGUMENT, "%s: NULL workspace", who);
+  if (!aligned16(workspace)) return fail(SVDQ_ERR_INVALID_ARGUMENT, "%s: misaligned workspace", who);
+  if (M < 1 || (int64_t)M * w->K > ((int64_t)1 << 31))
+    return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "%s: M=%d", who, M);
+  const MxWorkLayout Wl(M, w->K, w->rank);
+  if ((int64_t)ws_bytes < Wl.total)
+    return fail(SVDQ_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %lld bytes, got %zu", who,
+                (long long)Wl.total, ws_bytes);
+  return SVDQ_OK;
+}
+
+static svdq_status_t launch_k2_mx(const svdq_weights_t *w, int M, void *Y, svdq_dtype_t y_dtype,
+                                  svdq_epilogue_t epilogue, const void *workspace, hipStream_t stream) {
+  const MxWeightLayout L(w->N, w->K, w->rank);
+  const MxWorkLayout Wl(M, w->K, w->rank);
+  const uint8_t *blob = static_cast<const uint8_t *>(w->blob);
+  const uint8_t *ws = static_cast<const uint8_t *>(workspace);
+  K2Args a{};
+  a.qa = ws + Wl.qa;
+  a.sqa = ws + Wl.sa;
+  a.dpart = reinterpret_cast<const float *>(ws + Wl.d);
+  a.S = (int)Wl.S;
+  a.M = M;
+  a.Mp = (int)Wl.Mp;
+  a.qw = blob + L.q;
+  a.sqw = blob + L.s;
+  a.l2t = reinterpret_cast<const uint16_t *>(blob + L.l2t);
+  a.bias = reinterpret_cast<const float *>(blob + L.bias);
+  a.N = w->N;
+  a.Np = (int)L.Np;
+  a.K = w->K;
+  a.rp = (int)L.rp;
+  a.Y = Y;
+  a.TM = (M + k2c::BM - 1) / k2c::BM;
+  a.TN = (w->N + k2c::BN - 1) / k2c::BN;
+  const dim3 grid((unsigned)round_up((int64_t)a.TM * a.TN, 8));
+  const dim3 block(k2c::THREADS);
+  const bool f32 = y_dtype == SVDQ_FP32;
+  const bool gelu = epilogue == SVDQ_EPILOGUE_GELU_TANH;
+  constexpr int NONE = SVDQ_EPILOGUE_NONE, GELU = SVDQ_EPILOGUE_GELU_TANH;
+  if (!gelu && f32) hipLaunchKernelGGL((k2_w4a4_gemm<MODE_MX, NONE, true>), grid, block, 0, stream, a);
+  else if (!gelu) hipLaunchKernelGGL((k2_w4a4_gemm<MODE_MX, NONE, false>), grid, block, 0, stream, a);
+  else if (f32) hipLaunchKernelGGL((k2_w4a4_gemm<MODE_MX, GELU, true>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((k2_w4a4_gemm<MODE_MX, GELU, false>), grid, block, 0, stream, a);
+  return launch_status("FP4 GEMM kernel launch");
+}
+
+svdq_status_t svdq_mx_linear_quantize(const svdq_weights_t *w, const void *X, int M, void *workspace,
+                                      size_t ws_bytes, void *hip_stream) {
+  svdq_status_t st = validate_forward_mx(w, M, ws_bytes, workspace, "svdq_mx_linear_quantize");
+  if (st != SVDQ_OK) return st;
+  if (!X) return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_mx_linear_quantize: NULL X");
+  if (!aligned16(X)) return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_mx_linear_quantize: misaligned X");
+  if ((st = check_device()) != SVDQ_OK) return st;
+  return launch_k1<true>(MxWeightLayout(w->N, w->K, w->rank), MxWorkLayout(M, w->K, w->rank), w, X, M,
+                         static_cast<uint8_t *>(workspace), static_cast<hipStream_t>(hip_stream));
+}
+
+svdq_status_t svdq_mx_linear_gemm(const svdq_weights_t *w, int M, void *Y, svdq_dtype_t y_dtype,
+                                  svdq_epilogue_t epilogue, const void *workspace, size_t ws_bytes,
+                                  void *hip_stream) {
+  svdq_status_t st = validate_forward_mx(w, M, ws_bytes, workspace, "svdq_mx_linear_gemm");
+  if (st != SVDQ_OK) return st;
+  if ((st = validate_output(Y, y_dtype, epilogue, "svdq_mx_linear_gemm")) != SVDQ_OK) return st;
+  if ((st = check_device()) != SVDQ_OK) return st;
+  return launch_k2_mx(w, M, Y, y_dtype, epilogue, workspace, static_cast<hipStream_t>(hip_stream));
+}
+
+svdq_status_t svdq_mx_linear_forward(const svdq_weights_t *w, const void *X, int M, void *Y,
+                                     svdq_dtype_t y_dtype, svdq_epilogue_t epilogue, void *workspace,
+                                     size_t ws_bytes, void *hip_stream) {
+  svdq_status_t st = validate_output(Y, y_dtype, epilogue, "svdq_mx_linear_forward");
+  if (st != SVDQ_OK) return st;
+  if ((st = svdq_mx_linear_quantize(w, X, M, workspace, ws_bytes, hip_stream)) != SVDQ_OK) return st;
+  return launch_k2_mx(w, M, Y, y_dtype, epilogue, workspace, static_cast<hipStream_t>(hip_stream));
+}
+
+svdq_status_t svdq_mx_quantize_activations(const svdq_weights_t *w, const void *X, int M,
+                                           uint8_t *qact, uint8_t *ascales, float *lowrank_down,
+                                           void *workspace, size_t ws_bytes, void *hip_stream) {
+  svdq_status_t st = validate_forward_mx(w, M, ws_bytes, workspace, "svdq_mx_quantize_activations");
+  if (st != SVDQ_OK) return st;
+  if (!X || !qact || !ascales || (w->rank > 0 && !lowrank_down))
+    return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_mx_quantize_activations: NULL pointer");
+  if (!aligned16(X)) return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_mx_quantize_activations: misaligned X");
+  if ((st = check_device()) != SVDQ_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const MxWorkLayout Wl(M, w->K, w->rank);
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  if ((st = launch_k1<true>(MxWeightLayout(w->N, w->K, w->rank), Wl, w, X, M, ws, stream)) != SVDQ_OK)
+    return st;
+  const int T = (int)(Wl.Mp / kTile);
+  const int64_t nb = (int64_t)M * (w->K / 2);
+  hipLaunchKernelGGL(canon_mx_codes_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream,
+                     ws + Wl.qa, M, w->K, T, qact);
+  const int64_t ns = (int64_t)M * (w->K / kMxBlock);
+  hipLaunchKernelGGL(canon_mx_scales_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, stream,
+                     ws + Wl.sa, M, w->K, T, ascales);
+  if (w->rank > 0) {
+    const int64_t nd = (int64_t)M * w->rank;
+    hipLaunchKernelGGL(canon_down_kernel, dim3((unsigned)((nd + 255) / 256)), dim3(256), 0, stream,
+                       reinterpret_cast<const float *>(ws + Wl.d), M, (int)Wl.Mp, (int)Wl.S,
+                       (int)Wl.rp, w->rank, lowrank_down);
+  }
+  return launch_status("inspection kernels");
 }
 
 svdq_status_t awq_w4a16_forward(const void *blob, int N, int K, const void *x, int M,

@@ -72,11 +72,43 @@ void quantize_group64(const float *v, int8_t *q, float *s) {
   }
 }
 
+// ------------------------------------------------------ MXFP4 quantiser
+// One block of 32 float32 values in OCP MXFP4 (the FP4 form of the 4-bit
+// path): the shared scale is 2^e with e = floor(log2(max |v|)) - 2 (2 is the
+// largest exponent of FP4 E2M1), clamped to [-127, 127], -127 for an
+// all-zero block, stored biased by 127 (E8M0); each value v / 2^e is
+// rounded to the nearest E2M1 value (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6;
+// ties to an even mantissa bit; saturating at 6); zero is +0.
+uint8_t e2m1_code(float r) {
+  const float m = std::fabs(r);
+  const int idx = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) +
+                  (m >= 3.5f) + (m > 5.0f);
+  return (uint8_t)((r < 0.0f && idx > 0 ? 8 : 0) | idx);
+}
+
+void quantize_block32_mx(const float *v, uint8_t *codes, uint8_t *e8m0) {
+  float a = 0.0f;
+  for (int i = 0; i < kMxBlock; ++i) a = std::max(a, std::fabs(v[i]));
+  int e = -127;
+  if (a > 0.0f) {
+    int f;
+    std::frexp(a, &f);                       // a = m 2^f, 0.5 <= m < 1
+    e = std::min(127, std::max(-127, f - 1 - 2));
+  }
+  *e8m0 = (uint8_t)(e + 127);
+  for (int i = 0; i < kMxBlock; ++i)
+    codes[i] = e2m1_code((float)std::ldexp((double)v[i], -e));   // exact: a power-of-two scaling
+}
+
 // ---------------------------------------------------------------- prepare
-svdq_status_t prepare_weights(const uint16_t *W_bf16, int N, int K, const float *act_absmax,
-                              const uint16_t *bias_bf16, int rank, svdq_host_weights_t *out) {
+// The offline steps shared by both 4-bit encodings: smoothing factors, the
+// low-rank split of the smoothed weight and the residual against the
+// rounded factors, whose rows (float32) go to `emit(n, row)`.
+template <class Emit>
+static svdq_status_t prepare_common(const uint16_t *W_bf16, int N, int K, const float *act_absmax,
+                                    const uint16_t *bias_bf16, int rank, float *inv_lambda,
+                                    uint16_t *l1s, uint16_t *l2, float *bias, Emit emit) {
   const int64_t NK = (int64_t)N * K;
-  const int G = K / kGroup;
   std::vector<float> W((size_t)NK);
   bool finite = true;
   for (int64_t i = 0; i < NK; ++i) {
@@ -106,7 +138,7 @@ svdq_status_t prepare_weights(const uint16_t *W_bf16, int N, int K, const float 
       iota[k] = 1.0f / lam[k];
     }
   }
-  std::memcpy(out->inv_lambda, iota.data(), sizeof(float) * K);
+  std::memcpy(inv_lambda, iota.data(), sizeof(float) * K);
 
   // 2. smoothed weight (float64, exact) and its top-r SVD
   std::vector<double> What((size_t)NK);
@@ -124,23 +156,22 @@ svdq_status_t prepare_weights(const uint16_t *W_bf16, int N, int K, const float 
       for (int k = 0; k < K; ++k) {
         const double l1 = V[(int64_t)k * rank + t] * root;
         const uint16_t b = f64_to_bf16((double)iota[k] * l1);
-        out->l1s[(int64_t)k * rank + t] = b;
+        l1s[(int64_t)k * rank + t] = b;
         L1s[(int64_t)k * rank + t] = (double)bf16_to_f32(b);
       }
       for (int n = 0; n < N; ++n) {
         const uint16_t b = f64_to_bf16(root * U[(int64_t)n * rank + t]);
-        out->l2[(int64_t)t * N + n] = b;
+        l2[(int64_t)t * N + n] = b;
         L2[(int64_t)t * N + n] = (double)bf16_to_f32(b);
       }
     }
   }
 
-  // 3. residual against the rounded factors, float64 -> float32, quantised
-  //    per row and group of 64
+  // 3. residual against the rounded factors, float64 -> float32, one row at
+  //    a time to the 4-bit encoder
   parallel_for(N, 16, [&](int64_t n0, int64_t n1) {
     std::vector<float> row(K);
     std::vector<double> l2n(std::max(rank, 1));
-    std::vector<int8_t> q(kGroup);
     for (int64_t n = n0; n < n1; ++n) {
       for (int t = 0; t < rank; ++t) l2n[t] = L2[(int64_t)t * N + n];
       for (int k = 0; k < K; ++k) {
@@ -150,21 +181,54 @@ svdq_status_t prepare_weights(const uint16_t *W_bf16, int N, int K, const float 
         const double branch = s * (double)lam[k];
         row[k] = (float)(What[n * K + k] - branch);
       }
-      for (int g = 0; g < G; ++g) {
-        float sc;
-        quantize_group64(&row[g * kGroup], q.data(), &sc);
-        out->wscales[n * G + g] = sc;
-        uint8_t *dst = out->qweight + n * (K / 2) + g * (kGroup / 2);
-        for (int j = 0; j < kGroup / 2; ++j)
-          dst[j] = (uint8_t)(((uint8_t)q[2 * j] & 0x0F) | (((uint8_t)q[2 * j + 1] & 0x0F) << 4));
-      }
+      emit(n, row.data());
     }
   });
-  for (int n = 0; n < N; ++n) out->bias[n] = bias_bf16 ? bf16_to_f32(bias_bf16[n]) : 0.0f;
+  for (int n = 0; n < N; ++n) bias[n] = bias_bf16 ? bf16_to_f32(bias_bf16[n]) : 0.0f;
+  return SVDQ_OK;
+}
+
+svdq_status_t prepare_weights(const uint16_t *W_bf16, int N, int K, const float *act_absmax,
+                              const uint16_t *bias_bf16, int rank, svdq_host_weights_t *out) {
+  const int G = K / kGroup;
+  svdq_status_t st = prepare_common(
+      W_bf16, N, K, act_absmax, bias_bf16, rank, out->inv_lambda, out->l1s, out->l2, out->bias,
+      [&](int64_t n, const float *row) {
+        int8_t q[kGroup];
+        for (int g = 0; g < G; ++g) {
+          float sc;
+          quantize_group64(&row[g * kGroup], q, &sc);
+          out->wscales[n * G + g] = sc;
+          uint8_t *dst = out->qweight + n * (K / 2) + g * (kGroup / 2);
+          for (int j = 0; j < kGroup / 2; ++j)
+            dst[j] = (uint8_t)(((uint8_t)q[2 * j] & 0x0F) | (((uint8_t)q[2 * j + 1] & 0x0F) << 4));
+        }
+      });
+  if (st != SVDQ_OK) return st;
   out->N = N;
   out->K = K;
   out->rank = rank;
   out->group_size = kGroup;
+  return SVDQ_OK;
+}
+
+svdq_status_t prepare_weights_mx(const uint16_t *W_bf16, int N, int K, const float *act_absmax,
+                                 const uint16_t *bias_bf16, int rank, svdq_mx_host_weights_t *out) {
+  const int B = K / kMxBlock;
+  svdq_status_t st = prepare_common(
+      W_bf16, N, K, act_absmax, bias_bf16, rank, out->inv_lambda, out->l1s, out->l2, out->bias,
+      [&](int64_t n, const float *row) {
+        uint8_t q[kMxBlock];
+        for (int b = 0; b < B; ++b) {
+          quantize_block32_mx(&row[b * kMxBlock], q, &out->wscales[n * B + b]);
+          uint8_t *dst = out->qweight + n * (K / 2) + b * (kMxBlock / 2);
+          for (int j = 0; j < kMxBlock / 2; ++j) dst[j] = (uint8_t)(q[2 * j] | (q[2 * j + 1] << 4));
+        }
+      });
+  if (st != SVDQ_OK) return st;
+  out->N = N;
+  out->K = K;
+  out->rank = rank;
   return SVDQ_OK;
 }
 
@@ -205,6 +269,39 @@ svdq_status_t pack_device_weights(const svdq_host_weights_t *in, void *host_blob
   float *s = reinterpret_cast<float *>(b + L.s);
   for (int64_t n = 0; n < N; ++n)
     for (int64_t g = 0; g < L.G; ++g) s[g * L.Np + n] = in->wscales[n * L.G + g];
+  uint16_t *l2t = reinterpret_cast<uint16_t *>(b + L.l2t);
+  uint16_t *l1t = reinterpret_cast<uint16_t *>(b + L.l1t);
+  for (int64_t t = 0; t < r; ++t) {
+    for (int64_t n = 0; n < N; ++n) l2t[n * L.rp + t] = in->l2[t * N + n];
+    for (int64_t k = 0; k < K; ++k) l1t[l1_frag_index(k, t, L.rp)] = in->l1s[k * r + t];
+  }
+  std::memcpy(b + L.iota, in->inv_lambda, sizeof(float) * K);
+  std::memcpy(b + L.bias, in->bias, sizeof(float) * N);
+  return SVDQ_OK;
+}
+
+// --------------------------------------------------------- MXFP4 pack
+svdq_status_t pack_device_weights_mx(const svdq_mx_host_weights_t *in, void *host_blob, size_t bytes) {
+  const MxWeightLayout L(in->N, in->K, in->rank);
+  if ((int64_t)bytes < L.total)
+    return fail(SVDQ_ERR_WORKSPACE_TOO_SMALL, "blob needs %lld bytes, got %zu",
+                (long long)L.total, bytes);
+  uint8_t *b = static_cast<uint8_t *>(host_blob);
+  std::memset(b, 0, (size_t)L.total);
+  const int64_t N = in->N, K = in->K, r = in->rank, T = L.Np / kTile, G = L.G;
+  // lane l of block (s, t): row 32 t + l % 32, the row's canonical bytes
+  // 32 s + 16 (l / 32) + [0, 16) and the scale of MX block 2 s + l / 32;
+  // padding rows stay zero (codes +0, scales 2^-127)
+  uint8_t *q = b + L.q, *sc = b + L.s;
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t g = 0; g < G; ++g)
+      for (int lane = 0; lane < 64; ++lane) {
+        const int64_t n = t * kTile + (lane & 31);
+        if (n >= N) continue;
+        const int h = lane >> 5;
+        std::memcpy(q + mx_code_offset(g, t, T, lane), in->qweight + n * (K / 2) + 32 * g + 16 * h, 16);
+        sc[mx_scale_offset(g, t, T, lane)] = in->wscales[n * (K / kMxBlock) + 2 * g + h];
+      }
   uint16_t *l2t = reinterpret_cast<uint16_t *>(b + L.l2t);
   uint16_t *l1t = reinterpret_cast<uint16_t *>(b + L.l1t);
   for (int64_t t = 0; t < r; ++t) {

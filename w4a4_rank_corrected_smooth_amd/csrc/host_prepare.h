@@ -16,6 +16,15 @@ svdq_status_t prepare_weights(const uint16_t *W_bf16, int N, int K, const float 
 
 svdq_status_t pack_device_weights(const svdq_host_weights_t *in, void *host_blob, size_t bytes);
 
+// MXFP4: one FP4 E2M1 code (see the definition in svdq_mx_prepare_weights),
+// one block of 32 values (codes and the E8M0 scale byte), preparation and
+// device packing.
+uint8_t e2m1_code(float r);
+void quantize_block32_mx(const float *v, uint8_t *codes, uint8_t *e8m0);
+svdq_status_t prepare_weights_mx(const uint16_t *W_bf16, int N, int K, const float *act_absmax,
+                                 const uint16_t *bias_bf16, int rank, svdq_mx_host_weights_t *out);
+svdq_status_t pack_device_weights_mx(const svdq_mx_host_weights_t *in, void *host_blob, size_t bytes);
+
 svdq_status_t awq_quantize(const uint16_t *W_fp16, int N, int K, uint8_t *q, uint16_t *s,
                            uint16_t *z);
 

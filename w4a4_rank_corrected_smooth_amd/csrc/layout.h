@@ -125,6 +125,53 @@ struct WorkLayout {
   }
 };
 
+// MXFP4 device layouts (the FP4 form of the 4-bit path).  A K-step of 64
+// input channels is one block-scaled FP4 matrix instruction: for every
+// (K-step s, tile t of 32 rows) a 1 KB code block holds 16 bytes per lane;
+// lane l covers row l % 32 and the MX block h = l / 32 of the step, its 32
+// codes being channels 64 s + 32 h + [0, 32) in the canonical nibble order
+// (byte i = code 2i | code 2i+1 << 4), i.e. the row's canonical bytes
+// 32 s + 16 h + [0, 16).  The E8M0 scales of the same (s, t) follow as 64
+// bytes, one per lane, in a separate array.
+constexpr int kMxBlock = 32;
+constexpr int64_t mx_code_offset(int64_t s, int64_t t, int64_t T, int lane) {
+  return ((s * T + t) * 64 + lane) * 16;
+}
+constexpr int64_t mx_scale_offset(int64_t s, int64_t t, int64_t T, int lane) {
+  return (s * T + t) * 64 + lane;
+}
+
+struct MxWeightLayout {
+  int64_t N = 0, K = 0, rank = 0, Np = 0, rp = 0, G = 0;
+  int64_t q = 0, s = 0, l2t = 0, l1t = 0, iota = 0, bias = 0, total = 0;
+  constexpr MxWeightLayout(int64_t N_, int64_t K_, int64_t rank_)
+      : N(N_), K(K_), rank(rank_), Np(round_up(N_, kPad)), rp(rank_pad((int)rank_)),
+        G(K_ / kGroup) {
+    int64_t o = 0;
+    q = o;    o = round_up(o + Np * K / 2, kAlign);        // E2M1 codes, tiled
+    s = o;    o = round_up(o + Np * (K / kMxBlock), kAlign);  // E8M0 scales, tiled
+    l2t = o;  o = round_up(o + Np * rp * 2, kAlign);       // as WeightLayout
+    l1t = o;  o = round_up(o + rp * K * 2, kAlign);
+    iota = o; o = round_up(o + K * 4, kAlign);
+    bias = o; o = round_up(o + Np * 4, kAlign);
+    total = o;
+  }
+};
+
+struct MxWorkLayout {
+  int64_t M = 0, Mp = 0, K = 0, G = 0, rp = 0, S = 0;
+  int64_t qa = 0, sa = 0, d = 0, total = 0;
+  constexpr MxWorkLayout(int64_t M_, int64_t K_, int64_t rank_)
+      : M(M_), Mp(round_up(M_, kPad)), K(K_), G(K_ / kGroup), rp(rank_pad((int)rank_)),
+        S(k1_splits(round_up(M_, kPad), K_ / kGroup)) {
+    int64_t o = 0;
+    qa = o; o = round_up(o + Mp * K / 2, kAlign);          // E2M1 codes, tiled
+    sa = o; o = round_up(o + Mp * (K / kMxBlock), kAlign); // E8M0 scales, tiled
+    d = o;  o = round_up(o + (S > 2 ? S : 2) * Mp * rp * 4, kAlign);   // fp32 partials of D
+    total = o;
+  }
+};
+
 // AWQ W4A16 device blob.  Output channels are cut into tiles of 16; for each
 // (tile, pair of groups of 64) there is a 1024-byte block: lane l (column
 // l % 16 of the tile, quarter q = l / 16 of a group) holds, in 16 bytes, the
