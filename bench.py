@@ -320,22 +320,24 @@ def config_sweep(args):
                 "p90_us": round(float(np.percentile(t, 90)), 2),
                 "back_to_back_us": round(float(np.median(b2b)), 2)}
 
-    def w4a4(name, M, N, K, r, hw, Xbits, gelu):
+    def w4a4(name, M, N, K, r, hw, Xbits, gelu, mx=False):
         R = nsets(2 * M * K + M * N * 2 + N * K // 2 + S.workspace_bytes(M, N, K, r))
         log(f"{name}: {R} buffer sets")
-        Ls = [S.Linear(hw, dev) for _ in range(R)]
+        Ls = [(S.MxLinear if mx else S.Linear)(hw, dev) for _ in range(R)]
         Xs = [dev_bf16(Xbits) if isinstance(Xbits, np.ndarray) else Xbits.clone() for _ in range(R)]
         ws = [Ls[0].new_workspace(M) for _ in range(R)]
         Ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        quant = S.mx_linear_quantize if mx else S.linear_quantize
+        gemm = S.mx_linear_gemm if mx else S.linear_gemm
         for k in range(R):
-            S.linear_quantize(Ls[k], Xs[k], ws[k])
-        k1 = timed(lambda k: S.linear_quantize(Ls[k], Xs[k], ws[k]), R)
-        k2 = timed(lambda k: S.linear_gemm(Ls[k], M, Ys[k], ws[k], gelu=gelu), R)
+            quant(Ls[k], Xs[k], ws[k])
+        k1 = timed(lambda k: quant(Ls[k], Xs[k], ws[k]), R)
+        k2 = timed(lambda k: gemm(Ls[k], M, Ys[k], ws[k], gelu=gelu), R)
         ops = 2.0 * M * N * K
         k1_bytes = 2 * M * K + 4 * K + 2 * K * r + M * K // 2 + 4 * M * (K // 64) + 4 * M * r
         t1, t2 = k1["back_to_back_us"], k2["back_to_back_us"]
         out = {"config": name, "M": M, "N": N, "K": K, "rank": r, "gelu": gelu, "sets": R,
-               "k1": k1, "k2": k2,
+               "k1": k1, "k2": k2, "format": "mxfp4" if mx else "int4",
                "k2_tops": round(ops / t2 / 1e6, 1), "k2_frac_int8": round(ops / t2 / 1e6 / PEAK_INT8_TOPS, 4),
                "k1_gbs": round(k1_bytes / t1 / 1e3, 1), "k1_frac_hbm": round(k1_bytes / t1 / 1e3 / PEAK_HBM_GBS, 4),
                "layer_tops": round(ops / (t1 + t2) / 1e6, 1),
@@ -365,6 +367,16 @@ def config_sweep(args):
     c = synth.lowres_case()
     log("preparing the low-resolution layer on the host")
     w4a4("lowres_r128", c.M, c.N, c.K, 128, S.prepare_weights(c.W, c.calib_absmax(), c.bias, 128), c.X, False)
+    # the FP4 (MXFP4) form on the same layers
+    c = synth.qkv_case()
+    w4a4("qkv_mxfp4", c.M, c.N, c.K, 32, S.mx_prepare_weights(c.W, c.calib_absmax(), c.bias, 32), c.X,
+         False, mx=True)
+    w4a4("mlp_fc1_gelu_mxfp4", fc1.M, fc1.N, fc1.K, 32,
+         S.mx_prepare_weights(fc1.W, fc1.calib_absmax(), fc1.bias, 32), fc1.X, True, mx=True)
+    X2 = dev_bf16(np.random.default_rng(2).standard_normal((fc1.M, fc1.N), dtype=np.float32)
+                  .view(np.uint32).__rshift__(16).astype(np.uint16))
+    w4a4("mlp_fc2_mxfp4", fc1.M, fc1.K, fc1.N, 32, S.mx_prepare_weights(W2, None, b2, 32), X2, False, mx=True)
+    del X2
     a = synth.awq_case()
     q, sc, z = S.awq_quantize_weights(a.W)
     R = nsets(a.N * a.K // 2 + a.N * (a.K // 64) * 4)

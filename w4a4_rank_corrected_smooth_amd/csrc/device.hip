@@ -149,13 +149,14 @@ __device__ __forceinline__ float quantize_lane(const uint4 (&xr)[4], const float
 // with E the biased exponent field of a, floor(log2 a) = E - 127 for a
 // normal a, so the block exponent e = floor(log2 a) - 2 is E - 129, clamped
 // at -127, which also covers a zero or subnormal a (E = 0).  Each
-// x_hat 2^-e (exact: a power of two, no overflow as |x_hat| < 2^(e+3)) is
-// rounded to the nearest FP4 E2M1 magnitude by counting the rounding
-// boundaries it passes (ties go to the even mantissa bit: 0.25 -> 0,
-// 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4; above 5 -> 6,
-// which saturates), with the sign in bit 3 unless the magnitude is 0.
-// Codes go out in canonical nibble order (code i at bits 4 (i % 8) of word
-// i / 8); returns the E8M0 byte e + 127.
+// r = x_hat 2^-e is exact (a power of two, 2^-e a normal float, |r| < 8).
+// gfx950's packed FP4 conversion rounds r to the nearest E2M1 value, ties to
+// the even mantissa bit, saturating at 6 (checked against that definition
+// on every multiple of 1/128 in [-8, 8] and beyond), two values per
+// instruction, low nibble first; it keeps the sign of a zero, so -0 codes
+// (sign bit alone) are cleared afterwards.  Codes go out in canonical nibble
+// order (code i at bits 4 (i % 8) of word i / 8); returns the E8M0 byte
+// e + 127.
 __device__ __forceinline__ uint32_t quantize_lane_mx(const uint4 (&xm)[4], const float4 (&io)[8],
                                                      uint4 &codes) {
   float v[32];
@@ -166,8 +167,8 @@ __device__ __forceinline__ uint32_t quantize_lane_mx(const uint4 (&xm)[4], const
     const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      v[8 * j + 2 * c] = bf16_lo(wv[c]) * iv[2 * c];
-      v[8 * j + 2 * c + 1] = bf16_hi(wv[c]) * iv[2 * c + 1];
+      v[8 * j + 2 * c] = __fmul_rn(bf16_lo(wv[c]), iv[2 * c]);
+      v[8 * j + 2 * c + 1] = __fmul_rn(bf16_hi(wv[c]), iv[2 * c + 1]);
     }
   }
   float a = 0.0f;
@@ -176,16 +177,18 @@ __device__ __forceinline__ uint32_t quantize_lane_mx(const uint4 (&xm)[4], const
   const int E = (int)(__float_as_uint(a) >> 23);
   const int e = E == 0 ? -127 : max(E - 129, -127);
   const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  uint32_t w[4];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float r = v[i] * inv;
-    const float m = fabsf(r);
-    const uint32_t idx = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
-                         (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
-                         (uint32_t)(m > 5.0f);
-    const uint32_t code = idx | ((r < 0.0f && idx != 0u) ? 8u : 0u);
-    w[i / 8] |= code << (4 * (i % 8));
+  for (int j = 0; j < 4; ++j) {
+    uint32_t d = 0u;
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, __fmul_rn(v[8 * j], inv), __fmul_rn(v[8 * j + 1], inv), 1.0f, 0);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, __fmul_rn(v[8 * j + 2], inv), __fmul_rn(v[8 * j + 3], inv), 1.0f, 1);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, __fmul_rn(v[8 * j + 4], inv), __fmul_rn(v[8 * j + 5], inv), 1.0f, 2);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, __fmul_rn(v[8 * j + 6], inv), __fmul_rn(v[8 * j + 7], inv), 1.0f, 3);
+    // keep a nibble's sign bit only where its magnitude bits are not all 0
+    const uint32_t mag = d & 0x77777777u;
+    const uint32_t nz = (mag | (mag >> 1) | (mag >> 2)) & 0x11111111u;
+    w[j] = mag | (d & (nz << 3));
   }
   codes = make_uint4(w[0], w[1], w[2], w[3]);
   return (uint32_t)(e + 127);
