@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 256 CU x 2.4 GHz x 8192 ops/clk
 PEAK_HBM_GBS = 8000.0
+PEAK_FP4_TOPS = 10100.0     # MI355X dense FP4 MFMA
 
 
 def log(msg):
@@ -267,6 +268,66 @@ def summarize_configs(trace_dir, sweep_jsonl, out_path, command):
     print("\n".join(lines))
 
 
+def mx_pair(args, S, fc1, W2, b2, ax2, X, R, dev, stream):
+    """The MLP pair in the FP4 (MXFP4) form of the path, on the same inputs:
+    fc1 quantise, fc1 GEMM + GELU (bf16 out), fc2 quantise, fc2 GEMM, timed
+    like the step (uninstrumented steps for the rate, a pass with events
+    between kernels for each kernel's duration).  Reported beside the INT4
+    headline, not instead of it."""
+    import numpy as np
+    import torch
+    log("MXFP4 form: preparing fc1 and fc2 on the host")
+    m1 = [S.MxLinear(S.mx_prepare_weights(fc1.W, fc1.calib_absmax(), fc1.bias, 32), dev) for _ in range(R)]
+    m2 = [S.MxLinear(S.mx_prepare_weights(W2, ax2, b2, 32), dev) for _ in range(R)]
+    M, N1, K1 = fc1.M, fc1.N, fc1.K
+    w1 = [m1[0].new_workspace(M) for _ in range(R)]
+    w2 = [m2[0].new_workspace(M) for _ in range(R)]
+    Y1 = [torch.empty((M, N1), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    Y2 = [torch.empty((M, K1), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+
+    def step(i, ev=None):
+        k = i % R
+
+        def mark(j):
+            if ev:
+                ev[j].record(stream)
+        mark(0)
+        S.mx_linear_quantize(m1[k], X[k], w1[k])
+        mark(1)
+        S.mx_linear_gemm(m1[k], M, Y1[k], w1[k], gelu=True)
+        mark(2)
+        S.mx_linear_quantize(m2[k], Y1[k], w2[k])
+        mark(3)
+        S.mx_linear_gemm(m2[k], M, Y2[k], w2[k])
+        mark(4)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    names = ["fc1_quantize", "fc1_gemm_gelu", "fc2_quantize", "fc2_gemm"]
+    us = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) * 1e3 for e in evs])) for j, n in enumerate(names)}
+    ops = 2.0 * M * N1 * K1
+    k2 = 0.5 * (us["fc1_gemm_gelu"] + us["fc2_gemm"])
+    del m1, m2, w1, w2, Y1, Y2
+    torch.cuda.empty_cache()
+    return {"format": "mxfp4 (OCP MX: E2M1 codes, E8M0 scale per 32)",
+            "ms_per_step": round(wall / args.steps * 1e3, 4),
+            "value": round(2 * ops / (wall / args.steps) / 1e12, 2), "unit": "TOPS",
+            "kernels_us": {n: round(v, 2) for n, v in us.items()},
+            "k2_avg_us": round(k2, 2), "k2_tops": round(ops / k2 / 1e6, 1),
+            "k2_frac_int8": round(ops / k2 / 1e6 / PEAK_INT8_TOPS, 4),
+            "k2_frac_fp4": round(ops / k2 / 1e6 / PEAK_FP4_TOPS, 4)}
+
+
 def config_sweep(args):
     """Per-configuration kernel timings (not the one-line contract): for each
     W4A4 configuration, the quantiser (kernel 1) and the GEMM (kernel 2) are
@@ -403,6 +464,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-unfused", action="store_true",
                     help="do not time the unfused pair (profiling runs: only the step's own kernels)")
+    ap.add_argument("--skip-mx", action="store_true",
+                    help="do not time the MXFP4 form of the MLP pair")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run an elementwise copy of known size (for HBM counter calibration)")
     ap.add_argument("--profiled-log", default=None,
@@ -421,7 +484,7 @@ def main():
         return
     if args.summarize_profile:
         t, fe, wr = args.summarize_profile
-        base = "python3 bench.py --no-cpu-baseline --calibration-copy --skip-unfused"
+        base = "python3 bench.py --no-cpu-baseline --calibration-copy --skip-unfused --skip-mx"
         cmd = {"trace": f"rocprofv3 --kernel-trace --stats -f csv -d {t} -- {base}",
                "fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d {fe} -- {base}",
                "write": f"rocprofv3 --pmc WRITE_SIZE -f csv -d {wr} -- {base}"}
@@ -547,6 +610,10 @@ def main():
         step(args.warmup + args.steps + i, events[i])
     torch.cuda.synchronize()
 
+    mx = None
+    if not args.skip_mx:
+        mx = mx_pair(args, S, fc1, W2, b2, ax2, X, R, dev, stream)
+
     names = ["fc1_quantize", "fc1_gemm_gelu_quantize_fc2", "fc2_gemm", "awq_m1"]
     dur = {n: [] for n in names}
     span = []
@@ -598,6 +665,7 @@ def main():
                          {"ms_per_step": round(wall_unfused / args.steps * 1e3, 4),
                           "value": round(2 * ops_layer / (wall_unfused / args.steps) / 1e12, 2)}),
         "awq_gbs": round(awq_bytes / avg["awq_m1"] / 1e3, 1),
+        "mxfp4_pair": mx,
         "prepare_s": {"fc1": round(prep1, 2), "fc2": round(prep2, 2)},
         "source_hash": source_hash(),
     }
