@@ -18,5 +18,6 @@ from .gen import (  # noqa: F401
     lowres_case,
     awq_case,
     on_grid_case,
+    lora_factors,
     WORKLOADS,
 )

@@ -156,6 +156,17 @@ def awq_case(m_max: int = 16, N: int = 18432, K: int = 3072, seed: int = 4) -> A
     return AwqCase(name="awq", seed=seed, N=N, K=K, x=x, W=W)
 
 
+def lora_factors(seed: int, N: int, K: int, rank: int, a_std: float = 0.02,
+                 b_std: float = 0.02):
+    """A user LoRA for a [N, K] linear layer: down factor A [rank, K] and up
+    factor B [N, rank], both N(0, std) rounded to bf16 (A drawn first).
+    Returns the two arrays of bf16 patterns."""
+    rng = np.random.default_rng(seed)
+    A = rng.standard_normal((rank, K), dtype=np.float32) * np.float32(a_std)
+    B = rng.standard_normal((N, rank), dtype=np.float32) * np.float32(b_std)
+    return f32_to_bf16_bits(A), f32_to_bf16_bits(B)
+
+
 def on_grid_case(seed: int, M: int, N: int, K: int, exp_lo: int = 0, exp_hi: int = 0,
                  group: int = 64) -> LinearCase:
     """Activations and weights that already lie on the signed INT4 grid: every
