@@ -381,7 +381,7 @@ def config_sweep(args):
                 "p90_us": round(float(np.percentile(t, 90)), 2),
                 "back_to_back_us": round(float(np.median(b2b)), 2)}
 
-    def w4a4(name, M, N, K, r, hw, Xbits, gelu, mx=False):
+    def w4a4(name, M, N, K, r, hw, Xbits, gelu, mx=False, extra=None):
         R = nsets(2 * M * K + M * N * 2 + N * K // 2 + S.workspace_bytes(M, N, K, r))
         log(f"{name}: {R} buffer sets")
         Ls = [(S.MxLinear if mx else S.Linear)(hw, dev) for _ in range(R)]
@@ -403,6 +403,7 @@ def config_sweep(args):
                "k1_gbs": round(k1_bytes / t1 / 1e3, 1), "k1_frac_hbm": round(k1_bytes / t1 / 1e3 / PEAK_HBM_GBS, 4),
                "layer_tops": round(ops / (t1 + t2) / 1e6, 1),
                "lowrank_gflop": round(2.0 * M * (K + N) * r / 1e9, 2)}
+        out.update(extra or {})
         print(json.dumps(out), flush=True)
         del Ls, Xs, ws, Ys
         torch.cuda.empty_cache()
@@ -416,6 +417,14 @@ def config_sweep(args):
     log("preparing fc1 on the host")
     hw1 = S.prepare_weights(fc1.W, fc1.calib_absmax(), fc1.bias, 32)
     w4a4("mlp_fc1_gelu", fc1.M, fc1.N, fc1.K, 32, hw1, fc1.X, True)
+    # a user LoRA of rank 32 carried by the branch (merged rank 64)
+    A, B = synth.lora_factors(5, fc1.N, fc1.K, 32)
+    t0 = time.perf_counter()
+    hwl = S.merge_lora(hw1, A, B, 1.0)
+    merge_s = time.perf_counter() - t0
+    w4a4("mlp_fc1_gelu_lora32", fc1.M, fc1.N, fc1.K, 64, hwl, fc1.X, True,
+         extra={"lora_rank": 32, "merge_s": round(merge_s, 4)})
+    del hwl
     L1 = S.Linear(hw1, dev)
     Y1 = S.linear_forward(L1, dev_bf16(fc1.X), out_dtype=torch.bfloat16, gelu=True)
     torch.cuda.synchronize()

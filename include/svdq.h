@@ -139,6 +139,33 @@ size_t svdq_device_weights_bytes(int N, int K, int rank);
 svdq_status_t svdq_pack_device_weights(const svdq_host_weights_t *in,
                                        void *host_blob, size_t bytes);
 
+/* A user LoRA carried by the layer's low-rank branch (host only).  The pages
+ * keep LoRA loading working on quantised models ("Bringing Nunchaku 4-bit
+ * diffusion inference to Diffusers", Vietnamese edition, section "Tải
+ * nguyên bản trong Diffusers"; Russian edition, closing paragraph), and the
+ * Hacker News thread "SVDQuant: 4-Bit Quantization Powers 12B Flux on a 16GB
+ * 4090 GPU with 3x Speedup" describes the branch itself as a LoRA.  A LoRA
+ * with down factor A [r', K] and up factor B [N, r'] (bf16, row-major, the
+ * nn.Linear layouts of its two projections) and scale alpha adds
+ * alpha (X A^T) B^T to Y.  The merged layer has rank r + r':
+ *   l1s' = [l1s | A^T]                  [K, r + r']
+ *   l2'  = [l2 ; bf16(fl32(alpha B^T))]  [r + r', N]
+ * (one float32 product per element, one rounding to bf16); A acts on the raw
+ * activations.  Smoothing factors, residual codes and scales and bias are
+ * unchanged, so the 4-bit path is the base layer's bit for bit.
+ *   in:  a prepared layer; it is not modified.
+ *   out: caller-allocated with svdq_host_weights_sizes(N, K, r + r'); its
+ *        l1s and l2 must not overlap in's factors (SVDQ_ERR_INVALID_ARGUMENT).
+ *        Its inv_lambda, qweight, wscales and bias may be the very buffers of
+ *        `in` (then they are left as they are) or separate ones (copied).
+ *        N, K, rank (= r + r') and group_size are set on success.
+ * lora_rank = 0 copies the layer.  Errors: SVDQ_ERR_UNSUPPORTED_SHAPE when
+ * r + r' exceeds min(N, K, SVDQ_MAX_RANK); SVDQ_ERR_NUMERICAL for a
+ * non-finite alpha, down factor or alpha * up factor (nothing is written). */
+svdq_status_t svdq_merge_lora(const svdq_host_weights_t *in, const uint16_t *lora_down_bf16,
+                              const uint16_t *lora_up_bf16, int lora_rank, float alpha,
+                              svdq_host_weights_t *out);
+
 /* A prepared layer resident in device memory. */
 typedef struct {
   const void *blob;   /* device pointer to the uploaded blob */
@@ -250,6 +277,13 @@ size_t svdq_mx_device_weights_bytes(int N, int K, int rank);
 svdq_status_t svdq_mx_pack_device_weights(const svdq_mx_host_weights_t *in,
                                           void *host_blob, size_t bytes);
 size_t svdq_mx_workspace_bytes(int M, int N, int K, int rank);
+
+/* svdq_merge_lora for an MXFP4 layer: the same factor concatenation, the
+ * same arguments, ownership and errors; the E8M0 scales are copied like the
+ * INT4 group scales. */
+svdq_status_t svdq_mx_merge_lora(const svdq_mx_host_weights_t *in, const uint16_t *lora_down_bf16,
+                                 const uint16_t *lora_up_bf16, int lora_rank, float alpha,
+                                 svdq_mx_host_weights_t *out);
 
 /* Y = linear(X) [+ epilogue] through the MXFP4 path, with the conventions of
  * svdq_linear_forward; `w` describes a blob packed by

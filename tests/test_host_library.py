@@ -435,3 +435,75 @@ def test_host_weights_accept_fortran_ordered_arrays():
     l2t = blob[off_l2t: off_l2t + Np * rp * 2].view(np.uint16).reshape(Np, rp)
     assert np.array_equal(l2t[:96, :6].T, O.bf16_bits_of(ref["L2b"]))
     assert L == len(blob)
+
+
+# ------------------------------------------------------- user LoRA merge
+from oracle import lora as LO  # noqa: E402
+
+
+@pytest.mark.parametrize("form", ["int4", "mx"])
+@pytest.mark.parametrize("rank,r2,alpha", [(8, 5, 0.3), (0, 16, -1.25), (16, 0, 2.0)])
+def test_merge_lora_bit_exact(form, rank, r2, alpha):
+    c = synth.linear_case("lmerge", 92, 8, 96, 192, rank, x_outlier_n=2, x_outlier_scale=20.0)
+    A, B = synth.lora_factors(93, c.N, c.K, r2, b_std=0.7)
+    if form == "int4":
+        hw = S.prepare_weights(c.W, c.calib_absmax(), c.bias, rank)
+        ref = LO.merge(O.prepare(c.W, c.calib_absmax(), c.bias, rank), A, B, alpha)
+        got = S.merge_lora(hw, A, B, alpha)
+    else:
+        hw = S.mx_prepare_weights(c.W, c.calib_absmax(), c.bias, rank)
+        ref = LO.merge(MXO.prepare(c.W, c.calib_absmax(), c.bias, rank), A, B, alpha)
+        got = S.mx_merge_lora(hw, A, B, alpha)
+    assert got.rank == rank + r2 == ref["rank"]
+    # the appended LoRA factors bit for bit (the base factors' singular
+    # vectors may differ from the oracle's in sign, so those are compared
+    # with the host's own base layer below)
+    assert np.array_equal(got.l1s[:, rank:], O.bf16_bits_of(ref["L1s"][:, rank:]))
+    assert np.array_equal(got.l2[rank:], O.bf16_bits_of(ref["L2b"][rank:]))
+    # the 4-bit arrays are the base layer's own buffers, untouched
+    assert got.qweight is hw.qweight and got.wscales is hw.wscales
+    assert np.array_equal(got.l1s[:, :rank], hw.l1s) and np.array_equal(got.l2[:rank], hw.l2)
+
+
+def test_merge_lora_copies_into_separate_buffers_and_errors():
+    lib = S._lib
+    c = synth.linear_case("lmerr", 94, 8, 64, 128, 4, x_outlier_n=2, x_outlier_scale=20.0)
+    hw = S.prepare_weights(c.W, c.calib_absmax(), c.bias, 4)
+    A, B = synth.lora_factors(95, c.N, c.K, 3)
+    src = hw.as_struct()
+    out = S.PreparedHost(c.N, c.K, 7, np.zeros(c.K, np.float32), np.zeros((c.K, 7), np.uint16),
+                         np.zeros((7, c.N), np.uint16), np.zeros_like(hw.qweight),
+                         np.zeros_like(hw.wscales), np.zeros_like(hw.bias))
+    dst = out.as_struct()
+    assert lib.svdq_merge_lora(ctypes.byref(src), A.ctypes.data, B.ctypes.data, 3, 1.0,
+                               ctypes.byref(dst)) == 0
+    for k in ("inv_lambda", "qweight", "wscales", "bias"):
+        assert np.array_equal(getattr(out, k), getattr(hw, k))
+    assert (dst.N, dst.K, dst.rank, dst.group_size) == (c.N, c.K, 7, 64)
+    # errors: merged rank too large, non-finite alpha / factors / product,
+    # negative rank, missing factors, output factors aliasing the input's
+    big = np.zeros((c.N - 2, c.K), np.uint16), np.zeros((c.N, c.N - 2), np.uint16)
+    assert lib.svdq_merge_lora(ctypes.byref(src), big[0].ctypes.data, big[1].ctypes.data, c.N - 2,
+                               1.0, ctypes.byref(dst)) == SHAPE
+    assert lib.svdq_merge_lora(ctypes.byref(src), A.ctypes.data, B.ctypes.data, 3, float("nan"),
+                               ctypes.byref(dst)) == NUM
+    An = A.copy()
+    An[1, 7] = 0x7F80                      # bf16 +inf
+    assert lib.svdq_merge_lora(ctypes.byref(src), An.ctypes.data, B.ctypes.data, 3, 1.0,
+                               ctypes.byref(dst)) == NUM
+    Bh = B.copy()
+    Bh[5, 1] = 0x7F00                      # 2^127: times 4 overflows float32
+    before = out.l2.copy()
+    assert lib.svdq_merge_lora(ctypes.byref(src), A.ctypes.data, Bh.ctypes.data, 3, 4.0,
+                               ctypes.byref(dst)) == NUM
+    assert np.array_equal(out.l2, before)  # nothing written on failure
+    assert lib.svdq_merge_lora(ctypes.byref(src), A.ctypes.data, B.ctypes.data, -1, 1.0,
+                               ctypes.byref(dst)) == SHAPE
+    assert lib.svdq_merge_lora(ctypes.byref(src), None, B.ctypes.data, 3, 1.0,
+                               ctypes.byref(dst)) == INV
+    alias = S.HostWeights(c.N, c.K, 7, 64, dst.inv_lambda, src.l1s, dst.l2, dst.qweight,
+                          dst.wscales, dst.bias)
+    assert lib.svdq_merge_lora(ctypes.byref(src), A.ctypes.data, B.ctypes.data, 3, 1.0,
+                               ctypes.byref(alias)) == INV
+    with pytest.raises(ValueError):
+        S.merge_lora(hw, A, B[:, :2])

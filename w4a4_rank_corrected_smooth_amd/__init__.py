@@ -48,6 +48,7 @@ EXPORTS = [
     "svdq_mx_host_weights_sizes", "svdq_mx_prepare_weights", "svdq_mx_device_weights_bytes",
     "svdq_mx_pack_device_weights", "svdq_mx_workspace_bytes", "svdq_mx_linear_forward",
     "svdq_mx_linear_quantize", "svdq_mx_linear_gemm", "svdq_mx_quantize_activations",
+    "svdq_merge_lora", "svdq_mx_merge_lora",
 ]
 
 
@@ -110,6 +111,10 @@ _sig("svdq_mx_linear_forward", _i, [_W, _vp, _i, _vp, _i, _i, _vp, _sz, _vp])
 _sig("svdq_mx_linear_quantize", _i, [_W, _vp, _i, _vp, _sz, _vp])
 _sig("svdq_mx_linear_gemm", _i, [_W, _i, _vp, _i, _i, _vp, _sz, _vp])
 _sig("svdq_mx_quantize_activations", _i, [_W, _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp])
+_sig("svdq_merge_lora", _i, [ctypes.POINTER(HostWeights), _vp, _vp, _i, ctypes.c_float,
+                             ctypes.POINTER(HostWeights)])
+_sig("svdq_mx_merge_lora", _i, [ctypes.POINTER(MxHostWeights), _vp, _vp, _i, ctypes.c_float,
+                                ctypes.POINTER(MxHostWeights)])
 
 
 class SvdqError(RuntimeError):
@@ -211,6 +216,30 @@ def pack_device_weights(hw: PreparedHost) -> np.ndarray:
     s = hw.as_struct()
     _check(_lib.svdq_pack_device_weights(ctypes.byref(s), _ptr(blob), n), "svdq_pack_device_weights")
     return blob
+
+
+def _lora_args(hw, A_bits, B_bits):
+    A = np.ascontiguousarray(A_bits, dtype=np.uint16)
+    B = np.ascontiguousarray(B_bits, dtype=np.uint16)
+    if A.ndim != 2 or B.ndim != 2 or A.shape[1] != hw.K or B.shape != (hw.N, A.shape[0]):
+        raise ValueError(f"LoRA factors must be A [r', K={hw.K}] and B [N={hw.N}, r'], "
+                         f"got {A.shape} and {B.shape}")
+    return A, B, A.shape[0]
+
+
+def merge_lora(hw: PreparedHost, A_bits: np.ndarray, B_bits: np.ndarray,
+               alpha: float = 1.0) -> PreparedHost:
+    """A user LoRA (down A [r', K], up B [N, r'], bf16 patterns) concatenated
+    onto the low-rank branch of `hw` (svdq_merge_lora).  The 4-bit arrays are
+    shared with `hw`, not copied; `hw` is unchanged."""
+    A, B, r2 = _lora_args(hw, A_bits, B_bits)
+    rt = hw.rank + r2
+    out = PreparedHost(hw.N, hw.K, rt, hw.inv_lambda, np.empty((hw.K, rt), np.uint16),
+                       np.empty((rt, hw.N), np.uint16), hw.qweight, hw.wscales, hw.bias)
+    src, dst = hw.as_struct(), out.as_struct()
+    _check(_lib.svdq_merge_lora(ctypes.byref(src), _ptr(A), _ptr(B), r2, float(alpha),
+                                ctypes.byref(dst)), "svdq_merge_lora")
+    return out
 
 
 class Linear:
@@ -409,6 +438,19 @@ def mx_pack_device_weights(hw: PreparedHostMx) -> np.ndarray:
     _check(_lib.svdq_mx_pack_device_weights(ctypes.byref(s), _ptr(blob), n),
            "svdq_mx_pack_device_weights")
     return blob
+
+
+def mx_merge_lora(hw: PreparedHostMx, A_bits: np.ndarray, B_bits: np.ndarray,
+                  alpha: float = 1.0) -> PreparedHostMx:
+    """merge_lora for an MXFP4 layer (svdq_mx_merge_lora)."""
+    A, B, r2 = _lora_args(hw, A_bits, B_bits)
+    rt = hw.rank + r2
+    out = PreparedHostMx(hw.N, hw.K, rt, hw.inv_lambda, np.empty((hw.K, rt), np.uint16),
+                         np.empty((rt, hw.N), np.uint16), hw.qweight, hw.wscales, hw.bias)
+    src, dst = hw.as_struct(), out.as_struct()
+    _check(_lib.svdq_mx_merge_lora(ctypes.byref(src), _ptr(A), _ptr(B), r2, float(alpha),
+                                   ctypes.byref(dst)), "svdq_mx_merge_lora")
+    return out
 
 
 class MxLinear:

@@ -43,6 +43,52 @@ static bool shape_ok(int N, int K, int rank, const char *who, svdq_status_t *st)
   return true;
 }
 
+static bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+static void copy_unless_same(void *dst, const void *src, size_t bytes) {
+  if (dst != src && bytes) std::memmove(dst, src, bytes);
+}
+
+// Shared checks and the factor merge of svdq_merge_lora / svdq_mx_merge_lora.
+template <typename HW>
+static svdq_status_t merge_lora_checked(const HW *in, const uint16_t *A, const uint16_t *B, int r2,
+                                        float alpha, HW *out, const char *who) {
+  svdq_status_t st;
+  if (!in || !out) return fail(SVDQ_ERR_INVALID_ARGUMENT, "%s: NULL weights", who);
+  if (r2 < 0) return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "%s: lora_rank=%d < 0", who, r2);
+  if (r2 > 0 && (!A || !B)) return fail(SVDQ_ERR_INVALID_ARGUMENT, "%s: NULL LoRA factor", who);
+  const int N = in->N, K = in->K, r = in->rank;
+  if (!shape_ok(N, K, r, who, &st)) return st;
+  if (r + r2 > SVDQ_MAX_RANK || r + r2 > N || r + r2 > K)
+    return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "%s: merged rank %d + %d outside [0, min(N=%d, K=%d, %d)]",
+                who, r, r2, N, K, SVDQ_MAX_RANK);
+  if (!in->inv_lambda || !in->qweight || !in->wscales || !in->bias || (r > 0 && (!in->l1s || !in->l2)))
+    return fail(SVDQ_ERR_INVALID_ARGUMENT, "%s: NULL input buffer", who);
+  const int rt = r + r2;
+  if (!out->inv_lambda || !out->qweight || !out->wscales || !out->bias ||
+      (rt > 0 && (!out->l1s || !out->l2)))
+    return fail(SVDQ_ERR_INVALID_ARGUMENT, "%s: NULL output buffer", who);
+  const size_t f_in = 2 * (size_t)K * r, u_in = 2 * (size_t)r * N;
+  const size_t f_out = 2 * (size_t)K * rt, u_out = 2 * (size_t)rt * N;
+  if (overlaps(out->l1s, f_out, in->l1s, f_in) || overlaps(out->l1s, f_out, in->l2, u_in) ||
+      overlaps(out->l2, u_out, in->l1s, f_in) || overlaps(out->l2, u_out, in->l2, u_in) ||
+      overlaps(out->l1s, f_out, out->l2, u_out))
+    return fail(SVDQ_ERR_INVALID_ARGUMENT, "%s: output factors overlap the input factors", who);
+  st = merge_lora_factors(N, K, r, in->l1s, in->l2, A, B, r2, alpha, out->l1s, out->l2);
+  if (st != SVDQ_OK) return st;
+  copy_unless_same(out->inv_lambda, in->inv_lambda, sizeof(float) * (size_t)K);
+  copy_unless_same(out->bias, in->bias, sizeof(float) * (size_t)N);
+  copy_unless_same(out->qweight, in->qweight, (size_t)N * K / 2);
+  out->N = N;
+  out->K = K;
+  out->rank = rt;
+  return SVDQ_OK;
+}
+
 }  // namespace svdq
 
 using namespace svdq;
@@ -124,6 +170,19 @@ svdq_status_t svdq_pack_device_weights(const svdq_host_weights_t *in, void *blob
   return pack_device_weights(in, blob, bytes);
 }
 
+svdq_status_t svdq_merge_lora(const svdq_host_weights_t *in, const uint16_t *lora_down_bf16,
+                              const uint16_t *lora_up_bf16, int lora_rank, float alpha,
+                              svdq_host_weights_t *out) {
+  if (in && in->group_size != kGroup)
+    return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "svdq_merge_lora: group_size=%d (64 only)", in->group_size);
+  const svdq_status_t st = merge_lora_checked(in, lora_down_bf16, lora_up_bf16, lora_rank, alpha,
+                                              out, "svdq_merge_lora");
+  if (st != SVDQ_OK) return st;
+  copy_unless_same(out->wscales, in->wscales, sizeof(float) * (size_t)in->N * (in->K / kGroup));
+  out->group_size = kGroup;
+  return SVDQ_OK;
+}
+
 svdq_status_t svdq_mx_host_weights_sizes(int N, int K, int rank, size_t sizes_out[6]) {
   svdq_status_t st;
   if (!sizes_out) return fail(SVDQ_ERR_INVALID_ARGUMENT, "sizes_out is NULL");
@@ -162,6 +221,16 @@ svdq_status_t svdq_mx_pack_device_weights(const svdq_mx_host_weights_t *in, void
       (in->rank > 0 && (!in->l1s || !in->l2)))
     return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_mx_pack_device_weights: NULL input buffer");
   return pack_device_weights_mx(in, blob, bytes);
+}
+
+svdq_status_t svdq_mx_merge_lora(const svdq_mx_host_weights_t *in, const uint16_t *lora_down_bf16,
+                                 const uint16_t *lora_up_bf16, int lora_rank, float alpha,
+                                 svdq_mx_host_weights_t *out) {
+  const svdq_status_t st = merge_lora_checked(in, lora_down_bf16, lora_up_bf16, lora_rank, alpha,
+                                              out, "svdq_mx_merge_lora");
+  if (st != SVDQ_OK) return st;
+  copy_unless_same(out->wscales, in->wscales, (size_t)in->N * (in->K / kMxBlock));
+  return SVDQ_OK;
 }
 
 size_t svdq_mx_workspace_bytes(int M, int N, int K, int rank) {

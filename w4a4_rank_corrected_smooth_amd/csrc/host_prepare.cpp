@@ -54,6 +54,35 @@ uint16_t f64_to_bf16(double x) {
   return (uint16_t)(f32_bits((float)r) >> 16);        // r is a bf16 value
 }
 
+// ------------------------------------------------------- user LoRA merge
+svdq_status_t merge_lora_factors(int N, int K, int rank, const uint16_t *l1s, const uint16_t *l2,
+                                 const uint16_t *A, const uint16_t *B, int r2, float alpha,
+                                 uint16_t *l1s_out, uint16_t *l2_out) {
+  const int rt = rank + r2;
+  if (!std::isfinite(alpha))
+    return fail(SVDQ_ERR_NUMERICAL, "svdq_merge_lora: alpha is not finite");
+  for (int64_t i = 0; i < (int64_t)r2 * K; ++i)
+    if (!std::isfinite(bf16_to_f32(A[i])))
+      return fail(SVDQ_ERR_NUMERICAL, "svdq_merge_lora: non-finite LoRA down factor");
+  // the scaled up factor first, so that nothing is written on failure
+  std::vector<uint16_t> up((size_t)r2 * N);
+  for (int n = 0; n < N; ++n)
+    for (int j = 0; j < r2; ++j) {
+      const float p = alpha * bf16_to_f32(B[(int64_t)n * r2 + j]);   // one fp32 product
+      if (!std::isfinite(p))
+        return fail(SVDQ_ERR_NUMERICAL, "svdq_merge_lora: alpha * up factor is not finite");
+      up[(size_t)j * N + n] = f64_to_bf16((double)p);                // exact widening, one rounding
+    }
+  for (int k = 0; k < K; ++k) {
+    uint16_t *row = l1s_out + (int64_t)k * rt;
+    for (int t = 0; t < rank; ++t) row[t] = l1s[(int64_t)k * rank + t];
+    for (int j = 0; j < r2; ++j) row[rank + j] = A[(int64_t)j * K + k];
+  }
+  if (rank > 0) std::memcpy(l2_out, l2, sizeof(uint16_t) * (size_t)rank * N);
+  if (r2 > 0) std::memcpy(l2_out + (size_t)rank * N, up.data(), sizeof(uint16_t) * up.size());
+  return SVDQ_OK;
+}
+
 // --------------------------------------------------------- group quantiser
 void quantize_group64(const float *v, int8_t *q, float *s) {
   float a = 0.0f;

@@ -25,6 +25,12 @@ svdq_status_t prepare_weights_mx(const uint16_t *W_bf16, int N, int K, const flo
                                  const uint16_t *bias_bf16, int rank, svdq_mx_host_weights_t *out);
 svdq_status_t pack_device_weights_mx(const svdq_mx_host_weights_t *in, void *host_blob, size_t bytes);
 
+// User LoRA concatenated onto a low-rank branch (see svdq_merge_lora):
+// l1s_out [K, r + r2] = [l1s | A^T], l2_out [r + r2, N] = [l2 ; bf16(fl32(alpha B^T))].
+svdq_status_t merge_lora_factors(int N, int K, int rank, const uint16_t *l1s, const uint16_t *l2,
+                                 const uint16_t *A_bf16, const uint16_t *B_bf16, int r2,
+                                 float alpha, uint16_t *l1s_out, uint16_t *l2_out);
+
 svdq_status_t awq_quantize(const uint16_t *W_fp16, int N, int K, uint8_t *q, uint16_t *s,
                            uint16_t *z);
 
