@@ -571,26 +571,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // MXFP4 stage of K-step g: A codes (4 tile blocks of 1 KB), B codes (8),
   // and one copy of the step's E8M0 scales (lanes 0-15: A's 256 bytes,
-  // 16-47: B's 512, 48-63 repeat A's); 13 wavefront-loads, wavefront w
-  // issuing loads w, w + 4, w + 8 (and 12 for w = 0).  LDS: [A 4 KB][B 8 KB]
-  // [A scales 256 B][B scales 512 B].
+  // 16-47: B's 512, 48-63 repeat A's); 13 wavefront-loads.  Wavefront w
+  // copies A block w and B blocks w and w + 4; wavefront 0 also the scales.
+  // Every source is a base fixed per wavefront (per lane for the scales)
+  // plus g times a fixed step, so the copies take no branches.  LDS: [A 4 KB]
+  // [B 8 KB][A scales 256 B][B scales 512 B].
+  const uint8_t *mx_a = p.qa + (int64_t)(bm / kTile + wu) * 1024;
+  const uint8_t *mx_b = p.qw + (int64_t)(bn / kTile + wu) * 1024;
+  const int64_t mx_astep = (int64_t)Ta * 1024, mx_bstep = (int64_t)Tw * 1024;
+  const bool sc_b = lane >= 16 && lane < 48;
+  const uint8_t *mx_sc = sc_b ? p.sqw + (int64_t)(bn / kTile) * 64 + (lane - 16) * 16
+                              : p.sqa + (int64_t)(bm / kTile) * 64 + (lane & 15) * 16;
+  const int64_t mx_scstep = sc_b ? (int64_t)Tw * 64 : (int64_t)Ta * 64;
   auto fetch_mx = [&](int g) {
     const uint32_t buf = smem_lds + (uint32_t)((g % NBUF) * STAGE);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int L = wu + NWAVES * r;
-      if (L >= 13) break;
-      if (L < 4) {
-        lds_dma16_s(p.qa + ((int64_t)g * Ta + bm / kTile + L) * 1024, voff, buf + (uint32_t)(L * 1024));
-      } else if (L < 12) {
-        lds_dma16_s(p.qw + ((int64_t)g * Tw + bn / kTile + (L - 4)) * 1024, voff, buf + (uint32_t)(L * 1024));
-      } else {
-        const uint8_t *src = lane < 16 ? p.sqa + ((int64_t)g * Ta + bm / kTile) * 64 + lane * 16
-                           : lane < 48 ? p.sqw + ((int64_t)g * Tw + bn / kTile) * 64 + (lane - 16) * 16
-                                       : p.sqa + ((int64_t)g * Ta + bm / kTile) * 64 + (lane - 48) * 16;
-        lds_dma16(src, buf + (uint32_t)(12 * 1024));
-      }
-    }
+    lds_dma16_s(mx_a + g * mx_astep, voff, buf + (uint32_t)(wu * 1024));
+    lds_dma16_s(mx_b + g * mx_bstep, voff, buf + (uint32_t)((4 + wu) * 1024));
+    lds_dma16_s(mx_b + g * mx_bstep + 4 * 1024, voff, buf + (uint32_t)((8 + wu) * 1024));
+    if (wu == 0) lds_dma16(mx_sc + g * mx_scstep, buf + (uint32_t)(12 * 1024));
   };
 
   // Operands of one group as a wavefront holds them in registers: the fp6
