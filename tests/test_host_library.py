@@ -294,7 +294,8 @@ def test_mx_blob_layout():
     """Codes and scales sit where the documented MXFP4 tiling says: for
     K-step s and tile t, lane l = row % 32 + 32 h holds the row's canonical
     bytes 32 s + 16 h + [0, 16) at ((s T + t) 64 + l) 16, and the E8M0 scale
-    of MX block 2 s + h at (s T + t) 64 + l of the scale array."""
+    of MX block 2 s + h at (s T + 4 (t // 4)) 64 + 4 l + t % 4 of the scale
+    array (byte t % 4 of the lane's word for its group of four tiles)."""
     c = synth.linear_case("mxpk", 92, 8, 100, 192, 5, x_outlier_n=2, x_outlier_scale=20.0)
     hw = S.mx_prepare_weights(c.W, c.calib_absmax(), c.bias, 5)
     blob = S.mx_pack_device_weights(hw)
@@ -310,10 +311,12 @@ def test_mx_blob_layout():
                 lane = n % 32 + 32 * h
                 base = ((s_ * T + n // 32) * 64 + lane) * 16
                 assert np.array_equal(q[base: base + 16], hw.qweight[n, 32 * s_ + 16 * h: 32 * s_ + 16 * h + 16])
-                assert sc[(s_ * T + n // 32) * 64 + lane] == hw.wscales[n, 2 * s_ + h]
+                t = n // 32
+                assert sc[(s_ * T + 4 * (t // 4)) * 64 + 4 * lane + t % 4] == hw.wscales[n, 2 * s_ + h]
     # padded rows: +0 codes and the smallest scale byte (0)
     assert not np.any(q.reshape(G, T, 64, 16)[:, 3, 4:32]) and not np.any(q.reshape(G, T, 64, 16)[:, 4:])
-    assert not np.any(sc.reshape(G, T, 64)[:, 4:])
+    sc4 = sc.reshape(G, T // 4, 64, 4)
+    assert not np.any(sc4[:, 1:]) and not np.any(sc4[:, 0, 4:32, 3]) and not np.any(sc4[:, 0, 36:, 3])
 
 
 # ---------------------------------------------------------------- errors

@@ -784,20 +784,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       else if (wu == 0) vmcnt_wait<4>();
       else vmcnt_wait<3>();
     };
+    // Scales: one word per lane for the workgroup's 4 A tiles (this
+    // wavefront's two moved to bytes 0 and 1) and one for its own 4 B tiles;
+    // the matrix instruction selects the tile's byte.
     v8i xa[WTM], xb[WTN];
-    int xsa[WTM], xsb[WTN];
+    int xsa, xsb;
     auto mx_load = [&](int g) {
       const uint8_t *st = stage_of(g);
 #pragma unroll
-      for (int i = 0; i < WTM; ++i) {
-        xa[i] = mx_frag(st + (WTM * wmi + i) * 1024, lane);
-        xsa[i] = st[12288 + (WTM * wmi + i) * 64 + lane];
-      }
+      for (int i = 0; i < WTM; ++i) xa[i] = mx_frag(st + (WTM * wmi + i) * 1024, lane);
 #pragma unroll
-      for (int j = 0; j < WTN; ++j) {
-        xb[j] = mx_frag(st + 4096 + (WTN * wni + j) * 1024, lane);
-        xsb[j] = st[12288 + 256 + (WTN * wni + j) * 64 + lane];
-      }
+      for (int j = 0; j < WTN; ++j) xb[j] = mx_frag(st + 4096 + (WTN * wni + j) * 1024, lane);
+      xsa = (int)(reinterpret_cast<const uint32_t *>(st + 12288)[lane] >> (16 * wmi));
+      xsb = (int)reinterpret_cast<const uint32_t *>(st + 12288 + 256 + 256 * wni)[lane];
     };
     mx_wait(G <= 2);
     __syncthreads();
@@ -808,12 +807,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __syncthreads();
         if (g + 3 < G) fetch_mx(g + 3);
       }
-#pragma unroll
-      for (int i = 0; i < WTM; ++i)
-#pragma unroll
-        for (int j = 0; j < WTN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa[i], xb[j], acc[i][j], 4, 4, 0,
-                                                                      xsa[i], 0, xsb[j]);
+      static_assert(WTM == 2 && WTN == 4, "scale bytes: two A tiles and four B tiles per wavefront");
+#define MX_MM(i, j)                                                                                    \
+  acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa[i], xb[j], acc[i][j], 4, 4, i, xsa, j, xsb)
+      MX_MM(0, 0); MX_MM(0, 1); MX_MM(0, 2); MX_MM(0, 3);
+      MX_MM(1, 0); MX_MM(1, 1); MX_MM(1, 2); MX_MM(1, 3);
+#undef MX_MM
       mx_load(g + 1);
     }
   } else {

@@ -131,14 +131,18 @@ struct WorkLayout {
 // lane l covers row l % 32 and the MX block h = l / 32 of the step, its 32
 // codes being channels 64 s + 32 h + [0, 32) in the canonical nibble order
 // (byte i = code 2i | code 2i+1 << 4), i.e. the row's canonical bytes
-// 32 s + 16 h + [0, 16).  The E8M0 scales of the same (s, t) follow as 64
-// bytes, one per lane, in a separate array.
+// 32 s + 16 h + [0, 16).  The E8M0 scales sit in a separate array, 64
+// bytes per (s, t), interleaved over 4 tiles: for the tiles 4q .. 4q + 3 of
+// step s, a 256-byte block holds one 32-bit word per lane whose byte i is
+// the lane's scale in tile 4q + i, so one word read gives a lane the scales
+// of four tiles and the matrix instruction picks the byte.  T (a multiple of
+// 8 after padding) keeps the blocks whole.
 constexpr int kMxBlock = 32;
 constexpr int64_t mx_code_offset(int64_t s, int64_t t, int64_t T, int lane) {
   return ((s * T + t) * 64 + lane) * 16;
 }
 constexpr int64_t mx_scale_offset(int64_t s, int64_t t, int64_t T, int lane) {
-  return (s * T + t) * 64 + lane;
+  return (s * T + (t & ~int64_t(3))) * 64 + lane * 4 + (t & 3);
 }
 
 struct MxWeightLayout {
