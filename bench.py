@@ -462,6 +462,107 @@ def config_sweep(args):
                           "k3_frac_hbm": round(nbytes / t3 / 1e3 / PEAK_HBM_GBS, 4)}), flush=True)
 
 
+def block_study(args):
+    """Launch study of one transformer block's calls into the library (not
+    the one-line contract): the AWQ modulation projection (1 x 3072 ->
+    18432), the QKV (3072 -> 9216) and output (3072 -> 3072) projections and
+    the fused MLP pair (3072 -> 12288 -> 3072), all rank 32, at 4608 and
+    1024 tokens.  The same sequence runs eagerly (every call launched from
+    Python through the C ABI) and as one captured HIP graph; each call is
+    also timed alone between events.  One JSON line per token count.
+    Attention sits between these calls in a real block and is not part of
+    this library, so it is left out."""
+    import numpy as np
+    import torch
+    import synth
+    import w4a4_rank_corrected_smooth_amd as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    S.device_check()
+    D, F = 3072, 12288
+    log("block study: preparing QKV, output projection, fc1, fc2 and AWQ on the host")
+    fc1c, W2, b2 = synth.mlp_cases()
+    qc = synth.qkv_case()
+    oc = synth.linear_case("out_proj", 6, 8, D, D, 32, x_outlier_frac=0.005, x_outlier_scale=50.0)
+    qkv = S.Linear(S.prepare_weights(qc.W, qc.calib_absmax(), qc.bias, 32), dev)
+    outp = S.Linear(S.prepare_weights(oc.W, oc.calib_absmax(), oc.bias, 32), dev)
+    fc1 = S.Linear(S.prepare_weights(fc1c.W, fc1c.calib_absmax(), fc1c.bias, 32), dev)
+    fc2 = S.Linear(S.prepare_weights(W2, None, b2, 32), dev)
+    a = synth.awq_case()
+    q, sc, z = S.awq_quantize_weights(a.W)
+    awq = S.AwqLinear(q, sc, z, dev)
+    x1 = torch.from_numpy(np.ascontiguousarray(a.x[:1])).to(dev)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    for M in (4608, 1024):
+        X = torch.from_numpy(np.ascontiguousarray(qc.X[:M]).view(np.int16)).view(torch.bfloat16).to(dev)
+        mod = torch.empty(1, a.N, dtype=torch.float16, device=dev)
+        Yq = torch.empty(M, 3 * D, dtype=torch.bfloat16, device=dev)
+        Yo = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
+        Ym = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
+        wq, wo = qkv.new_workspace(M), outp.new_workspace(M)
+        w1, w2 = fc1.new_workspace(M), fc2.new_workspace(M)
+        calls = [("awq_mod", lambda: S.awq_forward(awq, x1, out=mod)),
+                 ("qkv", lambda: S.linear_forward(qkv, X, out=Yq, workspace=wq)),
+                 ("out_proj", lambda: S.linear_forward(outp, X, out=Yo, workspace=wo)),
+                 ("mlp_pair", lambda: S.mlp_forward(fc1, fc2, X, out=Ym, ws1=w1, ws2=w2))]
+
+        def block():
+            for _, f in calls:
+                f()
+
+        stream = torch.cuda.current_stream(dev)
+        for _ in range(10):
+            block()
+        torch.cuda.synchronize()
+        n = args.steps
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(n):
+            block()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eager = e0.elapsed_time(e1) * 1e3 / n
+        per = {}
+        for name, f in calls:
+            ts = []
+            for _ in range(n):
+                a0, a1 = ev(), ev()
+                a0.record(stream)
+                f()
+                a1.record(stream)
+                ts.append((a0, a1))
+            torch.cuda.synchronize()
+            per[name] = round(float(np.median([u.elapsed_time(v) * 1e3 for u, v in ts])), 2)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            block()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            block()
+        for _ in range(5):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(n):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph = e0.elapsed_time(e1) * 1e3 / n
+        print(json.dumps({"study": "block", "tokens": M, "calls_per_block": len(calls), "kernels_per_block": 8,
+                          "eager_us": round(eager, 2), "graph_us": round(graph, 2),
+                          "per_call_event_us": per, "sum_per_call_us": round(sum(per.values()), 2)}), flush=True)
+        del g, X, Yq, Yo, Ym, wq, wo, w1, w2
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -483,6 +584,8 @@ def main():
                     help="CPU only: summarise rocprofv3 output into profiles/ and exit")
     ap.add_argument("--configs", action="store_true",
                     help="per-configuration kernel timings (one JSON line each) instead of the step")
+    ap.add_argument("--block", action="store_true",
+                    help="launch study of one transformer block's calls, eager and as a HIP graph")
     ap.add_argument("--summarize-configs", nargs=2, metavar=("TRACE_DIR", "SWEEP_JSONL"),
                     help="CPU only: summarise a rocprofv3 trace of --configs into profiles/ and exit")
     args = ap.parse_args()
@@ -506,6 +609,9 @@ def main():
 
     if args.configs:
         config_sweep(args)
+        return
+    if args.block:
+        block_study(args)
         return
 
     import numpy as np
