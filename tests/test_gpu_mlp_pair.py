@@ -60,7 +60,8 @@ def _regions(M, K, rank):
 
 CASES = [("ragged", 130, 256, 320, 200, 8, 5), ("tiles", 256, 512, 576, 384, 16, 32),
          ("one-row", 1, 64, 64, 64, 1, 1), ("rank0-next", 300, 192, 384, 96, 12, 0),
-         ("wide-rank", 200, 128, 256, 130, 40, 70)]
+         ("wide-rank", 200, 128, 256, 130, 40, 70),
+         ("split-fc2", 200, 256, 1024, 256, 8, 8)]        # fc2's GEMM is K-split (2 tiles, 16 groups)
 
 
 @pytest.mark.parametrize("name,M,K1,N1,N2,r1,r2", CASES)

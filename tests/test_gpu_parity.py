@@ -157,3 +157,42 @@ def test_gelu_kernel_within_one_bf16_ulp(S, n):
     tiny = (np.abs(ref) < 2.0 ** -100) & (np.abs(got) < 2.0 ** -100)
     assert np.all((np.abs(got - ref) <= ulp) | tiny)
     assert np.mean(got == ref) > 0.99
+
+
+# K-split of the GEMM: tile grids smaller than the chip's CU count run as
+# ksplit K ranges whose fp32 partial tiles a second kernel sums in order
+# (sizing rule: tiles T of 128 x 256 < 256 -> ksplit = min(8, 512 // T,
+# groups // 8) when that is at least 2).
+def ksplit_of(M, N, K):
+    T = -(-M // 128) * -(-N // 256)
+    if T >= 256:
+        return 1
+    s = min(8, 512 // T, K // 64 // 8)
+    return s if s >= 2 else 1
+
+
+@pytest.mark.parametrize("M,N,K,rank,out,gelu", [(100, 200, 1024, 8, torch.float32, False),
+                                                 (300, 600, 2048, 16, torch.float32, False),
+                                                 (129, 257, 4096, 32, torch.float32, False),
+                                                 (64, 512, 1600, 5, torch.bfloat16, True),
+                                                 (1, 3072, 12288, 32, torch.bfloat16, False)])
+def test_k_split_gemm(S, M, N, K, rank, out, gelu):
+    ks = ksplit_of(M, N, K)
+    assert ks >= 2
+    c = synth.linear_case(f"ks{M}x{N}x{K}", 500 + M, M, N, K, rank,
+                          x_outlier_n=max(1, K // 64), x_outlier_scale=40.0)
+    ref, f, layer, X, ws, Y = run_case(S, c, out_dtype=out, gelu=gelu, check_codes=False)
+    Yref = OG.gelu_tanh_bf16(f["Y"]) if gelu else f["Y"]
+    tol = TOL_BF16 if out == torch.bfloat16 else TOL_F32
+    err = np.max(np.abs(Y - Yref)) / np.max(np.abs(f["Y"]))
+    announce(f"k-split {ks} max err / max|Y| {err:.3e}")
+    assert err <= (1.13 * TOL_F32 + 2.0 ** -8 if gelu else tol)
+    # the same layer with a workspace one byte short of the partials' room
+    # runs the unsplit GEMM; both agree with the oracle and with each other
+    part = ks * (-(-M // 256) * 256) * (-(-N // 256) * 256) * 4
+    small = torch.empty(ws.numel() - part, dtype=torch.uint8, device=ws.device)
+    Y1 = to_f64(S.linear_forward(layer, X, out_dtype=out, gelu=gelu, workspace=small))
+    torch.cuda.synchronize()
+    err1 = np.max(np.abs(Y1 - Yref)) / np.max(np.abs(f["Y"]))
+    assert err1 <= (1.13 * TOL_F32 + 2.0 ** -8 if gelu else tol)
+    assert np.max(np.abs(Y1 - Y)) / np.max(np.abs(f["Y"])) <= 2 * tol

@@ -510,3 +510,27 @@ def test_merge_lora_copies_into_separate_buffers_and_errors():
                                ctypes.byref(alias)) == INV
     with pytest.raises(ValueError):
         S.merge_lora(hw, A, B[:, :2])
+
+
+def test_workspace_includes_k_split_partials():
+    """svdq_workspace_bytes adds ksplit * Mp * Np * 4 bytes of fp32 partial
+    tiles exactly when the GEMM's 128 x 256 tile grid has fewer than 256
+    tiles (ksplit = min(8, 512 // tiles, groups // 8) >= 2)."""
+    lib = S._lib
+    up = lambda x: -(-x // 256) * 256
+    def base(M, K, r):
+        Mp, G, rp = up(M), K // 64, -(-r // 32) * 32 if r else 0
+        T = Mp // 32
+        Ssp = 1
+        for s_ in range(1, G + 1):
+            if G % s_:
+                continue
+            if s_ == 1 or G // s_ >= 4:
+                Ssp = s_
+            if G // s_ >= 4 and T * s_ >= 384:
+                break
+        return up(Mp * K * 3 // 4) + up(G * Mp * 4) + up(max(Ssp, 2) * Mp * rp * 4)
+    for M, N, K, r, ks in [(4608, 12288, 3072, 32, 1), (1024, 3072, 3072, 128, 5), (100, 200, 1024, 8, 2),
+                           (1, 3072, 12288, 32, 8), (64, 512, 448, 4, 1), (4608, 3072, 12288, 32, 1)]:
+        want = base(M, K, r) + (ks * up(M) * up(N) * 4 if ks > 1 else 0)
+        assert lib.svdq_workspace_bytes(M, N, K, r) == want, (M, N, K, r)

@@ -242,7 +242,7 @@ size_t svdq_mx_workspace_bytes(int M, int N, int K, int rank) {
 size_t svdq_workspace_bytes(int M, int N, int K, int rank) {
   svdq_status_t st;
   if (M < 1 || !shape_ok(N, K, rank, "svdq_workspace_bytes", &st)) return 0;
-  return (size_t)WorkLayout(M, K, rank).total;
+  return (size_t)(WorkLayout(M, K, rank).total + k2_split_bytes(M, N, K));
 }
 
 svdq_status_t awq_quantize_weights(const uint16_t *W, int N, int K, int group_size, uint8_t *q,

@@ -421,12 +421,15 @@ struct K2Args {
   int G2, rp2;
   // MXFP4 (MODE_MX): qa / qw hold E2M1 codes, these the E8M0 block scales
   const uint8_t *sqa; const uint8_t *sqw;
+  // K-split (SPLIT): ksplit ranges of groups, fp32 partial tiles [ksplit][Mp][Np]
+  int ksplit; float *part;
 };
 
 namespace k2c {
 constexpr int WTM = 2, WTN = 4;                   // MFMA tiles per wavefront (rows, columns)
 constexpr int WROWS = 32 * WTM, WCOLS = 32 * WTN; // 64 x 128
 constexpr int BM = 2 * WROWS, BN = 2 * WCOLS, THREADS = 256, NWAVES = THREADS / 64;
+static_assert(BM == kK2TileM && BN == kK2TileN, "the K-split sizing uses the workgroup tile");
 constexpr int A_BLK = BM / kTile, B_BLK = BN / kTile;
 constexpr int A_BYTES = A_BLK * kBlockBytes;     // one group per stage
 constexpr int B_BYTES = B_BLK * kBlockBytes;
@@ -500,14 +503,19 @@ __device__ __forceinline__ void k2_order_r() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int MODE, int EPI, bool OUT_F32, bool DFIX = false, bool QNEXT = false>
+template <int MODE, int EPI, bool OUT_F32, bool DFIX = false, bool QNEXT = false, bool SPLIT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_w4a4_gemm(K2Args p) {
   using namespace k2c;
-  // ---- tile of this workgroup (XCD-aware, grouped)
+  static_assert(!SPLIT || (MODE == MODE_FWD && !QNEXT), "K-split: plain INT4 forward only");
+  // ---- tile of this workgroup (XCD-aware, grouped); with a K-split,
+  // consecutive workgroups on one XCD take different tiles of one K range
   const int T = p.TM * p.TN;
-  const int per_xcd = (T + 7) / 8;
-  const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (L >= T) return;
+  const int TS = SPLIT ? T * p.ksplit : T;
+  const int per_xcd = (TS + 7) / 8;
+  const int L0 = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (L0 >= TS) return;
+  const int split = SPLIT ? L0 / T : 0;
+  const int L = SPLIT ? L0 - split * T : L0;
   const int band = L / (GM * p.TN);
   const int first_m = band * GM;
   const int gm = min(GM, p.TM - first_m);
@@ -520,7 +528,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int wu = __builtin_amdgcn_readfirstlane(w);      // wavefront index, scalar
   const int wmi = wu >> 1, wni = wu & 1;
   const int wm = bm + WROWS * wmi, wn = bn + WCOLS * wni;
-  const int G = p.K / kGroup;
+  // groups [g0, g0 + G) of the K range (all of K without a split)
+  const int Gall = p.K / kGroup;
+  const int g0 = SPLIT ? split * Gall / p.ksplit : 0;
+  const int G = SPLIT ? (split + 1) * Gall / p.ksplit - g0 : Gall;
   const int Ta = p.Mp / kTile, Tw = p.Np / kTile;
   const int hl = lane >> 5, ln = lane & 31;
 
@@ -556,6 +567,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       sbase[r] = reinterpret_cast<const uint8_t *>(p.sa + bm);
       sstride[r] = (int64_t)p.Mp * 4;
     }
+    if constexpr (SPLIT) sbase[r] += g0 * sstride[r];   // loop indices count from g0
   }
   const uint32_t voff = 16u * lane;
   const uint32_t voff_sa = 16u * (lane & 31);     // sA is half a load
@@ -684,7 +696,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if constexpr (MODE == MODE_MX) fetch_mx(g); else fetch(g);
   }
   if constexpr (MODE == MODE_FWD || MODE == MODE_MX) {
-    // Low-rank up-projection first, while the first stages are in flight:
+    // Low-rank up-projection first, while the first stages are in flight
+    // (with a K-split, the 32-rank chunks are dealt round the ranges, so
+    // each range's partial carries some of them and no range waits on all):
     // acc = D L2 on bf16 matrix cores, D entered as a bf16 high part plus a
     // bf16 remainder.  D of the workgroup's 128 rows is assembled once, in
     // the fourth stage buffer (free until the main loop starts), 32 ranks at
@@ -697,7 +711,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     uint16_t *dlo = dhi + BM * 32;                                     // [BM][32]
     static_assert(BM * 32 * 2 * 2 <= STAGE, "low-rank staging fits one stage buffer");
     const int rloc = 32 * wu + (lane >> 1), k0 = 16 * (lane & 1);
-    for (int c2 = 0; c2 < p.rp / 32; ++c2) {
+    for (int c2 = split; c2 < p.rp / 32; c2 += SPLIT ? p.ksplit : 1) {
       float d[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) d[e] = 0.f;
@@ -872,7 +886,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   }  // INT4 main loop
 
-  if constexpr (MODE == MODE_FWD && QNEXT) {
+  if constexpr (SPLIT) {
+    // K-split: the fp32 partial tile, padded rows and columns included (the
+    // partial buffer is [Mp][Np]); bias and the epilogue come in the sum.
+    float *pp = p.part + (int64_t)split * p.Mp * p.Np;
+#pragma unroll
+    for (int i = 0; i < WTM; ++i)
+#pragma unroll
+      for (int j = 0; j < WTN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = wm + 32 * i + 8 * (e >> 2) + 4 * hl + (e & 3), n = wn + 32 * j + ln;
+          pp[(int64_t)m * p.Np + n] = acc[i][j][e];
+        }
+  } else if constexpr (MODE == MODE_FWD && QNEXT) {
     // MLP pair: this layer's output never goes to memory.  Bias (+ GELU),
     // rounded to bf16 (exactly the values the unfused path stores), then the
     // next layer's quantiser runs on the tile: every (32-row tile, group of 64
@@ -1051,6 +1078,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+  }
+}
+
+// Sum of a K-split GEMM's partial tiles, in range order, + bias (+ GELU),
+// stored as Y.  Thread: 4 consecutive columns of one row.
+template <int EPI, bool OUT_F32>
+__global__ __launch_bounds__(256) void k2_split_sum(const float *__restrict__ part, int ksplit, int M,
+                                                    int N, int Mp, int Np, const float *__restrict__ bias,
+                                                    void *__restrict__ Y) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int nq = Np / 4;
+  const int64_t m = idx / nq;
+  const int n0 = (int)(idx - m * nq) * 4;
+  if (m >= M || n0 >= N) return;
+  const float *src = part + m * Np + n0;
+  float4 acc = *reinterpret_cast<const float4 *>(src);
+  for (int k = 1; k < ksplit; ++k) {
+    const float4 v = *reinterpret_cast<const float4 *>(src + (int64_t)k * Mp * Np);
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  const float a4[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int n = n0 + t;
+    if (n >= N) break;
+    float y = a4[t] + bias[n];
+    if constexpr (EPI == SVDQ_EPILOGUE_GELU_TANH) y = gelu_tanh_f32(y);
+    if constexpr (OUT_F32)
+      reinterpret_cast<float *>(Y)[m * N + n] = y;
+    else
+      reinterpret_cast<__bf16 *>(Y)[m * N + n] = (__bf16)y;
   }
 }
 
@@ -1540,7 +1598,7 @@ enum K2In { K2_D_PARTIALS = 0, K2_D_FIXED = 1 };
 static svdq_status_t launch_k2(const svdq_weights_t *w, int M, void *Y, svdq_dtype_t y_dtype,
                                svdq_epilogue_t epilogue, const void *workspace, hipStream_t stream,
                                K2In din = K2_D_PARTIALS, const svdq_weights_t *w2 = nullptr,
-                               void *ws2 = nullptr) {
+                               void *ws2 = nullptr, size_t ws_bytes = 0) {
   const WeightLayout L(w->N, w->K, w->rank);
   const WorkLayout Wl(M, w->K, w->rank);
   K2Args a = make_k2_args(L, Wl, w, M, static_cast<const uint8_t *>(workspace));
@@ -1561,11 +1619,35 @@ static svdq_status_t launch_k2(const svdq_weights_t *w, int M, void *Y, svdq_dty
     a.G2 = (int)W2.G;
     a.rp2 = (int)W2.rp;
   }
-  const dim3 grid((unsigned)round_up((int64_t)a.TM * a.TN, 8));
   const dim3 block(k2c::THREADS);
   const bool f32 = y_dtype == SVDQ_FP32;
   const bool gelu = epilogue == SVDQ_EPILOGUE_GELU_TANH;
   constexpr int NONE = SVDQ_EPILOGUE_NONE, GELU = SVDQ_EPILOGUE_GELU_TANH;
+  // K-split when the tile grid leaves the chip idle and the workspace has
+  // room for the partials (svdq_workspace_bytes includes it)
+  const int ks = (int)k2_ksplit(M, w->N, w->K);
+  if (!w2 && ks > 1 && (int64_t)ws_bytes >= Wl.total + k2_split_bytes(M, w->N, w->K)) {
+    a.ksplit = ks;
+    a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(const_cast<void *>(workspace)) + Wl.total);
+    const dim3 sgrid((unsigned)round_up((int64_t)a.TM * a.TN * ks, 8));
+    if (din == K2_D_FIXED)
+      hipLaunchKernelGGL((k2_w4a4_gemm<MODE_FWD, NONE, true, true, false, true>), sgrid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((k2_w4a4_gemm<MODE_FWD, NONE, true, false, false, true>), sgrid, block, 0, stream, a);
+    svdq_status_t st = launch_status("GEMM kernel launch");
+    if (st != SVDQ_OK) return st;
+    const int64_t threads = (int64_t)M * (L.Np / 4);
+    const dim3 rgrid((unsigned)((threads + 255) / 256));
+#define K2_SUM(E, F) hipLaunchKernelGGL((k2_split_sum<E, F>), rgrid, dim3(256), 0, stream, a.part, ks, M, \
+                                        w->N, (int)Wl.Mp, (int)L.Np, a.bias, Y)
+    if (!gelu && f32) K2_SUM(NONE, true);
+    else if (!gelu) K2_SUM(NONE, false);
+    else if (f32) K2_SUM(GELU, true);
+    else K2_SUM(GELU, false);
+#undef K2_SUM
+    return launch_status("K-split sum launch");
+  }
+  const dim3 grid((unsigned)round_up((int64_t)a.TM * a.TN, 8));
 #define K2_GO(E, F, DF, QN) hipLaunchKernelGGL((k2_w4a4_gemm<MODE_FWD, E, F, DF, QN>), grid, block, 0, stream, a)
   if (w2) {
     if (din == K2_D_FIXED) return fail(SVDQ_ERR_INVALID_ARGUMENT, "chained fused epilogues are not supported");
@@ -1605,7 +1687,8 @@ svdq_status_t svdq_linear_gemm(const svdq_weights_t *w, int M, void *Y, svdq_dty
   if (st != SVDQ_OK) return st;
   if ((st = validate_output(Y, y_dtype, epilogue, "svdq_linear_gemm")) != SVDQ_OK) return st;
   if ((st = check_device()) != SVDQ_OK) return st;
-  return launch_k2(w, M, Y, y_dtype, epilogue, workspace, static_cast<hipStream_t>(hip_stream));
+  return launch_k2(w, M, Y, y_dtype, epilogue, workspace, static_cast<hipStream_t>(hip_stream),
+                   K2_D_PARTIALS, nullptr, nullptr, ws_bytes);
 }
 
 svdq_status_t svdq_linear_forward(const svdq_weights_t *w, const void *X, int M, void *Y,
@@ -1622,7 +1705,8 @@ svdq_status_t svdq_linear_forward(const svdq_weights_t *w, const void *X, int M,
   const WorkLayout Wl(M, w->K, w->rank);
   if ((st = launch_k1(L, Wl, w, X, M, static_cast<uint8_t *>(workspace), stream)) != SVDQ_OK)
     return st;
-  return launch_k2(w, M, Y, y_dtype, epilogue, workspace, stream);
+  return launch_k2(w, M, Y, y_dtype, epilogue, workspace, stream, K2_D_PARTIALS, nullptr, nullptr,
+                   ws_bytes);
 }
 
 static svdq_status_t validate_pair(const svdq_weights_t *w1, const svdq_weights_t *w2, int M,
@@ -1671,7 +1755,7 @@ svdq_status_t svdq_mlp_gemm2(const svdq_weights_t *w2, int M, void *Y, svdq_dtyp
   if ((st = validate_output(Y, y_dtype, SVDQ_EPILOGUE_NONE, "svdq_mlp_gemm2")) != SVDQ_OK) return st;
   if ((st = check_device()) != SVDQ_OK) return st;
   return launch_k2(w2, M, Y, y_dtype, SVDQ_EPILOGUE_NONE, ws2, static_cast<hipStream_t>(hip_stream),
-                   K2_D_FIXED);
+                   K2_D_FIXED, nullptr, nullptr, ws2_bytes);
 }
 
 svdq_status_t svdq_mlp_forward(const svdq_weights_t *w1, const svdq_weights_t *w2, const void *X,

@@ -125,6 +125,27 @@ struct WorkLayout {
   }
 };
 
+// K-split of the INT4 GEMM.  A grid of fewer workgroup tiles (128 x 256)
+// than CUs leaves most of the chip idle; such a GEMM is split along K into
+// up to 8 ranges of at least 8 groups each, aiming at about 512 workgroups.
+// Each range's fp32 partial tile goes to the workspace ([ksplit][Mp][Np]
+// after the quantiser's part), and a second kernel sums the ranges in order
+// and adds the bias (+ GELU).
+constexpr int kK2TileM = 128, kK2TileN = 256;
+constexpr int64_t k2_ksplit(int64_t M, int64_t N, int64_t K) {
+  const int64_t T = ((M + kK2TileM - 1) / kK2TileM) * ((N + kK2TileN - 1) / kK2TileN);
+  if (T >= 256) return 1;
+  int64_t s = 512 / T;
+  if (s > 8) s = 8;
+  if (s > K / kGroup / 8) s = K / kGroup / 8;
+  return s >= 2 ? s : 1;
+}
+// bytes of the K-split partials after the quantiser's part of the workspace
+constexpr int64_t k2_split_bytes(int64_t M, int64_t N, int64_t K) {
+  const int64_t s = k2_ksplit(M, N, K);
+  return s > 1 ? s * round_up(M, kPad) * round_up(N, kPad) * 4 : 0;
+}
+
 // MXFP4 device layouts (the FP4 form of the 4-bit path).  A K-step of 64
 // input channels is one block-scaled FP4 matrix instruction: for every
 // (K-step s, tile t of 32 rows) a 1 KB code block holds 16 bytes per lane;
