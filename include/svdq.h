@@ -174,7 +174,14 @@ typedef struct {
 
 /* =================================================== runtime, device, async */
 
-/* Device scratch needed by svdq_linear_forward for M token rows. */
+/* Device scratch needed by svdq_linear_forward for M token rows.  When the
+ * GEMM's grid of 128 x 256 output tiles has fewer than 256 tiles (the chip
+ * has 256 CUs), the GEMM is split along K into ksplit = min(8, 512 / tiles,
+ * (K / 64) / 8) ranges (if that is at least 2) whose fp32 partial tiles a
+ * second kernel sums in range order, and the size includes ksplit * Mp * Np
+ * * 4 bytes for them (Mp, Np: M and N rounded up to 256).  A workspace
+ * without that room is still accepted; the GEMM then runs unsplit (the same
+ * result up to the order of fp32 additions). */
 size_t svdq_workspace_bytes(int M, int N, int K, int rank);
 
 /* Y = linear(X) [+ epilogue] for X bf16 [M, K] (device, row-major) into
