@@ -19,5 +19,6 @@ from .gen import (  # noqa: F401
     awq_case,
     on_grid_case,
     lora_factors,
+    device_normal_bf16,
     WORKLOADS,
 )

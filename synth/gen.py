@@ -167,6 +167,26 @@ def lora_factors(seed: int, N: int, K: int, rank: int, a_std: float = 0.02,
     return f32_to_bf16_bits(A), f32_to_bf16_bits(B)
 
 
+def device_normal_bf16(M: int, K: int, seed: int, device, outlier_n: int = 0,
+                       outlier_scale: float = 1.0):
+    """Activations too large to draw on the host: N(0, 1) float32 from
+    torch's generator on `device` (seeded), `outlier_n` channels (drawn with
+    numpy's PCG64 from the same seed) scaled in float32, then rounded to
+    bf16 (torch's cast: nearest, ties to even).  Returns (X bf16 tensor
+    [M, K] on the device, outlier channel indices)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    X = torch.randn(M, K, generator=g, device=device, dtype=torch.float32)
+    rng = np.random.default_rng(seed)
+    idx = np.sort(rng.choice(K, outlier_n, replace=False)) if outlier_n > 0 else np.zeros(0, np.int64)
+    if outlier_n > 0:
+        X[:, torch.from_numpy(idx).to(device)] *= outlier_scale
+    Xb = X.to(torch.bfloat16)
+    del X
+    return Xb, idx
+
+
 def on_grid_case(seed: int, M: int, N: int, K: int, exp_lo: int = 0, exp_hi: int = 0,
                  group: int = 64) -> LinearCase:
     """Activations and weights that already lie on the signed INT4 grid: every

@@ -214,3 +214,41 @@ def test_awq_ragged_with_bias(S, M, N, K):
                              bias=torch.from_numpy(bias).to("cuda")))
     yref = OA.forward(a.x, q, s, z, bias.astype(np.float64))
     assert rel_max_err(y, yref) <= 2e-3 + 2.0 ** -11
+
+
+# ------------------------------------------------------- largest input
+def test_largest_input_accepted(S):
+    """M * K = 2^31, the largest input the C ABI accepts (131072 tokens x
+    16384 channels, 4 GiB of bf16 activations; N = 256, r = 16): codes,
+    scales, the down-projection and Y on sampled rows, the first and last
+    rows among them; one row more is rejected before any launch."""
+    M, N, K, r = 131072, 256, 16384, 16
+    assert M * K == 2 ** 31
+    dev = torch.device("cuda")
+    announce(f"largest: drawing X {M}x{K} on the device")
+    X, _ = synth.device_normal_bf16(M, K, 800, dev, outlier_n=64, outlier_scale=40.0)
+    w = synth.linear_case("largest_w", 801, 8, N, K, r)
+    ax = O.calibration_absmax(X[:64].float().cpu().numpy())
+    announce("largest: oracle prepare 256x16384 r16")
+    ref = O.prepare(w.W, ax, w.bias, r)
+    layer = layer_from_oracle(ref)
+    ws = layer.new_workspace(M)
+    announce(f"largest: device forward, workspace {ws.numel() / 2**30:.2f} GiB")
+    Y = S.linear_forward(layer, X, out_dtype=torch.bfloat16, workspace=ws)
+    q, s, d = S.quantize_activations(layer, X, ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(802)
+    rows = np.unique(np.concatenate([[0, 1, M // 2, M - 2, M - 1], rng.choice(M, 40, replace=False)]))
+    ridx = torch.from_numpy(rows).to(dev)
+    Xr = X[ridx].cpu().view(torch.int16).numpy().view(np.uint16)
+    f = O.forward(ref, Xr)
+    assert np.array_equal(q[ridx].cpu().numpy(), O.pack_int4(f["qA"])), "activation codes"
+    assert np.array_equal(s[ridx].cpu().numpy(), f["sA"]), "activation scales"
+    assert rel_max_err(to_f64(d[ridx]), f["D"]) <= 1e-5, "low-rank down-projection"
+    err = rel_max_err(to_f64(Y[ridx]), f["Y"])
+    announce(f"largest max rel err {err:.3e}")
+    assert err <= TOL_BF16
+    import ctypes
+    st = S._lib.svdq_linear_forward(ctypes.byref(layer._w), X.data_ptr(), M + 1, Y.data_ptr(), S.BF16, 0,
+                                    ws.data_ptr(), ws.numel(), None)
+    assert st == 2, "one row past M * K = 2^31 is an unsupported shape"

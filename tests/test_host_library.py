@@ -361,6 +361,7 @@ def test_forward_validation_errors():
     assert call(X=None) == INV
     assert call(X=FAKE + 4) == INV                 # misaligned
     assert call(M=0) == SHAPE
+    assert call(M=(1 << 31) // 128 + 1, wsb=1 << 40) == SHAPE      # M * K past 2^31
     assert call(dt=S.FP16) == INV
     assert call(epi=7) == INV
     assert call(wsb=ws - 1) == WS
