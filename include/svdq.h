@@ -175,7 +175,7 @@ typedef struct {
 /* =================================================== runtime, device, async */
 
 /* Device scratch needed by svdq_linear_forward for M token rows.  When the
- * GEMM's grid of 128 x 256 output tiles has fewer than 256 tiles (the chip
+ * GEMM's grid of 128 x 256 output tiles has fewer than 128 tiles (the chip
  * has 256 CUs), the GEMM is split along K into ksplit = min(8, 512 / tiles,
  * (K / 64) / 8) ranges (if that is at least 2) whose fp32 partial tiles a
  * second kernel sums in range order, and the size includes ksplit * Mp * Np

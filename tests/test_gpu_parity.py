@@ -161,11 +161,11 @@ def test_gelu_kernel_within_one_bf16_ulp(S, n):
 
 # K-split of the GEMM: tile grids smaller than the chip's CU count run as
 # ksplit K ranges whose fp32 partial tiles a second kernel sums in order
-# (sizing rule: tiles T of 128 x 256 < 256 -> ksplit = min(8, 512 // T,
+# (sizing rule: tiles T of 128 x 256 < 128 -> ksplit = min(8, 512 // T,
 # groups // 8) when that is at least 2).
 def ksplit_of(M, N, K):
     T = -(-M // 128) * -(-N // 256)
-    if T >= 256:
+    if T >= 128:
         return 1
     s = min(8, 512 // T, K // 64 // 8)
     return s if s >= 2 else 1

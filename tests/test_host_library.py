@@ -515,8 +515,9 @@ def test_merge_lora_copies_into_separate_buffers_and_errors():
 
 def test_workspace_includes_k_split_partials():
     """svdq_workspace_bytes adds ksplit * Mp * Np * 4 bytes of fp32 partial
-    tiles exactly when the GEMM's 128 x 256 tile grid has fewer than 256
-    tiles (ksplit = min(8, 512 // tiles, groups // 8) >= 2)."""
+    tiles exactly when the GEMM's 128 x 256 tile grid has fewer than 128
+    tiles (ksplit = min(8, 512 // tiles, groups // 8) >= 2) and not from
+    128 tiles on."""
     lib = S._lib
     up = lambda x: -(-x // 256) * 256
     def base(M, K, r):
@@ -532,6 +533,7 @@ def test_workspace_includes_k_split_partials():
                 break
         return up(Mp * K * 3 // 4) + up(G * Mp * 4) + up(max(Ssp, 2) * Mp * rp * 4)
     for M, N, K, r, ks in [(4608, 12288, 3072, 32, 1), (1024, 3072, 3072, 128, 5), (100, 200, 1024, 8, 2),
-                           (1, 3072, 12288, 32, 8), (64, 512, 448, 4, 1), (4608, 3072, 12288, 32, 1)]:
+                           (1, 3072, 12288, 32, 8), (64, 512, 448, 4, 1), (4608, 3072, 12288, 32, 1),
+                           (512, 9216, 3072, 32, 1), (512, 3072, 3072, 32, 6)]:
         want = base(M, K, r) + (ks * up(M) * up(N) * 4 if ks > 1 else 0)
         assert lib.svdq_workspace_bytes(M, N, K, r) == want, (M, N, K, r)
