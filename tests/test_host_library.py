@@ -537,3 +537,19 @@ def test_workspace_includes_k_split_partials():
                            (512, 9216, 3072, 32, 1), (512, 3072, 3072, 32, 6)]:
         want = base(M, K, r) + (ks * up(M) * up(N) * 4 if ks > 1 else 0)
         assert lib.svdq_workspace_bytes(M, N, K, r) == want, (M, N, K, r)
+
+
+def test_package_refuses_to_load_without_the_library(tmp_path):
+    """The product path has no fallback: a copy of the package without
+    libsvdq.so fails at import with an error that names the missing file."""
+    import shutil
+    import subprocess
+    import sys
+    src = os.path.join(ROOT, "w4a4_rank_corrected_smooth_amd")
+    dst = tmp_path / "w4a4_rank_corrected_smooth_amd"
+    shutil.copytree(src, dst, ignore=shutil.ignore_patterns("*.so", "*.so.*", "__pycache__", "csrc"))
+    r = subprocess.run([sys.executable, "-c", "import w4a4_rank_corrected_smooth_amd"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=300,
+                       env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libsvdq.so" in r.stderr and "missing" in r.stderr
