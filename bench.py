@@ -196,6 +196,53 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir, command, run_lo
 CALIBRATION_BYTES = 256 << 20
 
 
+SQ_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+               "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU")
+
+
+def summarize_counters(pmc_dir, out_path, command):
+    """Per-kernel shader counters (one rocprofv3 --pmc pass of the default
+    profile command), averaged over each kernel's dispatches, with the clock
+    and the vector-ALU and matrix-pipe occupancy they imply."""
+    import csv
+    import glob
+    from collections import defaultdict
+    import numpy as np
+    path = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)[0]
+    vals = defaultdict(lambda: defaultdict(list))
+    durs = defaultdict(dict)
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        if not any(k in name for k in ("k1_quantize", "k2_w4a4", "k3_awq")):
+            continue
+        vals[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        durs[name][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    simds, xcds = 1024, 8
+    lines = ["# Shader counters per kernel, Flux MLP pair 4608x3072x12288 r32 + AWQ 1x3072x18432", "",
+             "Command:", "", "```", command, "```", "",
+             "Means over each kernel's dispatches.  cycles = GRBM_GUI_ACTIVE / 8 XCDs (the GPU's busy "
+             "cycles while the kernel runs; for kernels of a few microseconds they include the counter "
+             "pass's own start-up).  VALU busy = (SQ_INSTS_VALU - SQ_INSTS_MFMA) x 4 cycles (a wave64 "
+             "vector instruction holds its SIMD 4 cycles) / (1024 SIMDs x cycles); matrix busy = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles).  Durations come from the counter pass, "
+             "which runs slower than a plain trace.", "",
+             "| kernel | dispatches | us | cycles | " + " | ".join(SQ_COUNTERS[1:]) + " | VALU busy | matrix busy |",
+             "|---|---:|---:|---:|" + "---:|" * (len(SQ_COUNTERS) - 1) + "---:|---:|"]
+    for name in sorted(vals):
+        v = {c: float(np.mean(vals[name][c])) for c in SQ_COUNTERS if vals[name][c]}
+        if len(v) < len(SQ_COUNTERS):
+            continue
+        d = float(np.mean(list(durs[name].values())))
+        cyc = v["GRBM_GUI_ACTIVE"] / xcds
+        valu = (v["SQ_INSTS_VALU"] - v["SQ_INSTS_MFMA"]) * 4 / (simds * cyc)
+        mfma = v["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * cyc)
+        lines.append(f"| `{name}` | {len(durs[name])} | {d:.1f} | {cyc:.4g} | " +
+                     " | ".join(f"{v[c]:.4g}" for c in SQ_COUNTERS[1:]) + f" | {valu:.0%} | {mfma:.0%} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_configs(trace_dir, sweep_jsonl, out_path, command):
     """Exact per-configuration kernel durations from a rocprofv3 kernel trace
     of ``bench.py --configs``: the sweep launches each timed kernel 8 + steps
@@ -588,6 +635,8 @@ def main():
                     help="CPU only: summarise rocprofv3 output into profiles/ and exit")
     ap.add_argument("--configs", action="store_true",
                     help="per-configuration kernel timings (one JSON line each) instead of the step")
+    ap.add_argument("--summarize-counters", metavar="PMC_DIR",
+                    help="CPU only: summarise a rocprofv3 --pmc pass of the shader counters into profiles/")
     ap.add_argument("--block", action="store_true",
                     help="launch study of one transformer block's calls, eager and as a HIP graph")
     ap.add_argument("--summarize-configs", nargs=2, metavar=("TRACE_DIR", "SWEEP_JSONL"),
@@ -597,6 +646,11 @@ def main():
         t, j = args.summarize_configs
         summarize_configs(t, j, os.path.join(ROOT, "profiles", "kernels_all_configs.md"),
                           f"rocprofv3 --kernel-trace --stats -f csv -d {t} -- python3 bench.py --configs")
+        return
+    if args.summarize_counters:
+        base = "python3 bench.py --no-cpu-baseline --calibration-copy --skip-unfused --skip-mx"
+        summarize_counters(args.summarize_counters, os.path.join(ROOT, "profiles", "shader_counters_flux_mlp_pair.md"),
+                           f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} -f csv -d {args.summarize_counters} -- {base}")
         return
     if args.summarize_profile:
         t, fe, wr = args.summarize_profile
