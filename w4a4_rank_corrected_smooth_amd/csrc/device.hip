@@ -1150,12 +1150,15 @@ __device__ __forceinline__ void awq_group(const uint16_t *xg, uint32_t w0, uint3
   const _Float16 off = -((_Float16)1024.0f + zf);
   const v2h off2 = v2h{off, off};
   v8h bop[2];
+  const uint32_t magic = 0x64006400u;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const uint32_t word = half ? w1 : w0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t pr = ((word >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+      // (word >> 4j) & 0x000F000F | 0x64006400 in one vector instruction
+      uint32_t pr;
+      asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(pr) : "v"(word >> (4 * j)), "s"(0x000F000Fu), "v"(magic));
       const v2h v = __builtin_bit_cast(v2h, pr) + off2;
       bop[half][2 * j] = v.x;
       bop[half][2 * j + 1] = v.y;
