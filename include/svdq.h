@@ -351,6 +351,11 @@ svdq_status_t awq_quantize_weights(const uint16_t *W_fp16, int N, int K,
                                    int group_size, uint8_t *q,
                                    uint16_t *scales_fp16, uint16_t *zeros_fp16);
 
+/* Device blob of AWQ weights (host memory, caller-allocated, `bytes` >=
+ * awq_device_weights_bytes).  Zero points must be integers in 0..15 (the
+ * kernel forms q - z exactly in fp16 from that range) and scales finite:
+ * otherwise SVDQ_ERR_INVALID_ARGUMENT (zero point) or SVDQ_ERR_NUMERICAL
+ * (scale), and nothing is written. */
 size_t awq_device_weights_bytes(int N, int K);
 svdq_status_t awq_pack_device_weights(const uint8_t *q, const uint16_t *scales_fp16,
                                       const uint16_t *zeros_fp16, int N, int K,

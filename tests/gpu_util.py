@@ -45,3 +45,54 @@ def mx_host_from_oracle(ref: dict):
 def mx_layer_from_oracle(ref: dict, device="cuda"):
     import w4a4_rank_corrected_smooth_amd as S
     return S.MxLinear(mx_host_from_oracle(ref), device)
+
+
+def _up256(x: int) -> int:
+    return -(-x // 256) * 256
+
+
+def workspace_regions(M: int, K: int):
+    """Byte offsets of the INT4 workspace's code and scale regions (the
+    device layout: fp6 code blocks [G][Mp/32] x 1536, then fp32 scales
+    [G][Mp], each region 256-byte aligned)."""
+    Mp, G = _up256(M), K // 64
+    sa_off = _up256(Mp * K * 3 // 4)
+    d_off = _up256(sa_off + G * Mp * 4)
+    return Mp, G, sa_off, d_off
+
+
+def decode_fp6_codes(ws: np.ndarray, M: int, K: int) -> np.ndarray:
+    """INT4 activation codes [M, K] (int) from a workspace's fp6 blocks.
+
+    Test-side reader of the documented layout: for every (group g, tile t
+    of 32 rows) a 1536-byte block; lane l covers row 32 t + l % 32 and half
+    h = l / 32 of the group; its 8-byte word pair j (j = 0..2) sits at byte
+    512 j + 8 l; its code c occupies bits 6c..6c+5 of the 24 bytes and is
+    input channel 64 g + 16 (c / 8) + 8 h + c % 8, an OCP FP6 E2M3 value
+    (sign bit 5, exponent bits 4..3 with bias 1, mantissa bits 2..0)."""
+    Mp, G, _, _ = workspace_regions(M, K)
+    T = Mp // 32
+    raw = np.asarray(ws[: G * T * 1536], dtype=np.uint8).reshape(G, T, 3, 64, 8)
+    lane_bytes = raw.transpose(0, 1, 3, 2, 4).reshape(G, T, 64, 24)
+    bits = np.unpackbits(lane_bytes, axis=-1, bitorder="little").reshape(G, T, 64, 32, 6)
+    v = (bits.astype(np.int64) << np.arange(6)).sum(axis=-1)          # fp6 code
+    e, m = (v >> 3) & 3, v & 7
+    mag = np.where(e == 0, m / 8.0, (1.0 + m / 8.0) * np.exp2(e - 1.0))
+    val = np.where(v & 0x20, -mag, mag)
+    out = np.zeros((Mp, K), np.float64)
+    lane = np.arange(64)
+    c = np.arange(32)
+    rows = (np.arange(T)[:, None, None] * 32 + (lane % 32)[None, :, None])      # [T, 64, 1]
+    for g in range(G):
+        ks = 64 * g + 16 * (c[None, :] // 8) + 8 * (lane[:, None] // 32) + c[None, :] % 8   # [64, 32]
+        out[np.broadcast_to(rows, (T, 64, 32)), np.broadcast_to(ks[None], (T, 64, 32))] = val[g]
+    out = out[:M]                       # padding rows are not written by every kernel
+    assert np.all(out == np.rint(out)), "a code is not an integer"
+    return out.astype(np.int64)
+
+
+def decode_scales(ws: np.ndarray, M: int, K: int) -> np.ndarray:
+    """fp32 activation scales [M, K/64] from a workspace's [G][Mp] region."""
+    Mp, G, sa_off, _ = workspace_regions(M, K)
+    sa = np.asarray(ws[sa_off: sa_off + G * Mp * 4], dtype=np.uint8).view(np.float32).reshape(G, Mp)
+    return sa[:, :M].T.copy()

@@ -181,6 +181,17 @@ def test_device_blob_layout():
     assert np.array_equal(sdev[:, :N].T, hw.wscales) and not np.any(sdev[:, N:])
 
 
+def test_fp6_block_decoder_reads_the_packed_weights():
+    """The tests' reader of the fp6 code blocks (used on device workspaces)
+    recovers the canonical codes from the library's weight blob, which uses
+    the same block layout: pins the reader independently of any kernel."""
+    from tests.gpu_util import decode_fp6_codes
+    c = synth.linear_case("dec", 95, 8, 300, 320, 0, w_outlier_n=3, w_outlier_scale=8.0)
+    hw = S.prepare_weights(c.W, None, c.bias, 0)
+    blob = S.pack_device_weights(hw)
+    assert np.array_equal(decode_fp6_codes(blob, c.N, c.K), O.unpack_int4(hw.qweight))
+
+
 def test_awq_quantizer_bit_exact_and_packer():
     a = synth.awq_case(m_max=1, N=96, K=256, seed=81)
     q, s, z = S.awq_quantize_weights(a.W)
@@ -202,7 +213,8 @@ def test_awq_blob_layout():
     G, T, P, G4 = 5, 3, 3, 8
     q = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
     s = rng.integers(0x3000, 0x4000, size=(N, G), dtype=np.uint16)
-    z = rng.integers(0x4000, 0x4b00, size=(N, G), dtype=np.uint16)
+    # zero points are integers 0..15 held in fp16 (the packer refuses others)
+    z = rng.integers(0, 16, size=(N, G)).astype(np.float16).view(np.uint16)
     n_bytes = S._lib.awq_device_weights_bytes(N, K)
     qbytes = T * P * 1024
     s_off = (qbytes + 255) // 256 * 256
@@ -229,6 +241,57 @@ def test_awq_blob_layout():
     sz = blob[s_off: s_off + T * 16 * G4 * 4].view(np.uint32).reshape(T * 16, G4)
     assert np.array_equal(sz[:N, :G], s.astype(np.uint32) | (z.astype(np.uint32) << 16))
     assert not np.any(sz[N:]) and not np.any(sz[:, G:])
+
+
+def test_awq_packer_refuses_bad_zero_points_and_scales():
+    """The kernel forms q - z exactly as (1024 + q) - (1024 + z) in fp16,
+    which holds for integer zero points 0..15 only: the packer refuses any
+    other zero point, and non-finite scales, before writing anything."""
+    N, K = 16, 128
+    q = np.zeros((N, K // 2), np.uint8)
+    s = np.full((N, K // 64), 0.01, np.float16).view(np.uint16)
+    n_bytes = S._lib.awq_device_weights_bytes(N, K)
+    blob = np.full(n_bytes, 0xAB, np.uint8)
+
+    def pack(zv, sv=None):
+        z = np.full((N, K // 64), 3.0, np.float16)
+        z[5, 1] = zv
+        ss = s.copy()
+        if sv is not None:
+            ss.view(np.float16)[2, 0] = sv
+        return S._lib.awq_pack_device_weights(q.ctypes.data, ss.ctypes.data,
+                                              z.view(np.uint16).ctypes.data, N, K,
+                                              blob.ctypes.data, n_bytes)
+    for bad in (2.5, -1.0, 16.0, np.inf, np.nan, 15.5):
+        assert pack(bad) == INV, bad
+        assert "zero point" in S._lib.svdq_last_error().decode()
+    assert pack(3.0, np.inf) == 6 and pack(3.0, np.nan) == 6
+    assert np.all(blob == 0xAB)                  # nothing written on refusal
+    assert pack(0.0) == 0 and pack(15.0) == 0
+
+
+def test_wrappers_check_outputs_and_bias():
+    """The Python wrappers refuse caller outputs of the wrong shape, dtype or
+    layout (the kernels write exactly M x N elements of the output type) and
+    AWQ biases that are not fp16 of N elements, before calling the library."""
+    import torch
+    dev = torch.device("cpu")
+    good = torch.empty((4, 8), dtype=torch.bfloat16)
+    S._check_out(good, 4, 8, dev)
+    S._check_out(torch.empty((4, 8), dtype=torch.float32), 4, 8, dev)
+    with pytest.raises(ValueError):
+        S._check_out(torch.empty((4, 7), dtype=torch.bfloat16), 4, 8, dev)
+    with pytest.raises(ValueError):
+        S._check_out(torch.empty((4, 8), dtype=torch.float16), 4, 8, dev)
+    with pytest.raises(ValueError):
+        S._check_out(torch.empty((8, 4), dtype=torch.bfloat16).t(), 4, 8, dev)
+    with pytest.raises(ValueError):
+        S._check_out(torch.empty((4, 8), dtype=torch.float32), 4, 8, dev, dtypes=(torch.float16,))
+    S._check_bias(torch.zeros(8, dtype=torch.float16), 8, dev)
+    with pytest.raises(ValueError):
+        S._check_bias(torch.zeros(8, dtype=torch.float32), 8, dev)
+    with pytest.raises(ValueError):
+        S._check_bias(torch.zeros(7, dtype=torch.float16), 8, dev)
 
 
 # ----------------------------------------------------------- MXFP4 form

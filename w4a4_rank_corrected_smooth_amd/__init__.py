@@ -129,6 +129,28 @@ def _check(status: int, where: str) -> None:
         raise SvdqError(status, where)
 
 
+def _check_out(out: torch.Tensor, M: int, N: int, device, dtypes=(torch.bfloat16, torch.float32)) -> None:
+    """A caller-supplied output must be a contiguous [M, N] tensor of an
+    accepted dtype on the inputs' device: the kernels write exactly M * N
+    elements of that type."""
+    if not isinstance(out, torch.Tensor):
+        raise TypeError("out must be a torch.Tensor")
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
+    if out.dtype not in dtypes:
+        raise ValueError(f"out has dtype {out.dtype}, expected one of {dtypes}")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    if out.device != torch.device(device):
+        raise ValueError(f"out is on {out.device}, expected {device}")
+
+
+def _check_bias(bias: torch.Tensor, N: int, device) -> None:
+    if not isinstance(bias, torch.Tensor) or bias.dtype != torch.float16 or bias.numel() != N \
+            or not bias.is_contiguous() or bias.device != torch.device(device):
+        raise ValueError(f"bias must be a contiguous float16 tensor of {N} elements on {device}")
+
+
 def _ptr(a) -> Optional[int]:
     if a is None:
         return None
@@ -274,6 +296,7 @@ def linear_forward(layer: Linear, X: torch.Tensor, out: Optional[torch.Tensor] =
     M = X.shape[0]
     if out is None:
         out = torch.empty((M, layer.N), dtype=out_dtype, device=X.device)
+    _check_out(out, M, layer.N, X.device)
     if workspace is None:
         workspace = layer.new_workspace(M)
     dt = FP32 if out.dtype == torch.float32 else BF16
@@ -295,6 +318,7 @@ def linear_quantize(layer: Linear, X: torch.Tensor, workspace: torch.Tensor) -> 
 def linear_gemm(layer: Linear, M: int, out: torch.Tensor, workspace: torch.Tensor,
                 gelu: bool = False) -> torch.Tensor:
     """Kernel (2) of the forward alone, from a workspace filled by linear_quantize."""
+    _check_out(out, M, layer.N, workspace.device)
     dt = FP32 if out.dtype == torch.float32 else BF16
     _check(_lib.svdq_linear_gemm(ctypes.byref(layer._w), M, out.data_ptr(), dt,
                                  EPILOGUE_GELU_TANH if gelu else EPILOGUE_NONE,
@@ -312,6 +336,7 @@ def mlp_forward(l1: Linear, l2: Linear, X: torch.Tensor, out: Optional[torch.Ten
     M = X.shape[0]
     if out is None:
         out = torch.empty((M, l2.N), dtype=out_dtype, device=X.device)
+    _check_out(out, M, l2.N, X.device)
     ws1 = l1.new_workspace(M) if ws1 is None else ws1
     ws2 = l2.new_workspace(M) if ws2 is None else ws2
     dt = FP32 if out.dtype == torch.float32 else BF16
@@ -342,6 +367,7 @@ def mlp_gemm1(l1: Linear, l2: Linear, M: int, ws1: torch.Tensor, ws2: torch.Tens
 
 def mlp_gemm2(l2: Linear, M: int, out: torch.Tensor, ws2: torch.Tensor) -> torch.Tensor:
     """Third kernel of mlp_forward: l2's GEMM from the workspace mlp_gemm1 filled."""
+    _check_out(out, M, l2.N, ws2.device)
     dt = FP32 if out.dtype == torch.float32 else BF16
     _check(_lib.svdq_mlp_gemm2(ctypes.byref(l2._w), M, out.data_ptr(), dt, ws2.data_ptr(),
                                ws2.numel(), _stream(out.device)), "svdq_mlp_gemm2")
@@ -352,6 +378,9 @@ def gelu_tanh_bf16(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch
     assert x.dtype == torch.bfloat16 and x.is_contiguous()
     if out is None:
         out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() \
+            or out.device != x.device:
+        raise ValueError("out must be a contiguous bf16 tensor shaped like the input")
     _check(_lib.svdq_gelu_tanh_bf16(x.data_ptr(), out.data_ptr(), x.numel(), _stream(x.device)),
            "svdq_gelu_tanh_bf16")
     return out
@@ -480,6 +509,7 @@ def mx_linear_forward(layer: MxLinear, X: torch.Tensor, out: Optional[torch.Tens
     M = X.shape[0]
     if out is None:
         out = torch.empty((M, layer.N), dtype=out_dtype, device=X.device)
+    _check_out(out, M, layer.N, X.device)
     if workspace is None:
         workspace = layer.new_workspace(M)
     dt = FP32 if out.dtype == torch.float32 else BF16
@@ -499,6 +529,7 @@ def mx_linear_quantize(layer: MxLinear, X: torch.Tensor, workspace: torch.Tensor
 
 def mx_linear_gemm(layer: MxLinear, M: int, out: torch.Tensor, workspace: torch.Tensor,
                    gelu: bool = False) -> torch.Tensor:
+    _check_out(out, M, layer.N, workspace.device)
     dt = FP32 if out.dtype == torch.float32 else BF16
     _check(_lib.svdq_mx_linear_gemm(ctypes.byref(layer._w), M, out.data_ptr(), dt,
                                     EPILOGUE_GELU_TANH if gelu else EPILOGUE_NONE,
@@ -557,6 +588,9 @@ def awq_forward(layer: AwqLinear, x: torch.Tensor, bias: Optional[torch.Tensor] 
     M = x.shape[0]
     if out is None:
         out = torch.empty((M, layer.N), dtype=torch.float16, device=x.device)
+    _check_out(out, M, layer.N, x.device, dtypes=(torch.float16,))
+    if bias is not None:
+        _check_bias(bias, layer.N, x.device)
     _check(_lib.awq_w4a16_forward(layer.blob.data_ptr(), layer.N, layer.K, x.data_ptr(), M,
                                   None if bias is None else bias.data_ptr(), out.data_ptr(),
                                   _stream(x.device)), "awq_w4a16_forward")

@@ -382,6 +382,17 @@ svdq_status_t awq_pack(const uint8_t *q, const uint16_t *s, const uint16_t *z, i
   if ((int64_t)bytes < L.total)
     return fail(SVDQ_ERR_WORKSPACE_TOO_SMALL, "blob needs %lld bytes, got %zu",
                 (long long)L.total, bytes);
+  // The kernel forms q - z exactly as (1024 + q) - (1024 + z) in fp16, which
+  // holds only for integer zero points 0..15; scales must be finite.
+  for (int64_t i = 0; i < (int64_t)N * L.G; ++i) {
+    const float zf = f16_to_f32(z[i]), sf = f16_to_f32(s[i]);
+    if (!(zf >= 0.0f && zf <= 15.0f && zf == std::floor(zf)))
+      return fail(SVDQ_ERR_INVALID_ARGUMENT, "awq_pack_device_weights: zero point %g at (%lld, %lld) is not an integer in 0..15",
+                  (double)zf, (long long)(i / L.G), (long long)(i % L.G));
+    if (!std::isfinite(sf))
+      return fail(SVDQ_ERR_NUMERICAL, "awq_pack_device_weights: non-finite scale at (%lld, %lld)",
+                  (long long)(i / L.G), (long long)(i % L.G));
+  }
   uint8_t *b = static_cast<uint8_t *>(host_blob);
   std::memset(b, 0, (size_t)L.total);
   uint8_t *qd = b + L.q;
