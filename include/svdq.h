@@ -194,6 +194,24 @@ svdq_status_t svdq_linear_forward(const svdq_weights_t *w, const void *X, int M,
                                   svdq_epilogue_t epilogue, void *workspace,
                                   size_t ws_bytes, void *hip_stream);
 
+/* svdq_linear_forward for callers that cannot allocate device memory at all
+ * (code under stream capture, tight serving loops, harnesses that forbid
+ * allocation).  The same two kernels, with the workspace in a file-scope
+ * device array of the library (SVDQ_STATIC_SCRATCH_BYTES per device,
+ * reserved for the life of the process on every device the library runs on)
+ * instead of a caller buffer.  Nothing is allocated, by the library or by
+ * the call.  Shapes whose svdq_workspace_bytes(M, N, K, rank) without the
+ * K-split room exceeds the limit get SVDQ_ERR_WORKSPACE_TOO_SMALL; the
+ * K-split runs when its partials fit too.  Every call on one device shares
+ * that device's array: calls that overlap in time on one device (two
+ * streams, two threads) race, so such callers order them.  The array keeps
+ * the last call's contents; the call needs none of it cleared.  Other
+ * arguments, validation and errors as for svdq_linear_forward. */
+#define SVDQ_STATIC_SCRATCH_BYTES (64ll << 20)
+svdq_status_t svdq_linear_forward_static(const svdq_weights_t *w, const void *X, int M,
+                                         void *Y, svdq_dtype_t y_dtype,
+                                         svdq_epilogue_t epilogue, void *hip_stream);
+
 /* The forward's two kernels as separate calls, for callers that time or
  * schedule them apart.  svdq_linear_quantize runs kernel (1) on X and leaves
  * the activation codes, scales and low-rank partials in `workspace`;

@@ -270,6 +270,28 @@ def test_awq_packer_refuses_bad_zero_points_and_scales():
     assert pack(0.0) == 0 and pack(15.0) == 0
 
 
+def test_static_forward_validation():
+    """svdq_linear_forward_static validates like the forward and refuses
+    shapes whose workspace exceeds the static scratch array, all before any
+    HIP call."""
+    lib = S._lib
+    w = _dw()
+    call = lambda **kw: lib.svdq_linear_forward_static(
+        ctypes.byref(kw.get("w", w)), kw.get("X", FAKE), kw.get("M", 64), kw.get("Y", FAKE),
+        kw.get("dt", S.BF16), kw.get("epi", 0), None)
+    assert call(X=None) == INV
+    assert call(X=FAKE + 4) == INV
+    assert call(Y=None) == INV
+    assert call(M=0) == SHAPE
+    assert call(dt=S.FP16) == INV
+    assert call(epi=3) == INV
+    assert call(w=_dw(K=100)) == SHAPE
+    big = _dw(N=256, K=16384, rank=32)
+    # M = 6144, K = 16384: the fp6 codes alone are 72 MiB
+    assert call(w=big, M=6144) == WS
+    assert "limit" in lib.svdq_last_error().decode()
+
+
 def test_wrappers_check_outputs_and_bias():
     """The Python wrappers refuse caller outputs of the wrong shape, dtype or
     layout (the kernels write exactly M x N elements of the output type) and

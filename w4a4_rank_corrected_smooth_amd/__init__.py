@@ -40,7 +40,7 @@ EXPORTS = [
     "svdq_abi_version", "svdq_status_string", "svdq_last_error", "svdq_device_check",
     "svdq_host_weights_sizes", "svdq_calibration_absmax", "svdq_prepare_weights",
     "svdq_device_weights_bytes", "svdq_pack_device_weights", "svdq_workspace_bytes",
-    "svdq_linear_forward", "svdq_linear_quantize", "svdq_linear_gemm", "svdq_mlp_forward",
+    "svdq_linear_forward", "svdq_linear_forward_static", "svdq_linear_quantize", "svdq_linear_gemm", "svdq_mlp_forward",
     "svdq_mlp_quantize", "svdq_mlp_gemm1", "svdq_mlp_gemm2", "svdq_gelu_tanh_bf16",
     "svdq_quantize_activations",
     "svdq_debug_group_sums", "awq_quantize_weights", "awq_device_weights_bytes",
@@ -86,6 +86,7 @@ _sig("svdq_device_weights_bytes", _sz, [_i, _i, _i])
 _sig("svdq_pack_device_weights", _i, [ctypes.POINTER(HostWeights), _vp, _sz])
 _sig("svdq_workspace_bytes", _sz, [_i, _i, _i, _i])
 _sig("svdq_linear_forward", _i, [ctypes.POINTER(DeviceWeights), _vp, _i, _vp, _i, _i, _vp, _sz, _vp])
+_sig("svdq_linear_forward_static", _i, [ctypes.POINTER(DeviceWeights), _vp, _i, _vp, _i, _i, _vp])
 _sig("svdq_linear_quantize", _i, [ctypes.POINTER(DeviceWeights), _vp, _i, _vp, _sz, _vp])
 _sig("svdq_linear_gemm", _i, [ctypes.POINTER(DeviceWeights), _i, _vp, _i, _i, _vp, _sz, _vp])
 _sig("svdq_gelu_tanh_bf16", _i, [_vp, _vp, _sz, _vp])
@@ -304,6 +305,24 @@ def linear_forward(layer: Linear, X: torch.Tensor, out: Optional[torch.Tensor] =
                                     EPILOGUE_GELU_TANH if gelu else EPILOGUE_NONE,
                                     workspace.data_ptr(), workspace.numel(), _stream(X.device)),
            "svdq_linear_forward")
+    return out
+
+
+STATIC_SCRATCH_BYTES = 64 << 20     # SVDQ_STATIC_SCRATCH_BYTES
+
+
+def linear_forward_static(layer: Linear, X: torch.Tensor, out: torch.Tensor,
+                          gelu: bool = False) -> torch.Tensor:
+    """svdq_linear_forward_static: the forward with the library's own device
+    scratch array as workspace (no allocation in the call); `out` is the
+    caller's [M, N] bf16 or fp32 tensor."""
+    assert X.dtype == torch.bfloat16 and X.is_contiguous() and X.shape[1] == layer.K
+    _check_out(out, X.shape[0], layer.N, X.device)
+    dt = FP32 if out.dtype == torch.float32 else BF16
+    _check(_lib.svdq_linear_forward_static(ctypes.byref(layer._w), X.data_ptr(), X.shape[0],
+                                           out.data_ptr(), dt,
+                                           EPILOGUE_GELU_TANH if gelu else EPILOGUE_NONE,
+                                           _stream(X.device)), "svdq_linear_forward_static")
     return out
 
 

@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <cstring>
 
 #include "common.h"
@@ -1710,6 +1711,70 @@ svdq_status_t svdq_linear_forward(const svdq_weights_t *w, const void *X, int M,
     return st;
   return launch_k2(w, M, Y, y_dtype, epilogue, workspace, stream, K2_D_PARTIALS, nullptr, nullptr,
                    ws_bytes);
+}
+
+// ------------------------------------------------ allocation-free forward
+// For callers that cannot allocate device memory (code under stream
+// capture, serving loops, harnesses that forbid it): the forward's workspace
+// is this file-scope device array instead of a caller buffer.  Each device
+// holds its own copy, at its own address, until the process ends.  In host
+// code the array's name is not a device address; the address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+static __device__ __align__(256) uint8_t scratch[SVDQ_STATIC_SCRATCH_BYTES];
+
+namespace {
+std::atomic<void *> g_scratch_addr[64];
+std::mutex g_scratch_mu;
+
+svdq_status_t scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(SVDQ_ERR_NO_DEVICE, "hipGetDevice failed");
+  if (dev >= 64) return fail(SVDQ_ERR_UNSUPPORTED_DEVICE, "device index %d beyond 63", dev);
+  void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr) {
+        (void)hipGetLastError();
+        return fail(SVDQ_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                    hipGetErrorString(e));
+      }
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SVDQ_OK;
+}
+}  // namespace
+
+svdq_status_t svdq_linear_forward_static(const svdq_weights_t *w, const void *X, int M, void *Y,
+                                         svdq_dtype_t y_dtype, svdq_epilogue_t epilogue,
+                                         void *hip_stream) {
+  static const char *who = "svdq_linear_forward_static";
+  svdq_status_t st = validate_weights(w, who);
+  if (st != SVDQ_OK) return st;
+  if (!X) return fail(SVDQ_ERR_INVALID_ARGUMENT, "%s: NULL X", who);
+  if (!aligned16(X)) return fail(SVDQ_ERR_INVALID_ARGUMENT, "%s: misaligned X", who);
+  if ((st = validate_output(Y, y_dtype, epilogue, who)) != SVDQ_OK) return st;
+  if (M < 1 || (int64_t)M * w->K > ((int64_t)1 << 31))
+    return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "%s: M=%d", who, M);
+  const WorkLayout Wl(M, w->K, w->rank);
+  if (Wl.total > (int64_t)SVDQ_STATIC_SCRATCH_BYTES)
+    return fail(SVDQ_ERR_WORKSPACE_TOO_SMALL, "%s: M=%d K=%d rank=%d needs %lld bytes of scratch, the limit is %lld",
+                who, M, w->K, w->rank, (long long)Wl.total, (long long)SVDQ_STATIC_SCRATCH_BYTES);
+  if ((st = check_device()) != SVDQ_OK) return st;
+  void *ws = nullptr;
+  if ((st = scratch_address(&ws)) != SVDQ_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const WeightLayout L(w->N, w->K, w->rank);
+  // every byte the GEMM reads is written by the quantiser first (all Mp
+  // rows, every split's partial), so nothing is cleared
+  if ((st = launch_k1(L, Wl, w, X, M, static_cast<uint8_t *>(ws), stream)) != SVDQ_OK) return st;
+  return launch_k2(w, M, Y, y_dtype, epilogue, ws, stream, K2_D_PARTIALS, nullptr, nullptr,
+                   (size_t)SVDQ_STATIC_SCRATCH_BYTES);
 }
 
 static svdq_status_t validate_pair(const svdq_weights_t *w1, const svdq_weights_t *w2, int M,
