@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 256 CU x 2.4 GHz x 8192 ops/clk
 PEAK_HBM_GBS = 8000.0
 PEAK_FP4_TOPS = 10100.0     # MI355X dense FP4 MFMA
+PEAK_FP6_TOPS = 10100.0     # MI355X dense FP6 MFMA (the instruction the INT4 GEMM runs on)
 
 
 def log(msg):
@@ -355,6 +356,7 @@ def mx_pair(args, S, fc1, W2, b2, ax2, X, R, dev, stream):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    settle(step, 0.1)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
@@ -614,6 +616,108 @@ def block_study(args):
         torch.cuda.empty_cache()
 
 
+SETTLE_S = 0.3     # seconds of sustained load before any timed pass
+
+
+def settle(fn, seconds):
+    """Run `fn(i)` in batches until `seconds` of wall time have passed: the
+    GPU takes tens of milliseconds of sustained load to reach steady clocks,
+    whatever the warm-up step count."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for _ in range(10):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n
+
+
+def back_to_back(fn, stream, n=30, reps=5):
+    """Median over `reps` series of the mean duration of `n` launches of
+    fn(i) enqueued back to back between two events (us)."""
+    import numpy as np
+    import torch
+    settle(fn, 0.05)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / n)
+    return float(np.median(ts))
+
+
+def read_sclk_mhz():
+    """Current shader clock from the driver's DPM table (the level marked
+    '*'), or None where the file is not readable."""
+    import glob
+    for p in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(p):
+                if "*" in line:
+                    return int("".join(ch for ch in line.split(":")[1] if ch.isdigit()))
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
+def footprint(S, layers, awq_case):
+    """Device weight bytes per layer (MB): the fp6 blob this library
+    uploads, the canonical INT4 form (nibble codes, fp32 scales, bf16
+    factors, 1/lambda, bias) and the layer in bf16; the AWQ blob against
+    fp16."""
+    out = {}
+    for name, N, K, r in layers:
+        canon = N * K // 2 + N * (K // 64) * 4 + 2 * (K + N) * r + 4 * K + 4 * N
+        out[name] = {"device_blob": round(S.device_weights_bytes(N, K, r) / 1e6, 2),
+                     "int4_canonical": round(canon / 1e6, 2), "bf16": round((2 * N * K + 2 * N) / 1e6, 2)}
+    N, K = awq_case.N, awq_case.K
+    out["awq_mod"] = {"device_blob": round(S._lib.awq_device_weights_bytes(N, K) / 1e6, 2),
+                      "fp16": round(2 * N * K / 1e6, 2)}
+    return out
+
+
+def hbm_floor(args):
+    """The practical HBM rate at the bandwidth-bound kernels' own sizes and
+    grids: a plain streaming read (and copy) of the quantiser's input (4608 x
+    3072 and 4608 x 12288 bf16: 28.3 / 113.2 MB, grid (M/32) x splits) and
+    of the W4A16 blob (18432 x 3072: 32 MB, grid N/16), each over rotating
+    buffers whose total exceeds the 256 MB Infinity Cache, timed back to
+    back; plus a sweep of grids.  One JSON line per case."""
+    import torch
+    import w4a4_rank_corrected_smooth_amd as S
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    S.device_check()
+    stream = torch.cuda.current_stream(dev)
+    cases = [("k1_fc1_input", 4608 * 3072 * 2, 144 * 3), ("k1_fc2_input", 4608 * 12288 * 2, 144 * 3),
+             ("k3_awq_blob", S._lib.awq_device_weights_bytes(18432, 3072), 18432 // 16)]
+    for name, nbytes, kgrid in cases:
+        nbytes = nbytes // 16 * 16
+        RB = max(3, -(-640_000_000 // nbytes))
+        src = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(i) for i in range(RB)]
+        dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        grids = sorted({kgrid, 256, 512, 1024, 2048, 4096, 8192})
+        sink = torch.empty(max(grids), dtype=torch.int32, device=dev)
+        res = {}
+        for g in grids:
+            us = back_to_back(lambda i: S.measure_stream(src[i % RB], g, sink=sink), stream)
+            res[g] = round(nbytes / us / 1e3, 1)
+        cus = back_to_back(lambda i: S.measure_stream(src[i % RB], kgrid, dst=dst), stream)
+        best = max(res.values())
+        print(json.dumps({"hbm_floor": name, "bytes": nbytes, "kernel_grid": kgrid, "rotating_sets": RB,
+                          "read_gbs_by_grid": res, "read_gbs_at_kernel_grid": res[kgrid],
+                          "read_gbs_best": best, "copy_gbs_at_kernel_grid": round(2 * nbytes / cus / 1e3, 1),
+                          "read_frac_of_8tbs_best": round(best / PEAK_HBM_GBS, 4)}), flush=True)
+        del src, dst
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -639,6 +743,8 @@ def main():
                     help="CPU only: summarise a rocprofv3 --pmc pass of the shader counters into profiles/")
     ap.add_argument("--block", action="store_true",
                     help="launch study of one transformer block's calls, eager and as a HIP graph")
+    ap.add_argument("--hbm-floor", action="store_true",
+                    help="streaming read/copy rates at the quantiser's and W4A16 kernel's sizes and grids")
     ap.add_argument("--summarize-configs", nargs=2, metavar=("TRACE_DIR", "SWEEP_JSONL"),
                     help="CPU only: summarise a rocprofv3 trace of --configs into profiles/ and exit")
     args = ap.parse_args()
@@ -670,6 +776,9 @@ def main():
         return
     if args.block:
         block_study(args)
+        return
+    if args.hbm_floor:
+        hbm_floor(args)
         return
 
     import numpy as np
@@ -752,36 +861,49 @@ def main():
         S.awq_forward(A[k], xm[k], out=ym[k])
         mark(4)
 
-    log(f"warmup {args.warmup} steps")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(NEV)] for _ in range(args.steps)]
-    log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    wall_unfused = None
-    if not args.skip_unfused:
-        log(f"timing {args.steps} steps of the unfused pair (fc1 output stored, fc2 quantised apart)")
-        for i in range(args.warmup // 4):
-            step(i, fused=False)
+    def wall_pass(fused=True, sample_clock=False):
+        """K uninstrumented steps between two device synchronisations; the
+        shader clock is read while they run."""
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
-            step(args.warmup + i, fused=False)
+            step(i, fused=fused)
+        mhz = read_sclk_mhz() if sample_clock else None
         torch.cuda.synchronize()
-        wall_unfused = time.perf_counter() - t0
-    log(f"timing {args.steps} steps with per-kernel events")
-    for i in range(args.warmup // 4):
+        return time.perf_counter() - t0, mhz
+
+    log(f"warmup {args.warmup} steps, then at least {SETTLE_S} s of sustained load (clock settle)")
+    for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    settle_steps = settle(lambda i: step(i), SETTLE_S)
+    log(f"timing {args.steps} steps (headline), then the same steps with per-kernel events")
+    wall, sclk_mhz = wall_pass(True, sample_clock=True)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(NEV)] for _ in range(args.steps)]
     for i in range(args.steps):
-        step(args.warmup + args.steps + i, events[i])
+        step(i, events[i])
     torch.cuda.synchronize()
+    wall_unfused = wall_fused2 = None
+    if not args.skip_unfused:
+        log(f"timing {args.steps} steps of the unfused pair, then the fused pair again")
+        settle(lambda i: step(i, fused=False), 0.05)
+        wall_unfused, _ = wall_pass(False)
+        wall_fused2, _ = wall_pass(True)
+
+    # bandwidth-bound kernels: back-to-back launches (no event between them)
+    # over enough rotating buffers that a series exceeds the 256 MB
+    # Infinity Cache
+    k1_us = k3_us = None
+    if not args.skip_unfused:
+        log("K1 and K3 back to back over rotating buffers")
+        RB = 10
+        Xb = [X[i % R] if i < R else X[0].clone() for i in range(RB)]
+        wsb = [ws1[i % R] if i < R else L1[0].new_workspace(M) for i in range(RB)]
+        k1_us = back_to_back(lambda i: S.linear_quantize(L1[0], Xb[i % RB], wsb[i % RB]), stream)
+        Ab = [A[i % R] if i < R else S.AwqLinear(q, s, z, dev) for i in range(RB)]
+        k3_us = back_to_back(lambda i: S.awq_forward(Ab[i % RB], xm[0], out=ym[0]), stream)
+        del Xb, wsb, Ab
+        torch.cuda.empty_cache()
 
     mx = None
     if not args.skip_mx:
@@ -822,22 +944,34 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": "int4",
         "data": "synthetic",
         "config": {"workload": "flux_mlp_pair_4608x3072x12288_r32_gelu+awq_mod_1x3072x18432",
                    "tokens": M, "d_model": K1, "d_ff": N1, "rank": 32, "group": 64,
                    "awq_rows": 1, "rotation_sets": R},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+        # The INT4 x INT4 group sums run on gfx950's block-scaled matrix
+        # instruction with fp6 E2M3 operands (codes -7..7 exact), so the
+        # instruction's own peak (fp6, 10.1 POP/s) is the roofline; the
+        # metric's int8 peak (5.0 POP/s) is reported beside it.
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP6_TOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP6_TOPS, 4),
                      "traffic": traffic, "kernel": "k2_w4a4_gemm",
+                     "instruction": "v_mfma_scale_f32_32x32x64_f8f6f4 (fp6 E2M3 operands)",
+                     "frac_int8_peak": round(achieved / PEAK_INT8_TOPS, 4), "peak_int8": PEAK_INT8_TOPS,
                      "ops_per_launch": ops_layer, "avg_launch_us": round(k2_us, 2)},
         "kernels_us": {n: round(v, 2) for n, v in avg.items()},
         "event_step_us": round(float(np.mean(span)), 2),
-        "k1_gbs": {"fc1": round(k1_bytes_fc1 / avg["fc1_quantize"] / 1e3, 1)},
+        "settle_steps": settle_steps,
+        "sclk_mhz_during_timing": sclk_mhz,
+        "k1_gbs": ({"fc1": round(k1_bytes_fc1 / k1_us / 1e3, 1), "us_back_to_back": round(k1_us, 2),
+                    "frac_hbm": round(k1_bytes_fc1 / k1_us / 1e3 / PEAK_HBM_GBS, 4)} if k1_us else None),
+        "awq_gbs": ({"m1": round(awq_bytes / k3_us / 1e3, 1), "us_back_to_back": round(k3_us, 2),
+                     "frac_hbm": round(awq_bytes / k3_us / 1e3 / PEAK_HBM_GBS, 4)} if k3_us else None),
         "unfused_pair": (None if wall_unfused is None else
                          {"ms_per_step": round(wall_unfused / args.steps * 1e3, 4),
-                          "value": round(2 * ops_layer / (wall_unfused / args.steps) / 1e12, 2)}),
-        "awq_gbs": round(awq_bytes / avg["awq_m1"] / 1e3, 1),
+                          "value": round(2 * ops_layer / (wall_unfused / args.steps) / 1e12, 2),
+                          "fused_again_ms_per_step": round(wall_fused2 / args.steps * 1e3, 4)}),
+        "weights_mb": footprint(S, [("fc1", N1, K1, 32), ("fc2", N2, K2, 32)], a),
         "mxfp4_pair": mx,
         "prepare_s": {"fc1": round(prep1, 2), "fc2": round(prep2, 2)},
         "source_hash": source_hash(),

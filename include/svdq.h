@@ -385,6 +385,16 @@ svdq_status_t awq_w4a16_forward(const void *blob, int N, int K, const void *x_fp
                                 int M, const void *bias_fp16, void *y_fp16,
                                 void *hip_stream);
 
+/* ============================================================ measurement
+ * Not part of the layer: the practical HBM rate that the bandwidth-bound
+ * kernels (the quantiser, the W4A16 GEMV) are judged against.  Streams
+ * `bytes` (a multiple of 16) from device `src` with `grid` workgroups of 256
+ * threads: mode 0 reads every 16-byte word once and writes one 32-bit word
+ * per workgroup to device `sink` [grid]; mode 1 copies to device `dst`.
+ * Asynchronous on `hip_stream`. */
+svdq_status_t svdq_measure_stream(const void *src, void *dst, size_t bytes, int grid, int mode,
+                                  uint32_t *sink, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

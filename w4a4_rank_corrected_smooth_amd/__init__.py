@@ -48,7 +48,7 @@ EXPORTS = [
     "svdq_mx_host_weights_sizes", "svdq_mx_prepare_weights", "svdq_mx_device_weights_bytes",
     "svdq_mx_pack_device_weights", "svdq_mx_workspace_bytes", "svdq_mx_linear_forward",
     "svdq_mx_linear_quantize", "svdq_mx_linear_gemm", "svdq_mx_quantize_activations",
-    "svdq_merge_lora", "svdq_mx_merge_lora",
+    "svdq_merge_lora", "svdq_mx_merge_lora", "svdq_measure_stream",
 ]
 
 
@@ -112,6 +112,7 @@ _sig("svdq_mx_linear_forward", _i, [_W, _vp, _i, _vp, _i, _i, _vp, _sz, _vp])
 _sig("svdq_mx_linear_quantize", _i, [_W, _vp, _i, _vp, _sz, _vp])
 _sig("svdq_mx_linear_gemm", _i, [_W, _i, _vp, _i, _i, _vp, _sz, _vp])
 _sig("svdq_mx_quantize_activations", _i, [_W, _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp])
+_sig("svdq_measure_stream", _i, [_vp, _vp, _sz, _i, _i, _vp, _vp])
 _sig("svdq_merge_lora", _i, [ctypes.POINTER(HostWeights), _vp, _vp, _i, ctypes.c_float,
                              ctypes.POINTER(HostWeights)])
 _sig("svdq_mx_merge_lora", _i, [ctypes.POINTER(MxHostWeights), _vp, _vp, _i, ctypes.c_float,
@@ -614,3 +615,21 @@ def awq_forward(layer: AwqLinear, x: torch.Tensor, bias: Optional[torch.Tensor] 
                                   None if bias is None else bias.data_ptr(), out.data_ptr(),
                                   _stream(x.device)), "awq_w4a16_forward")
     return out
+
+
+# ------------------------------------------------------------ measurement
+def measure_stream(src: torch.Tensor, grid: int, dst: Optional[torch.Tensor] = None,
+                   sink: Optional[torch.Tensor] = None) -> None:
+    """svdq_measure_stream: a plain streaming read of `src` (dst None) or
+    copy into `dst`, with `grid` workgroups: the practical HBM floor."""
+    nbytes = src.numel() * src.element_size()
+    if dst is None:
+        if sink is None or sink.numel() < grid or sink.dtype != torch.int32:
+            raise ValueError("a read needs an int32 sink of at least `grid` elements")
+        _check(_lib.svdq_measure_stream(src.data_ptr(), None, nbytes, grid, 0, sink.data_ptr(),
+                                        _stream(src.device)), "svdq_measure_stream")
+    else:
+        if dst.numel() * dst.element_size() < nbytes:
+            raise ValueError("dst is smaller than src")
+        _check(_lib.svdq_measure_stream(src.data_ptr(), dst.data_ptr(), nbytes, grid, 1, None,
+                                        _stream(src.device)), "svdq_measure_stream")

@@ -1400,6 +1400,49 @@ __global__ __launch_bounds__(256) void gelu_tanh_bf16_kernel(const uint16_t *__r
   }
 }
 
+// ============================================================ measurement
+// Plain streaming read (mode 0: every 16-byte word loaded once, 16 loads in
+// flight per lane, folded into one word per workgroup so nothing is
+// optimised away) or copy (mode 1) of `bytes` with a caller-chosen grid:
+// the practical HBM rate at a given size and grid, against which the codec
+// kernels are judged.
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void stream_probe_kernel(const v4u *__restrict__ src,
+                                                           v4u *__restrict__ dst, int64_t n16,
+                                                           int mode, uint32_t *__restrict__ sink) {
+  constexpr int U = 16;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (mode == 0) {
+    v4u acc = v4u{0u, 0u, 0u, 0u};
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+      v4u v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc ^= v[u];
+    }
+    for (; i < n16; i += stride) acc ^= src[i];
+    __shared__ uint32_t red[256];
+    red[threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t r = 0;
+      for (int t = 0; t < 256; ++t) r ^= red[t];
+      sink[blockIdx.x] = r;
+    }
+  } else {
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+      v4u v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(v[u], dst + i + u * stride);
+    }
+    for (; i < n16; i += stride) dst[i] = src[i];
+  }
+}
+
 // ============================================================ inspection
 __global__ void canon_codes_kernel(const uint8_t *__restrict__ qa, int M, int K, int T,
                                    uint8_t *__restrict__ out) {
@@ -2025,6 +2068,21 @@ svdq_status_t svdq_mx_quantize_activations(const svdq_weights_t *w, const void *
                        (int)Wl.rp, w->rank, lowrank_down);
   }
   return launch_status("inspection kernels");
+}
+
+svdq_status_t svdq_measure_stream(const void *src, void *dst, size_t bytes, int grid, int mode,
+                                  uint32_t *sink, void *hip_stream) {
+  if (!src || (mode == 1 && !dst) || (mode == 0 && !sink))
+    return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_measure_stream: NULL pointer");
+  if (!aligned16(src) || (dst && !aligned16(dst)) || bytes % 16 != 0)
+    return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_measure_stream: pointers and size must be 16-byte multiples");
+  if (mode != 0 && mode != 1) return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_measure_stream: mode %d", mode);
+  if (grid < 1 || grid > (1 << 20)) return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "svdq_measure_stream: grid %d", grid);
+  svdq_status_t st = check_device();
+  if (st != SVDQ_OK) return st;
+  hipLaunchKernelGGL(stream_probe_kernel, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(hip_stream),
+                     static_cast<const v4u *>(src), static_cast<v4u *>(dst), (int64_t)(bytes / 16), mode, sink);
+  return launch_status("stream probe launch");
 }
 
 svdq_status_t awq_w4a16_forward(const void *blob, int N, int K, const void *x, int M,
