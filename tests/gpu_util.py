@@ -51,14 +51,26 @@ def _up256(x: int) -> int:
     return -(-x // 256) * 256
 
 
+SCALE_OP_BYTES = 16
+
+
 def workspace_regions(M: int, K: int):
     """Byte offsets of the INT4 workspace's code and scale regions (the
-    device layout: fp6 code blocks [G][Mp/32] x 1536, then fp32 scales
-    [G][Mp], each region 256-byte aligned)."""
+    device layout: fp6 code blocks [G][Mp/32] x 1536, then the scales as
+    16-byte matrix operands [G][Mp], each region 256-byte aligned)."""
     Mp, G = _up256(M), K // 64
     sa_off = _up256(Mp * K * 3 // 4)
-    d_off = _up256(sa_off + G * Mp * 4)
+    d_off = _up256(sa_off + G * Mp * SCALE_OP_BYTES)
     return Mp, G, sa_off, d_off
+
+
+def scale_from_operand(words: np.ndarray) -> np.ndarray:
+    """fp32 scales from their 16-byte operand form (bf16 slots a1 a1 a1 a2 a2
+    a2 a3 a3): s = a1 + a2 + a3, exact in float32 (test-side reader of the
+    documented layout)."""
+    w = np.asarray(words, dtype=np.uint8).reshape(-1, 8).view(np.uint16).reshape(-1, 8)
+    a = (w.astype(np.uint32) << 16).view(np.float32)
+    return ((a[:, 0] + a[:, 3]) + a[:, 6]).astype(np.float32)
 
 
 def decode_fp6_codes(ws: np.ndarray, M: int, K: int) -> np.ndarray:
@@ -92,7 +104,7 @@ def decode_fp6_codes(ws: np.ndarray, M: int, K: int) -> np.ndarray:
 
 
 def decode_scales(ws: np.ndarray, M: int, K: int) -> np.ndarray:
-    """fp32 activation scales [M, K/64] from a workspace's [G][Mp] region."""
+    """fp32 activation scales [M, K/64] from a workspace's [G][Mp] operand region."""
     Mp, G, sa_off, _ = workspace_regions(M, K)
-    sa = np.asarray(ws[sa_off: sa_off + G * Mp * 4], dtype=np.uint8).view(np.float32).reshape(G, Mp)
-    return sa[:, :M].T.copy()
+    raw = np.asarray(ws[sa_off: sa_off + G * Mp * SCALE_OP_BYTES], dtype=np.uint8).reshape(G, Mp, 16)
+    return scale_from_operand(raw[:, :M].reshape(-1)).reshape(G, M).T.copy()

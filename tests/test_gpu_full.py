@@ -151,9 +151,10 @@ def test_mlp_pair_fused_as_benchmarked(S, mlp):
     K2, G2, Mp, rp = ref2["K"], ref2["K"] // 64, -(-M // 256) * 256, 32
     qa_bytes = Mp * K2 * 3 // 4
     sa_off = -(-qa_bytes // 256) * 256
-    d_off = -(-(sa_off + G2 * Mp * 4) // 256) * 256
+    sa_bytes = G2 * Mp * 16                        # scales as 16-byte operands
+    d_off = -(-(sa_off + sa_bytes) // 256) * 256
     assert torch.equal(ws2[:qa_bytes], ws2u[:qa_bytes]), "fc2 codes"
-    assert torch.equal(ws2[sa_off:sa_off + G2 * Mp * 4], ws2u[sa_off:sa_off + G2 * Mp * 4]), "fc2 scales"
+    assert torch.equal(ws2[sa_off:sa_off + sa_bytes], ws2u[sa_off:sa_off + sa_bytes]), "fc2 scales"
     X2 = Y1.cpu().view(torch.int16).numpy().view(np.uint16)
     rows = sample_rows(M, 5)
     f = O.forward(ref2, X2, rows=rows)

@@ -54,7 +54,7 @@ def _regions(M, K, rank):
     up = lambda x: -(-x // 256) * 256
     qa_bytes = Mp * K * 3 // 4
     sa_off = up(qa_bytes)
-    d_off = up(sa_off + G * Mp * 4)
+    d_off = up(sa_off + G * Mp * 16)              # scales as 16-byte operands
     return Mp, G, sa_off, d_off
 
 
@@ -79,8 +79,8 @@ def test_fused_pair_codes_scales_and_D(S, name, M, K1, N1, N2, r1, r2):
     for g in range(G):
         lo, hi = g * T * 1536, (g * T + tM) * 1536
         assert np.array_equal(a[lo:hi], b[lo:hi]), f"codes of group {g}"
-    sa = a[sa_off: sa_off + G * Mp * 4].view(np.float32).reshape(G, Mp)[:, :M]
-    sb = b[sa_off: sa_off + G * Mp * 4].view(np.float32).reshape(G, Mp)[:, :M]
+    sa = a[sa_off: sa_off + G * Mp * 16].reshape(G, Mp, 16)[:, :M]
+    sb = b[sa_off: sa_off + G * Mp * 16].reshape(G, Mp, 16)[:, :M]
     assert np.array_equal(sa, sb), "scales"
     if r2 > 0:
         rp = -(-r2 // 32) * 32

@@ -176,9 +176,17 @@ def test_device_blob_layout():
             assert _e2m3_to_int((bits >> (6 * cidx)) & 63) == codes[n, k]
     # padded rows hold zero codes
     assert not np.any(qdev.reshape(G, T, 1536)[:, 4:, :])
+    # scales as the GEMM's column operands: bf16 slots b1 b2 b3 b1 b2 b3 b1 b2
+    # with s = b1 + b2 + b3 exactly, b1 and b2 the top bits of s and of the
+    # remainder, [G][Np] x 16 bytes
     s_off = (qbytes + 255) // 256 * 256
-    sdev = blob[s_off: s_off + G * Np * 4].view(np.float32).reshape(G, Np)
-    assert np.array_equal(sdev[:, :N].T, hw.wscales) and not np.any(sdev[:, N:])
+    ops = blob[s_off: s_off + G * Np * 16].view(np.uint16).reshape(G, Np, 8)
+    assert np.array_equal(ops[:, :, 3:6], ops[:, :, 0:3]) and np.array_equal(ops[:, :, 6:8], ops[:, :, 0:2])
+    piece = (ops[:, :, :3].astype(np.uint32) << 16).view(np.float32)
+    s = (piece[:, :, 0] + piece[:, :, 1]) + piece[:, :, 2]
+    assert np.array_equal(s[:, :N].T, hw.wscales) and not np.any(ops[:, N:])
+    hi = hw.wscales.T.view(np.uint32) >> 16
+    assert np.array_equal(ops[:, :N, 0], hi.astype(np.uint16))
 
 
 def test_fp6_block_decoder_reads_the_packed_weights():
@@ -506,7 +514,7 @@ def test_host_weights_accept_fortran_ordered_arrays():
     blob = S.pack_device_weights(hw)
     L = S.device_weights_bytes(96, 128, 6)
     Np, rp, K = 256, 32, 128
-    off_l2t = Np * K * 3 // 4 + 2 * Np * 4
+    off_l2t = Np * K * 3 // 4 + 2 * Np * 16      # codes, then 2 groups of 16-byte scale operands
     off_l1t = off_l2t + Np * rp * 2
     # L1s in the quantiser's fragment order: [group][32-rank block][16-channel
     # step j][lane][8 channels]; lane l is rank l % 32 of the block, channels
@@ -616,7 +624,8 @@ def test_workspace_includes_k_split_partials():
                 Ssp = s_
             if G // s_ >= 4 and T * s_ >= 384:
                 break
-        return up(Mp * K * 3 // 4) + up(G * Mp * 4) + up(max(Ssp, 2) * Mp * rp * 4)
+        # fp6 codes, 16-byte scale operands, fp32 partials of D
+        return up(Mp * K * 3 // 4) + up(G * Mp * 16) + up(max(Ssp, 2) * Mp * rp * 4)
     for M, N, K, r, ks in [(4608, 12288, 3072, 32, 1), (1024, 3072, 3072, 128, 5), (100, 200, 1024, 8, 2),
                            (1, 3072, 12288, 32, 8), (64, 512, 448, 4, 1), (4608, 3072, 12288, 32, 1),
                            (512, 9216, 3072, 32, 1), (512, 3072, 3072, 32, 6)]:

@@ -47,6 +47,19 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ v8bf as_v8bf(uint4 u) { return __builtin_bit_cast(v8bf, u); }
 
+// A group scale as the row operand of the GEMM's scale product: s = a1 + a2
+// + a3 exactly (a1 = s with the low 16 bits of its encoding cleared, a2 the
+// same of s - a1, a3 the rest, each subtraction exact and each piece a bf16),
+// laid out as the eight K slots a1 a1 a1 a2 a2 a2 a3 a3 (layout.h).
+__device__ __forceinline__ uint4 scale_row_operand(float s) {
+  const uint32_t u = __float_as_uint(s);
+  const float r = s - __uint_as_float(u & 0xFFFF0000u);
+  const uint32_t ur = __float_as_uint(r);
+  const float a3 = r - __uint_as_float(ur & 0xFFFF0000u);
+  const uint32_t h1 = u >> 16, h2 = ur >> 16, h3 = __float_as_uint(a3) >> 16;
+  return make_uint4(h1 | (h1 << 16), h1 | (h2 << 16), h2 | (h2 << 16), h3 | (h3 << 16));
+}
+
 // tanh-form GELU, 0.5 y (1 + tanh u) with u = sqrt(2/pi) (y + 0.044715 y^3),
 // evaluated as y / (1 + exp(-2u)) (the same function) so that large negative
 // y keep their relative accuracy instead of cancelling in 1 + tanh(u).  With
@@ -339,7 +352,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
 #pragma unroll
       for (int j = 0; j < 3; ++j)
         *reinterpret_cast<uint2 *>(qp + 512 * j) = make_uint2(packed[2 * j], packed[2 * j + 1]);
-      sa[(int64_t)g * Mp + row] = sc;            // both halves hold the same scale
+      // both halves hold the same scale; the first writes its operand form
+      if (h == 0) reinterpret_cast<uint4 *>(sa)[(int64_t)g * Mp + row] = scale_row_operand(sc);
     }
     if (TB > 0 && live) {
 #pragma unroll
@@ -407,8 +421,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
 enum { MODE_FWD = 0, MODE_SUMS = 1, MODE_MX = 2 };
 
 struct K2Args {
-  const uint8_t *qa; const float *sa; const float *dpart; int S, M, Mp;
-  const uint8_t *qw; const float *sw; const uint16_t *l2t; const float *bias;
+  // sa / sw: the group scales as matrix operands ([G][Mp] / [G][Np] x 16 B)
+  const uint8_t *qa; const uint8_t *sa; const float *dpart; int S, M, Mp;
+  const uint8_t *qw; const uint8_t *sw; const uint16_t *l2t; const float *bias;
   int N, Np, K, rp;
   void *Y;
   int32_t *P; int m0, mcount, n0, ncount;
@@ -434,22 +449,30 @@ static_assert(BM == kK2TileM && BN == kK2TileN, "the K-split sizing uses the wor
 constexpr int A_BLK = BM / kTile, B_BLK = BN / kTile;
 constexpr int A_BYTES = A_BLK * kBlockBytes;     // one group per stage
 constexpr int B_BYTES = B_BLK * kBlockBytes;
-constexpr int SA_BYTES = BM * 4, SW_BYTES = BN * 4;
-constexpr int STAGE_USED = A_BYTES + B_BYTES + SA_BYTES + SW_BYTES;   // 19968
-constexpr int UNITS = STAGE_USED / 16;                                 // 1248
-constexpr int WAVE_LOADS = (UNITS + 63) / 64;                          // 20
-constexpr int STAGE = WAVE_LOADS * 64 * 16;                            // 20480, padded
-constexpr int MAX_LOADS = WAVE_LOADS / NWAVES;                         // 5 per wave
-constexpr int NBUF = 4;                                                // stages in LDS
+// INT4 stage: A codes | B codes | weight-scale operands | activation-scale
+// operands, 24 loads of 1 KB (6 per wavefront); three stages rotate.
+constexpr int I4_SW_OFF = A_BYTES + B_BYTES;                    // 18432
+constexpr int I4_SA_OFF = I4_SW_OFF + BN * kScaleOpBytes;       // 22528
+constexpr int I4_STAGE = I4_SA_OFF + BM * kScaleOpBytes;        // 24576
+constexpr int I4_LOADS = I4_STAGE / 1024, I4_LOADS_W = I4_LOADS / NWAVES;   // 24, 6
+constexpr int I4_NBUF = 3;
+// after the stages: the low-rank staging of the prologue (8 KB), which the
+// main loop then uses as a zero area (lanes 32..63 of the weight-scale
+// operand read zeros there)
+constexpr int I4_AUX_OFF = I4_NBUF * I4_STAGE;                  // 73728
+constexpr int I4_ZERO_BYTES = 2048;
+// MXFP4 stage: one K-step's codes and E8M0 scales (13 KB) in 20 KB slots;
+// four rotate, the fourth holding the prologue's low-rank staging at first.
+constexpr int MX_STAGE = 20480, MX_NBUF = 4;
+constexpr int SMEM_BYTES = 80 * 1024;             // two workgroups per CU
 constexpr int GM = 8;             // tile-rows walked together on one XCD
 constexpr int EPI_WAVE_BYTES = 32 * WCOLS * 4;   // one 32-row half of a wavefront tile, fp32
-static_assert(STAGE_USED % 16 == 0, "stage must be whole 16-byte units");
-static_assert(WAVE_LOADS % NWAVES == 0, "every wavefront issues the same number of copies per stage");
-static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0 && SW_BYTES % 1024 == 0 && SA_BYTES == 512 &&
-              WAVE_LOADS * 1024 == A_BYTES + B_BYTES + SW_BYTES + 1024,
-              "each copy reads one array; sA is the upper half of the last");
-static_assert(2 * NBUF * STAGE <= 160 * 1024, "two workgroups must fit in one CU's LDS");
-static_assert(NWAVES * EPI_WAVE_BYTES <= NBUF * STAGE, "epilogue staging reuses the stages");
+static_assert(I4_STAGE % 1024 == 0 && I4_LOADS % NWAVES == 0, "whole 1 KB loads, equal per wavefront");
+static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0 && (BN * kScaleOpBytes) % 1024 == 0 &&
+              (BM * kScaleOpBytes) % 1024 == 0, "each load reads one array");
+static_assert(I4_AUX_OFF + 8192 <= SMEM_BYTES && MX_NBUF * MX_STAGE <= SMEM_BYTES, "stages fit");
+static_assert(2 * SMEM_BYTES <= 160 * 1024, "two workgroups must fit in one CU's LDS");
+static_assert(NWAVES * EPI_WAVE_BYTES <= SMEM_BYTES, "epilogue staging reuses the stages");
 }  // namespace k2c
 
 // The fp6 operand occupies six registers; the instruction's 8-register
@@ -474,36 +497,6 @@ __device__ __forceinline__ v8i mx_frag(const uint8_t *blk, int lane) {
   return r;
 }
 
-// Instruction order inside one step of K2's pipeline: the step's matrix
-// instruction first, then D1 LDS reads (operands it no longer needs), the
-// vector work, then D2 more LDS reads (scales the vector work has just used
-// for the last time), and a fence so nothing crosses into the next step.
-// This keeps the matrix core busy under the FMAs.
-template <int D1, int D2>
-__device__ __forceinline__ void k2_order() {
-  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  if constexpr (D1 > 0) __builtin_amdgcn_sched_group_barrier(0x100, D1, 0);
-  __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
-  if constexpr (D2 > 0) __builtin_amdgcn_sched_group_barrier(0x100, D2, 0);
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// As k2_order, for a step whose vector work swaps the activation scales for
-// the next row tile: each of the four float4 reads goes right after the FMAs
-// that last read the register it overwrites.
-template <int D1, int D2 = 0>
-__device__ __forceinline__ void k2_order_r() {
-  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  if constexpr (D1 > 0) __builtin_amdgcn_sched_group_barrier(0x100, D1, 0);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  if constexpr (D2 > 0) __builtin_amdgcn_sched_group_barrier(0x100, D2, 0);
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 template <int MODE, int EPI, bool OUT_F32, bool DFIX = false, bool QNEXT = false, bool SPLIT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_w4a4_gemm(K2Args p) {
   using namespace k2c;
@@ -524,7 +517,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tm = first_m + within % gm, tn = within / gm;
   const int bm = p.tile_m0 + tm * BM, bn = p.tile_n0 + tn * BN;
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM_BYTES];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int wu = __builtin_amdgcn_readfirstlane(w);      // wavefront index, scalar
   const int wmi = wu >> 1, wni = wu & 1;
@@ -542,44 +535,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int j = 0; j < WTN; ++j) acc[i][j] = v16f{};
 
-  // Copy schedule: a stage is WAVE_LOADS wavefront-loads of 64 x 16 bytes,
-  // A codes | B codes | sW | sA, each load from one array: wave w issues
-  // loads w, w + 4, w + 8, ... with every lane active; the last load's upper
-  // half repeats sA into the padding.  A load's source is a wave-uniform
-  // base (scalar registers) plus the lane's byte offset, and advances by one
-  // row of blocks (codes) or one row of the [G][Mp] / [G][Np] scale arrays
-  // from one group to the next.
+  // INT4 copy schedule: a stage is I4_LOADS wavefront-loads of 64 x 16
+  // bytes (A codes | B codes | weight-scale operands | activation-scale
+  // operands), each from one array: wave w issues loads w, w + 4, w + 8, ...
+  // with every lane active.  A load's source is a wave-uniform base (scalar
+  // registers) plus the lane's byte offset, and advances by one row of blocks
+  // (codes) or one row of the [G][Np] / [G][Mp] operand arrays per group.
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
-  const uint8_t *sbase[MAX_LOADS];
-  int64_t sstride[MAX_LOADS];
+  const uint8_t *sbase[I4_LOADS_W];
+  int64_t sstride[I4_LOADS_W];
 #pragma unroll
-  for (int r = 0; r < MAX_LOADS; ++r) {
+  for (int r = 0; r < I4_LOADS_W; ++r) {
     const int L = wu + NWAVES * r;               // load index within the stage
     if (L < A_BYTES / 1024) {
       sbase[r] = p.qa + (int64_t)(bm / kTile) * kBlockBytes + 1024 * L;
       sstride[r] = (int64_t)Ta * kBlockBytes;
-    } else if (L < (A_BYTES + B_BYTES) / 1024) {
+    } else if (L < I4_SW_OFF / 1024) {
       sbase[r] = p.qw + (int64_t)(bn / kTile) * kBlockBytes + 1024 * (L - A_BYTES / 1024);
       sstride[r] = (int64_t)Tw * kBlockBytes;
-    } else if (L < (A_BYTES + B_BYTES + SW_BYTES) / 1024) {
-      sbase[r] = reinterpret_cast<const uint8_t *>(p.sw + bn) + 1024 * (L - (A_BYTES + B_BYTES) / 1024);
-      sstride[r] = (int64_t)p.Np * 4;
+    } else if (L < I4_SA_OFF / 1024) {
+      sbase[r] = p.sw + (int64_t)bn * kScaleOpBytes + 1024 * (L - I4_SW_OFF / 1024);
+      sstride[r] = (int64_t)p.Np * kScaleOpBytes;
     } else {
-      sbase[r] = reinterpret_cast<const uint8_t *>(p.sa + bm);
-      sstride[r] = (int64_t)p.Mp * 4;
+      sbase[r] = p.sa + (int64_t)bm * kScaleOpBytes + 1024 * (L - I4_SA_OFF / 1024);
+      sstride[r] = (int64_t)p.Mp * kScaleOpBytes;
     }
     if constexpr (SPLIT) sbase[r] += g0 * sstride[r];   // loop indices count from g0
   }
   const uint32_t voff = 16u * lane;
-  const uint32_t voff_sa = 16u * (lane & 31);     // sA is half a load
   auto fetch = [&](int g) {
-    const uint32_t buf = smem_lds + (uint32_t)((g % NBUF) * STAGE) + (uint32_t)(wu * 64 * 16);
+    const uint32_t buf = smem_lds + (uint32_t)((g % I4_NBUF) * I4_STAGE) + (uint32_t)(wu * 1024);
 #pragma unroll
-    for (int r = 0; r < MAX_LOADS; ++r) {
-      const int L = wu + NWAVES * r;
-      lds_dma16_s(sbase[r] + g * sstride[r], (r == MAX_LOADS - 1 && L == WAVE_LOADS - 1) ? voff_sa : voff,
-                  buf + (uint32_t)(r * NWAVES * 64 * 16));
-    }
+    for (int r = 0; r < I4_LOADS_W; ++r)
+      lds_dma16_s(sbase[r] + g * sstride[r], voff, buf + (uint32_t)(r * NWAVES * 1024));
   };
 
   // MXFP4 stage of K-step g: A codes (4 tile blocks of 1 KB), B codes (8),
@@ -597,102 +585,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                               : p.sqa + (int64_t)(bm / kTile) * 64 + (lane & 15) * 16;
   const int64_t mx_scstep = sc_b ? (int64_t)Tw * 64 : (int64_t)Ta * 64;
   auto fetch_mx = [&](int g) {
-    const uint32_t buf = smem_lds + (uint32_t)((g % NBUF) * STAGE);
+    const uint32_t buf = smem_lds + (uint32_t)((g % MX_NBUF) * MX_STAGE);
     lds_dma16_s(mx_a + g * mx_astep, voff, buf + (uint32_t)(wu * 1024));
     lds_dma16_s(mx_b + g * mx_bstep, voff, buf + (uint32_t)((4 + wu) * 1024));
     lds_dma16_s(mx_b + g * mx_bstep + 4 * 1024, voff, buf + (uint32_t)((8 + wu) * 1024));
     if (wu == 0) lds_dma16(mx_sc + g * mx_scstep, buf + (uint32_t)(12 * 1024));
   };
 
-  // Operands of one group as a wavefront holds them in registers: the fp6
-  // codes of its row tiles and column tiles, the activation scales of the
-  // 16 rows each lane's accumulator elements belong to (per row tile: rows
-  // 8 q + 4 (lane / 32) + [0, 4), q = 0..3, four float4 reads), and the
-  // weight scale of the lane's column in each column tile.
-  struct Frags { v8i a[WTM], b[WTN]; float4 sa[4]; float sw[WTN]; };
-  Frags F;
-  auto stage_of = [&](int g) { return smem + (g % NBUF) * STAGE; };
-  auto load_a = [&](int g, int i) {
-    F.a[i] = k2_frag(stage_of(g) + (WTM * wmi + i) * kBlockBytes, lane);
-  };
-  auto load_b = [&](int g, int j) {
-    F.b[j] = k2_frag(stage_of(g) + A_BYTES + (WTN * wni + j) * kBlockBytes, lane);
-  };
-  auto sa_src = [&](int g, int i) {
-    return reinterpret_cast<const float4 *>(stage_of(g) + A_BYTES + B_BYTES + SW_BYTES) +
-           (WROWS * wmi + 32 * i + 4 * hl) / 4;
-  };
-  auto load_sw = [&](int g, int j) {
-    F.sw[j] = reinterpret_cast<const float *>(stage_of(g) + A_BYTES + B_BYTES)
-        [WCOLS * wni + 32 * j + ln];
-  };
-  // Per group each of the wavefront's 32 x 32 tiles t = (i, j) =
-  // (t / WTN, t % WTN) takes one fp6 product; its elements are then scaled
-  // by the fp32 product sA[m] sW[n] (one rounding) and accumulated with one
-  // FMA.
-  auto mm = [&](int t, v16f &P) {
-    const int i = t / WTN, j = t % WTN;
-    P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[i], F.b[j], v16f{}, 2, 2, 0, 127, 0, 127);
-  };
-  auto consume_impl = [&](int t, int g, const v16f &P, const float4 *next, auto swap) {
-    const int i = t / WTN, j = t % WTN;
-    if constexpr (MODE == MODE_SUMS) {
-      const int n = wn + 32 * j + ln;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = wm + 32 * i + 8 * (e >> 2) + 4 * hl + (e & 3);
-        if (m >= p.m0 && m < p.m0 + p.mcount && n >= p.n0 && n < p.n0 + p.ncount)
-          p.P[((int64_t)(m - p.m0) * p.ncount + (n - p.n0)) * G + g] = (int32_t)P[e];
-      }
-      if constexpr (decltype(swap)::value) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) F.sa[q] = next[2 * q];
-      }
-    } else {
-      const float swj = F.sw[j];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 sa4 = F.sa[q];
-        const float sv[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int e = 4 * q + k;
-          acc[i][j][e] = __builtin_fmaf(P[e], __fmul_rn(sv[k], swj), acc[i][j][e]);
-        }
-        if constexpr (decltype(swap)::value) F.sa[q] = next[2 * q];
-      }
-    }
-  };
-  // consume(t): scale and accumulate tile t.  consume_swap(t, next): the
-  // same, and each float4 of activation scales is replaced by the one at
-  // `next` (the next row tile's) as soon as its last FMA has read it.
-  auto consume = [&](int t, int g, const v16f &P) {
-    consume_impl(t, g, P, nullptr, std::false_type{});
-  };
-  auto consume_swap = [&](int t, int g, const v16f &P, const float4 *next) {
-    consume_impl(t, g, P, next, std::true_type{});
-  };
-  auto mm_hi = [&](int t, v16f &P) {
-    __builtin_amdgcn_s_setprio(1);
-    mm(t, P);
-    __builtin_amdgcn_s_setprio(0);
-  };
+  auto stage_of = [&](int g) { return smem + (g % MX_NBUF) * MX_STAGE; };
+  auto stage_i4 = [&](int g) { return smem + (g % I4_NBUF) * I4_STAGE; };
 
-  // Software pipeline over (group, tile): while the FMAs of tile t run on
-  // the vector ALU, the matrix core works on tile t + 1 (the next group's
-  // first tile after the last).  Each operand of group g + 1 is read from
-  // LDS into its registers right after the last instruction of group g that
-  // uses it; the activation scales are held for one row tile at a time and
-  // swapped float4 by float4 inside the last tile that reads them.  The
-  // matrix instructions are issued at raised wave priority so the SIMD's
-  // other wavefront does not delay them.  One barrier per group; three of
-  // the four buffers hold stages g, g + 1, g + 2 while stage g + 3 is being
-  // requested.  The scheduling fences keep each step's products from being
-  // hoisted above the FMAs that still read the registers they overwrite.
-  // After the last group the loads and the first product still run, on a
-  // stale but in-bounds LDS buffer, and their results are never used:
-  // branch-free code keeps the operands and products in fixed registers.
-  v16f Pa, Pb;
   for (int g = 0; g < 3 && g < G; ++g) {
     if constexpr (MODE == MODE_MX) fetch_mx(g); else fetch(g);
   }
@@ -708,9 +610,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // loads issued four splits at a time, indices clamped, surplus ones not
     // added) and stores the two bf16 parts; every wavefront then reads its
     // operands from there.
-    uint16_t *dhi = reinterpret_cast<uint16_t *>(smem + 3 * STAGE);   // [BM][32]
-    uint16_t *dlo = dhi + BM * 32;                                     // [BM][32]
-    static_assert(BM * 32 * 2 * 2 <= STAGE, "low-rank staging fits one stage buffer");
+    // The staging is the fourth MXFP4 stage buffer (16 KB: 32 ranks at a
+    // time) or, for INT4, whose three stages are all in flight, the 8 KB
+    // after them (16 ranks at a time: the two halves of each 32-rank chunk
+    // pass through it in turn).
+    constexpr bool HALF = MODE != MODE_MX;
+    constexpr int RS = HALF ? 16 : 32;                                  // staging row, bf16
+    uint16_t *dhi = reinterpret_cast<uint16_t *>(smem + (HALF ? I4_AUX_OFF : 3 * MX_STAGE));
+    uint16_t *dlo = dhi + BM * RS;
+    static_assert(BM * 16 * 2 * 2 <= SMEM_BYTES - I4_AUX_OFF && BM * 32 * 2 * 2 <= MX_STAGE,
+                  "low-rank staging fits");
     const int rloc = 32 * wu + (lane >> 1), k0 = 16 * (lane & 1);
     for (int c2 = split; c2 < p.rp / 32; c2 += SPLIT ? p.ksplit : 1) {
       float d[16];
@@ -757,32 +666,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         hw[e] = h0 | (h1 << 16);
         lw[e] = l0 | (l1 << 16);
       }
-      uint4 *hp = reinterpret_cast<uint4 *>(dhi + rloc * 32 + k0);
-      uint4 *lp = reinterpret_cast<uint4 *>(dlo + rloc * 32 + k0);
-      hp[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]); hp[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
-      lp[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]); lp[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
       uint4 bw[2][WTN];
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int j = 0; j < WTN; ++j)
           bw[cc][j] = *reinterpret_cast<const uint4 *>(p.l2t + (int64_t)(wn + 32 * j + ln) * p.rp + 32 * c2 + 16 * cc + 8 * hl);
-      __syncthreads();
 #pragma unroll
-      for (int i = 0; i < WTM; ++i) {
-        const int r = WROWS * wmi + 32 * i + ln;
+      for (int pass = 0; pass < (HALF ? 2 : 1); ++pass) {
+        if (!HALF || (lane & 1) == pass) {
+          uint4 *hp = reinterpret_cast<uint4 *>(dhi + rloc * RS + (HALF ? 0 : k0));
+          uint4 *lp = reinterpret_cast<uint4 *>(dlo + rloc * RS + (HALF ? 0 : k0));
+          hp[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]); hp[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+          lp[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]); lp[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+        }
+        __syncthreads();
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const v8bf ah = as_v8bf(*reinterpret_cast<const uint4 *>(dhi + r * 32 + 16 * cc + 8 * hl));
-          const v8bf al = as_v8bf(*reinterpret_cast<const uint4 *>(dlo + r * 32 + 16 * cc + 8 * hl));
+        for (int i = 0; i < WTM; ++i) {
+          const int r = WROWS * wmi + 32 * i + ln;
 #pragma unroll
-          for (int j = 0; j < WTN; ++j) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, as_v8bf(bw[cc][j]), acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, as_v8bf(bw[cc][j]), acc[i][j], 0, 0, 0);
+          for (int cc = (HALF ? pass : 0); cc < (HALF ? pass + 1 : 2); ++cc) {
+            const int col = (HALF ? 0 : 16 * cc) + 8 * hl;
+            const v8bf ah = as_v8bf(*reinterpret_cast<const uint4 *>(dhi + r * RS + col));
+            const v8bf al = as_v8bf(*reinterpret_cast<const uint4 *>(dlo + r * RS + col));
+#pragma unroll
+            for (int j = 0; j < WTN; ++j) {
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, as_v8bf(bw[cc][j]), acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, as_v8bf(bw[cc][j]), acc[i][j], 0, 0, 0);
+            }
           }
         }
+        __syncthreads();                 // staging free for the next ranks
       }
-      __syncthreads();                   // staging free for the next 32 ranks
     }
   }
   if constexpr (MODE == MODE_MX) {
@@ -831,60 +746,106 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       mx_load(g + 1);
     }
   } else {
-  if (G > 2) vmcnt_wait<MAX_LOADS>(); else vmcnt_wait0();
-  __syncthreads();
-  load_a(0, 0); load_a(0, 1);
-#pragma unroll
-  for (int j = 0; j < WTN; ++j) { load_b(0, j); load_sw(0, j); }
-  {
-    const float4 *s0 = sa_src(0, 0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) F.sa[q] = s0[2 * q];
-  }
-  mm(0, Pa);
-  for (int g = 0; g < G; ++g) {
-    // Every wavefront waits for its copies of stage g + 1 (stage g + 2 may
-    // still be in flight) and meets the others; stage g - 1 has then been
-    // read by all of them, so its buffer takes stage g + 3.
-    if (g + 1 < G) {
-      if (MODE == MODE_FWD && g + 2 < G) vmcnt_wait<MAX_LOADS>(); else vmcnt_wait0();
-      __syncthreads();
-      if (g + 3 < G) fetch(g + 3);
+    // INT4 main loop.  Per group and 32 x 32 tile (i, j) of the wavefront:
+    //   P  = fp6 matrix instruction on the codes (unit block scales): the
+    //        exact integer group sums
+    //   S  = bf16 matrix instruction on the scale operands: sA[m] sW[n]
+    //        from the exact bf16 pieces of both scales
+    //   acc = fma(P, S, acc)            (one vector instruction per element)
+    // The scale product runs on the matrix core, which the codes alone leave
+    // mostly idle, so the vector ALU does one instruction per element and
+    // group instead of two.  Each operand of group g + 1 is read from LDS
+    // right after the last matrix instruction of group g that uses it; the
+    // SIMD's other wavefront covers the wait for each tile's products.
+    // Lanes 32..63 of the weight-scale operand (K slots 8..15) read the zero
+    // area after the stages, so those slots contribute nothing.  One barrier
+    // per group: every wavefront waits for its copies of stage g + 1 and for
+    // its own LDS reads of stage g, meets the others, and requests stage
+    // g + 3 into stage g's buffer.  After the last group the reads of "group
+    // G" run on a stale but in-bounds buffer and are never used.
+    v8i fa[WTM], fb[WTN];
+    v8bf xa[WTM], xb[WTN];
+    if constexpr (MODE == MODE_FWD) {
+      // the zero area (the prologue's staging until now)
+      reinterpret_cast<uint2 *>(smem + I4_AUX_OFF)[tid] = make_uint2(0u, 0u);
+      static_assert(THREADS * 8 == I4_ZERO_BYTES && 3 * 512 + 16 <= I4_ZERO_BYTES, "zero area");
     }
-    mm_hi(1, Pb);                         // tile (0,1)
-    consume(0, g, Pa);
-    k2_order<0, 0>();
-    mm_hi(2, Pa);                         // tile (0,2)
-    consume(1, g, Pb);
-    k2_order<0, 0>();
-    mm_hi(3, Pb);                         // tile (0,3): last use of a0
-    load_a(g + 1, 0);
-    consume(2, g, Pa);
-    k2_order<3, 0>();
-    mm_hi(4, Pa);                         // tile (1,0): last use of b0
-    load_b(g + 1, 0);
-    consume_swap(3, g, Pb, sa_src(g, 1));      // row-0 scales give way to row 1
-    k2_order_r<3>();
-    mm_hi(5, Pb);                         // tile (1,1): last use of b1
-    load_b(g + 1, 1);
-    consume(4, g, Pa);           // last use of sw0
-    load_sw(g + 1, 0);
-    k2_order<3, 1>();
-    mm_hi(6, Pa);                         // tile (1,2): last use of b2
-    load_b(g + 1, 2);
-    consume(5, g, Pb);           // last use of sw1
-    load_sw(g + 1, 1);
-    k2_order<3, 1>();
-    mm_hi(7, Pb);                         // tile (1,3): last use of a1, b3
-    load_a(g + 1, 1); load_b(g + 1, 3);
-    consume(6, g, Pa);           // last use of sw2
-    load_sw(g + 1, 2);
-    k2_order<6, 1>();
-    mm_hi(0, Pa);                         // next group's tile (0,0)
-    consume_swap(7, g, Pb, sa_src(g + 1, 0));  // row-1 scales give way to the next group's row 0
-    load_sw(g + 1, 3);
-    k2_order_r<0, 1>();
+    const bool lo_half = lane < 32;
+    auto ld_a = [&](int g, int i) {
+      const uint8_t *st = stage_i4(g);
+      fa[i] = k2_frag(st + (WTM * wmi + i) * kBlockBytes, lane);
+      if constexpr (MODE == MODE_FWD)
+        xa[i] = as_v8bf(*reinterpret_cast<const uint4 *>(st + I4_SA_OFF + (WROWS * wmi + 32 * i + ln) * kScaleOpBytes));
+    };
+    auto ld_b = [&](int g, int j) {
+      const uint8_t *st = stage_i4(g);
+      fb[j] = k2_frag(st + A_BYTES + (WTN * wni + j) * kBlockBytes, lane);
+      if constexpr (MODE == MODE_FWD) {
+        const uint8_t *xp = lo_half ? st + I4_SW_OFF + (WCOLS * wni + ln) * kScaleOpBytes : smem + I4_AUX_OFF;
+        xb[j] = as_v8bf(*reinterpret_cast<const uint4 *>(xp + 32 * kScaleOpBytes * j));
+      }
+    };
+    auto sums_store = [&](int g, int i, int j, const v16f &P) {
+      const int n = wn + 32 * j + ln;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = wm + 32 * i + 8 * (e >> 2) + 4 * hl + (e & 3);
+        if (m >= p.m0 && m < p.m0 + p.mcount && n >= p.n0 && n < p.n0 + p.ncount)
+          p.P[((int64_t)(m - p.m0) * p.ncount + (n - p.n0)) * G + g] = (int32_t)P[e];
+      }
+    };
+    // One step of the pipeline for tile t = (i, j): the scale product of
+    // tile t and the group sums of the next tile (i2, j2) go to the matrix
+    // core, then the reads of group g + 1 that this step frees (NDS LDS
+    // instructions), then tile t's FMAs, which wait only for the scale
+    // product: the next tile's group sums run under them.  P holds the
+    // current and the next tile's sums.  The fences keep that order.
+#define I4_STEP(i, j, i2, j2, NDS, LOADS)                                                      \
+  {                                                                                           \
+    if constexpr (MODE == MODE_SUMS) {                                                        \
+      P[(i2 * WTN + j2) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                \
+          fa[i2], fb[j2], v16f{}, 2, 2, 0, 127, 0, 127);                                      \
+      LOADS;                                                                                  \
+      sums_store(g, i, j, P[(i * WTN + j) & 1]);                                              \
+    } else {                                                                                  \
+      const v16f Sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], v16f{}, 0, 0, 0); \
+      P[(i2 * WTN + j2) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                \
+          fa[i2], fb[j2], v16f{}, 2, 2, 0, 127, 0, 127);                                      \
+      LOADS;                                                                                  \
+      _Pragma("unroll") for (int e = 0; e < 16; ++e)                                          \
+          acc[i][j][e] = __builtin_fmaf(P[(i * WTN + j) & 1][e], Sx[e], acc[i][j][e]);        \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                      \
+      if (NDS > 0) __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);                       \
+      __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);                                     \
+    }                                                                                         \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
   }
+    v16f P[2];
+    if (MODE == MODE_FWD && G > 2) vmcnt_wait<I4_LOADS_W>(); else vmcnt_wait0();
+    __syncthreads();
+    ld_a(0, 0); ld_a(0, 1);
+#pragma unroll
+    for (int j = 0; j < WTN; ++j) ld_b(0, j);
+    P[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[0], fb[0], v16f{}, 2, 2, 0, 127, 0, 127);
+    for (int g = 0; g < G; ++g) {
+      if (g + 1 < G) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wavefront is done reading stage g
+        if (MODE == MODE_FWD && g + 2 < G) vmcnt_wait<I4_LOADS_W>(); else vmcnt_wait0();
+        __syncthreads();
+        if (g + 3 < G) fetch(g + 3);
+      }
+      I4_STEP(0, 0, 0, 1, 0, );
+      I4_STEP(0, 1, 0, 2, 0, );
+      I4_STEP(0, 2, 0, 3, 0, );
+      I4_STEP(0, 3, 1, 0, 4, ld_a(g + 1, 0));              // a0 last read by (0,3)'s sums
+      I4_STEP(1, 0, 1, 1, 4, ld_b(g + 1, 0));              // b0 by (1,0)'s
+      I4_STEP(1, 1, 1, 2, 4, ld_b(g + 1, 1));
+      I4_STEP(1, 2, 1, 3, 4, ld_b(g + 1, 2));
+      // the next group's first sums (after the last group: a stale but
+      // in-bounds buffer, never used)
+      I4_STEP(1, 3, 0, 0, 8, ld_a(g + 1, 1); ld_b(g + 1, 3));
+    }
+#undef I4_STEP
   }  // INT4 main loop
 
   if constexpr (SPLIT) {
@@ -951,7 +912,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         lf[j] = *reinterpret_cast<const uint4 *>(p.l1f2 + ((((int64_t)g2 * TB2 + b) * 4 + j) * 64 + lane) * 8);
     };
     float *exch = reinterpret_cast<float *>(smem + NWAVES * EPI_WAVE_BYTES);   // [4][16][64]
-    static_assert(NWAVES * EPI_WAVE_BYTES + NWAVES * 16 * 64 * 4 <= NBUF * STAGE, "exchange fits");
+    static_assert(NWAVES * EPI_WAVE_BYTES + NWAVES * 16 * 64 * 4 <= SMEM_BYTES, "exchange fits");
     auto finish = [&](int b, const v16f (&dacc)[WTM]) {
       // wavefront (wmi, wni) finishes row tile wni of its pair's rows
 #pragma unroll
@@ -994,7 +955,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int j = 0; j < 3; ++j)
           *reinterpret_cast<uint2 *>(qp + 512 * j) = make_uint2(packed[2 * j], packed[2 * j + 1]);
-        p.sa2[(int64_t)g2 * p.Mp + wm + 32 * i + rr] = sc;   // both halves hold the same scale
+        if (h == 0)                                           // both halves hold the same scale
+          reinterpret_cast<uint4 *>(p.sa2)[(int64_t)g2 * p.Mp + wm + 32 * i + rr] = scale_row_operand(sc);
         if (TB2 > 0) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
@@ -1468,12 +1430,14 @@ __global__ void canon_codes_kernel(const uint8_t *__restrict__ qa, int M, int K,
   out[idx] = (uint8_t)(((uint32_t)code[0] & 0x0Fu) | (((uint32_t)code[1] & 0x0Fu) << 4));
 }
 
-__global__ void canon_scales_kernel(const float *__restrict__ sa, int M, int Mp, int G,
+// fp32 scale of (m, g) from its operand form: a1 + a2 + a3, exact
+__global__ void canon_scales_kernel(const uint4 *__restrict__ sa, int M, int Mp, int G,
                                     float *__restrict__ out) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)M * G) return;
   const int64_t m = idx / G, g = idx % G;
-  out[idx] = sa[g * Mp + m];
+  const uint4 v = sa[g * Mp + m];
+  out[idx] = (__uint_as_float(v.x << 16) + __uint_as_float(v.y & 0xFFFF0000u)) + __uint_as_float(v.w << 16);
 }
 
 // MXFP4 codes and scales of the workspace -> canonical [M, K/2] bytes and
@@ -1590,13 +1554,13 @@ K2Args make_k2_args(const WeightLayout &L, const WorkLayout &Wl, const svdq_weig
   const uint8_t *blob = static_cast<const uint8_t *>(w->blob);
   K2Args a{};
   a.qa = ws + Wl.qa;
-  a.sa = reinterpret_cast<const float *>(ws + Wl.sa);
+  a.sa = ws + Wl.sa;
   a.dpart = reinterpret_cast<const float *>(ws + Wl.d);
   a.S = (int)Wl.S;
   a.M = M;
   a.Mp = (int)Wl.Mp;
   a.qw = blob + L.q;
-  a.sw = reinterpret_cast<const float *>(blob + L.s);
+  a.sw = blob + L.s;
   a.l2t = reinterpret_cast<const uint16_t *>(blob + L.l2t);
   a.bias = reinterpret_cast<const float *>(blob + L.bias);
   a.N = w->N;
@@ -1921,7 +1885,7 @@ svdq_status_t svdq_quantize_activations(const svdq_weights_t *w, const void *X, 
                      ws + Wl.qa, M, w->K, (int)(Wl.Mp / kTile), qact);
   const int64_t ns = (int64_t)M * Wl.G;
   hipLaunchKernelGGL(canon_scales_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, stream,
-                     reinterpret_cast<const float *>(ws + Wl.sa), M, (int)Wl.Mp, (int)Wl.G, ascales);
+                     reinterpret_cast<const uint4 *>(ws + Wl.sa), M, (int)Wl.Mp, (int)Wl.G, ascales);
   if (w->rank > 0) {
     const int64_t nd = (int64_t)M * w->rank;
     hipLaunchKernelGGL(canon_down_kernel, dim3((unsigned)((nd + 255) / 256)), dim3(256), 0, stream,

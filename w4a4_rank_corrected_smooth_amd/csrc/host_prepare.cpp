@@ -18,6 +18,28 @@
 namespace svdq {
 
 // ------------------------------------------------------------ conversions
+// s = p0 + p1 + p2 exactly, each a bf16: p0 is s with the low 16 bits of
+// its encoding cleared, p1 the same of the remainder, p2 the rest (at most
+// 8 significant bits).  Every subtraction is exact.
+void split_scale_bf16x3(float s, uint16_t p[3]) {
+  uint32_t u;
+  std::memcpy(&u, &s, 4);
+  float a1, r, a2, a3;
+  const uint32_t u1 = u & 0xFFFF0000u;
+  std::memcpy(&a1, &u1, 4);
+  r = s - a1;
+  uint32_t ur;
+  std::memcpy(&ur, &r, 4);
+  const uint32_t u2 = ur & 0xFFFF0000u;
+  std::memcpy(&a2, &u2, 4);
+  a3 = r - a2;
+  uint32_t u3;
+  std::memcpy(&u3, &a3, 4);
+  p[0] = (uint16_t)(u >> 16);
+  p[1] = (uint16_t)(ur >> 16);
+  p[2] = (uint16_t)(u3 >> 16);
+}
+
 float f16_to_f32(uint16_t h) {
   const uint32_t sign = (uint32_t)(h & 0x8000) << 16;
   const uint32_t e = (h >> 10) & 0x1F, m = h & 0x3FF;
@@ -295,9 +317,17 @@ svdq_status_t pack_device_weights(const svdq_host_weights_t *in, void *host_blob
             std::memcpy(q + pair_offset(g, t, T, lane, j), &w[2 * j], 8);
         }
   });
-  float *s = reinterpret_cast<float *>(b + L.s);
+  // weight scales as the column operand of the GEMM's scale product:
+  // b1 b2 b3 b1 b2 b3 b1 b2 (bf16), s = b1 + b2 + b3 exactly (layout.h)
+  uint16_t *s = reinterpret_cast<uint16_t *>(b + L.s);
   for (int64_t n = 0; n < N; ++n)
-    for (int64_t g = 0; g < L.G; ++g) s[g * L.Np + n] = in->wscales[n * L.G + g];
+    for (int64_t g = 0; g < L.G; ++g) {
+      uint16_t p[3];
+      split_scale_bf16x3(in->wscales[n * L.G + g], p);
+      uint16_t *o = s + (g * L.Np + n) * (kScaleOpBytes / 2);
+      const int order[8] = {0, 1, 2, 0, 1, 2, 0, 1};
+      for (int e = 0; e < 8; ++e) o[e] = p[order[e]];
+    }
   uint16_t *l2t = reinterpret_cast<uint16_t *>(b + L.l2t);
   uint16_t *l1t = reinterpret_cast<uint16_t *>(b + L.l1t);
   for (int64_t t = 0; t < r; ++t) {

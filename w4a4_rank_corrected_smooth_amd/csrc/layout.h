@@ -62,6 +62,18 @@ constexpr int int_of_e2m3(uint32_t v) {
   return (v & 0x20u) ? -mag : mag;
 }
 
+// Group scales are stored as matrix-core operands.  A float32 scale s splits
+// exactly into three bf16 pieces, s = s1 + s2 + s3: s1 = s with the low 16
+// bits of its encoding cleared, s2 the same of s - s1, s3 = s - s1 - s2
+// (each subtraction exact; s3 has at most 8 significant bits).  The GEMM
+// forms sA sW for a 32 x 32 tile with one bf16 matrix instruction whose
+// eight K slots (lanes 0..31) hold
+//     activation row m:   a1 a1 a1 a2 a2 a2 a3 a3
+//     weight column n:    b1 b2 b3 b1 b2 b3 b1 b2
+// so the sum of the eight exact products is sA sW - a3 b3 (a3 b3 < 2^-32
+// sA sW).  Each row or column takes 16 bytes: the bf16 values in that order.
+constexpr int kScaleOpBytes = 16;
+
 // The down-projection factor L1s [K][rp] is stored in the order in which the
 // quantiser's matrix instruction consumes it (B operand of a 32x32x16 bf16
 // product, one 32-rank block b at a time): for group g, block b and 16-channel
@@ -82,7 +94,7 @@ struct WeightLayout {
         G(K_ / kGroup) {
     int64_t o = 0;
     q = o;    o = round_up(o + Np * K * 3 / 4, kAlign);  // fp6 codes, tiled
-    s = o;    o = round_up(o + G * Np * 4, kAlign);      // fp32 scales [G][Np]
+    s = o;    o = round_up(o + G * Np * kScaleOpBytes, kAlign);   // scale operands [G][Np]
     l2t = o;  o = round_up(o + Np * rp * 2, kAlign);     // bf16 L2^T [Np][rp]
     l1t = o;  o = round_up(o + rp * K * 2, kAlign);      // bf16 L1s, MFMA fragment order (l1_frag_index)
     iota = o; o = round_up(o + K * 4, kAlign);           // fp32 1/lambda [K]
@@ -116,7 +128,7 @@ struct WorkLayout {
         S(k1_splits(round_up(M_, kPad), K_ / kGroup)) {
     int64_t o = 0;
     qa = o; o = round_up(o + Mp * K * 3 / 4, kAlign);    // fp6 codes, tiled
-    sa = o; o = round_up(o + G * Mp * 4, kAlign);        // fp32 scales [G][Mp]
+    sa = o; o = round_up(o + G * Mp * kScaleOpBytes, kAlign);   // scale operands [G][Mp]
     // D = X L1s: either fp32 partials [S][Mp][rp] from the quantiser, or,
     // when the previous layer's GEMM quantised this layer's input in its
     // epilogue, one int64 fixed-point sum [Mp][rp] (units of 2^-32)
