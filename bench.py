@@ -682,6 +682,64 @@ def footprint(S, layers, awq_case):
     return out
 
 
+def branch_fusion(S, dev, stream, layers):
+    """What fusing the low-rank branch saves: each layer's forward (K1 with
+    the down-projection + K2 with the up-projection) against the same layer
+    with the branch as two separate bf16 GEMMs and the 4-bit GEMM's fp32
+    result through memory (svdq_linear_forward_unfused), both timed back to
+    back over two buffer sets."""
+    import torch
+    out = {}
+    for name, layer, Xs, gelu in layers:
+        M = Xs[0].shape[0]
+        Ys = [torch.empty((M, layer.N), dtype=torch.bfloat16, device=dev) for _ in Xs]
+        wf = [layer.new_workspace(M) for _ in Xs]
+        wu = [torch.empty(S.unfused_workspace_bytes(M, layer.N, layer.K, layer.rank), dtype=torch.uint8,
+                          device=dev) for _ in Xs]
+        R = len(Xs)
+        fused = back_to_back(lambda i: S.linear_forward(layer, Xs[i % R], out=Ys[i % R], gelu=gelu,
+                                                        workspace=wf[i % R]), stream, n=10)
+        unfused = back_to_back(lambda i: S.linear_forward_unfused(layer, Xs[i % R], out=Ys[i % R], gelu=gelu,
+                                                                  workspace=wu[i % R]), stream, n=10)
+        out[name] = {"M": M, "N": layer.N, "K": layer.K, "rank": layer.rank, "fused_us": round(fused, 2),
+                     "unfused_us": round(unfused, 2), "fusion_saves": round(1 - fused / unfused, 4)}
+        del Ys, wf, wu
+        torch.cuda.empty_cache()
+    return out
+
+
+def branch_ablation_mode(args):
+    """bench.py --branch-ablation: only the fused-against-unfused branch
+    timings (QKV, fc1 + GELU, fc2, low-res rank 128), one JSON line; under a
+    kernel trace it gives each unfused kernel's duration."""
+    import numpy as np
+    import torch
+    import synth
+    import w4a4_rank_corrected_smooth_amd as S
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    S.device_check()
+    stream = torch.cuda.current_stream(dev)
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+    log("preparing QKV, fc1, fc2 and the low-res layer on the host")
+    qc, lc = synth.qkv_case(), synth.lowres_case()
+    fc1, W2, b2 = synth.mlp_cases()
+    L1 = S.Linear(S.prepare_weights(fc1.W, fc1.calib_absmax(), fc1.bias, 32), dev)
+    x1 = [dev_bf16(fc1.X) for _ in range(2)]
+    y1 = S.linear_forward(L1, x1[0], out_dtype=torch.bfloat16, gelu=True)
+    torch.cuda.synchronize()
+    ax2 = S.calibration_absmax(y1[:64].cpu().view(torch.int16).numpy().view(np.uint16))
+    L2 = S.Linear(S.prepare_weights(W2, ax2, b2, 32), dev)
+    Lq = S.Linear(S.prepare_weights(qc.W, qc.calib_absmax(), qc.bias, 32), dev)
+    Ll = S.Linear(S.prepare_weights(lc.W, lc.calib_absmax(), lc.bias, 128), dev)
+    res = branch_fusion(S, dev, stream, [("qkv", Lq, [dev_bf16(qc.X) for _ in range(2)], False),
+                                         ("fc1_gelu", L1, x1, True), ("fc2", L2, [y1, y1.clone()], False),
+                                         ("lowres_r128", Ll, [dev_bf16(lc.X) for _ in range(2)], False)])
+    print(json.dumps({"study": "branch_fusion", "layers": res}), flush=True)
+
+
 def hbm_floor(args):
     """The practical HBM rate at the bandwidth-bound kernels' own sizes and
     grids: a plain streaming read (and copy) of the quantiser's input (4608 x
@@ -743,6 +801,8 @@ def main():
                     help="CPU only: summarise a rocprofv3 --pmc pass of the shader counters into profiles/")
     ap.add_argument("--block", action="store_true",
                     help="launch study of one transformer block's calls, eager and as a HIP graph")
+    ap.add_argument("--branch-ablation", action="store_true",
+                    help="fused against unfused low-rank branch at QKV, fc1, fc2 and low-res (one JSON line)")
     ap.add_argument("--hbm-floor", action="store_true",
                     help="streaming read/copy rates at the quantiser's and W4A16 kernel's sizes and grids")
     ap.add_argument("--summarize-configs", nargs=2, metavar=("TRACE_DIR", "SWEEP_JSONL"),
@@ -779,6 +839,9 @@ def main():
         return
     if args.hbm_floor:
         hbm_floor(args)
+        return
+    if args.branch_ablation:
+        branch_ablation_mode(args)
         return
 
     import numpy as np
@@ -905,6 +968,21 @@ def main():
         del Xb, wsb, Ab
         torch.cuda.empty_cache()
 
+    branch = None
+    if not args.skip_unfused:
+        log("branch fusion ablation: QKV, fc1, fc2, low-res r128 fused and unfused")
+        qc, lc = synth.qkv_case(), synth.lowres_case()
+        Lq = S.Linear(S.prepare_weights(qc.W, qc.calib_absmax(), qc.bias, 32), dev)
+        Ll = S.Linear(S.prepare_weights(lc.W, lc.calib_absmax(), lc.bias, 128), dev)
+        xq = [dev_bf16(qc.X) for _ in range(2)]
+        xl = [dev_bf16(lc.X) for _ in range(2)]
+        S.linear_forward(L1[0], X[0], out=Y1[0], gelu=True, workspace=ws1[0])
+        branch = branch_fusion(S, dev, stream, [("qkv", Lq, xq, False), ("fc1_gelu", L1[0], X[:2], True),
+                                                ("fc2", L2[0], [Y1[0], Y1[0].clone()], False),
+                                                ("lowres_r128", Ll, xl, False)])
+        del Lq, Ll, xq, xl
+        torch.cuda.empty_cache()
+
     mx = None
     if not args.skip_mx:
         mx = mx_pair(args, S, fc1, W2, b2, ax2, X, R, dev, stream)
@@ -972,6 +1050,7 @@ def main():
                           "value": round(2 * ops_layer / (wall_unfused / args.steps) / 1e12, 2),
                           "fused_again_ms_per_step": round(wall_fused2 / args.steps * 1e3, 4)}),
         "weights_mb": footprint(S, [("fc1", N1, K1, 32), ("fc2", N2, K2, 32)], a),
+        "branch_fusion": branch,
         "mxfp4_pair": mx,
         "prepare_s": {"fc1": round(prep1, 2), "fc2": round(prep2, 2)},
         "source_hash": source_hash(),

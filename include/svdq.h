@@ -212,6 +212,23 @@ svdq_status_t svdq_linear_forward_static(const svdq_weights_t *w, const void *X,
                                          void *Y, svdq_dtype_t y_dtype,
                                          svdq_epilogue_t epilogue, void *hip_stream);
 
+/* The same forward with the 16-bit branch unfused, for measuring what the
+ * fusion saves (the pages credit the original engine with fusing the
+ * down-projection into the quantiser and the up-projection into the 4-bit
+ * GEMM, Korean edition, section "SVDQuant 및 Nunchaku 엔진").  Four
+ * kernels: the quantiser without the down-projection; D = X L1s as its own
+ * bf16 GEMM (D to memory); the 4-bit GEMM without the up-projection, its
+ * fp32 result (bias included) to memory; Y = epilogue(that + D L2) as a
+ * second bf16 GEMM.  Same arguments, results (up to the order of fp32
+ * additions) and errors as svdq_linear_forward; the workspace must hold
+ * svdq_unfused_workspace_bytes(M, N, K, rank) bytes (the forward's, plus
+ * the fp32 result [M, N]). */
+size_t svdq_unfused_workspace_bytes(int M, int N, int K, int rank);
+svdq_status_t svdq_linear_forward_unfused(const svdq_weights_t *w, const void *X, int M,
+                                          void *Y, svdq_dtype_t y_dtype,
+                                          svdq_epilogue_t epilogue, void *workspace,
+                                          size_t ws_bytes, void *hip_stream);
+
 /* The forward's two kernels as separate calls, for callers that time or
  * schedule them apart.  svdq_linear_quantize runs kernel (1) on X and leaves
  * the activation codes, scales and low-rank partials in `workspace`;

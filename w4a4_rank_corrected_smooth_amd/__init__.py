@@ -40,7 +40,8 @@ EXPORTS = [
     "svdq_abi_version", "svdq_status_string", "svdq_last_error", "svdq_device_check",
     "svdq_host_weights_sizes", "svdq_calibration_absmax", "svdq_prepare_weights",
     "svdq_device_weights_bytes", "svdq_pack_device_weights", "svdq_workspace_bytes",
-    "svdq_linear_forward", "svdq_linear_forward_static", "svdq_linear_quantize", "svdq_linear_gemm", "svdq_mlp_forward",
+    "svdq_linear_forward", "svdq_linear_forward_static", "svdq_linear_quantize",
+    "svdq_unfused_workspace_bytes", "svdq_linear_forward_unfused", "svdq_linear_gemm", "svdq_mlp_forward",
     "svdq_mlp_quantize", "svdq_mlp_gemm1", "svdq_mlp_gemm2", "svdq_gelu_tanh_bf16",
     "svdq_quantize_activations",
     "svdq_debug_group_sums", "awq_quantize_weights", "awq_device_weights_bytes",
@@ -87,6 +88,8 @@ _sig("svdq_pack_device_weights", _i, [ctypes.POINTER(HostWeights), _vp, _sz])
 _sig("svdq_workspace_bytes", _sz, [_i, _i, _i, _i])
 _sig("svdq_linear_forward", _i, [ctypes.POINTER(DeviceWeights), _vp, _i, _vp, _i, _i, _vp, _sz, _vp])
 _sig("svdq_linear_forward_static", _i, [ctypes.POINTER(DeviceWeights), _vp, _i, _vp, _i, _i, _vp])
+_sig("svdq_unfused_workspace_bytes", _sz, [_i, _i, _i, _i])
+_sig("svdq_linear_forward_unfused", _i, [ctypes.POINTER(DeviceWeights), _vp, _i, _vp, _i, _i, _vp, _sz, _vp])
 _sig("svdq_linear_quantize", _i, [ctypes.POINTER(DeviceWeights), _vp, _i, _vp, _sz, _vp])
 _sig("svdq_linear_gemm", _i, [ctypes.POINTER(DeviceWeights), _i, _vp, _i, _i, _vp, _sz, _vp])
 _sig("svdq_gelu_tanh_bf16", _i, [_vp, _vp, _sz, _vp])
@@ -306,6 +309,34 @@ def linear_forward(layer: Linear, X: torch.Tensor, out: Optional[torch.Tensor] =
                                     EPILOGUE_GELU_TANH if gelu else EPILOGUE_NONE,
                                     workspace.data_ptr(), workspace.numel(), _stream(X.device)),
            "svdq_linear_forward")
+    return out
+
+
+def unfused_workspace_bytes(M: int, N: int, K: int, rank: int) -> int:
+    n = _lib.svdq_unfused_workspace_bytes(M, N, K, rank)
+    if n == 0:
+        raise SvdqError(2, "svdq_unfused_workspace_bytes")
+    return n
+
+
+def linear_forward_unfused(layer: Linear, X: torch.Tensor, out: Optional[torch.Tensor] = None,
+                           out_dtype=torch.bfloat16, gelu: bool = False,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """svdq_linear_forward_unfused: the forward with the low-rank branch as
+    two separate bf16 GEMMs (the fusion ablation)."""
+    assert X.dtype == torch.bfloat16 and X.is_contiguous() and X.shape[1] == layer.K
+    M = X.shape[0]
+    if out is None:
+        out = torch.empty((M, layer.N), dtype=out_dtype, device=X.device)
+    _check_out(out, M, layer.N, X.device)
+    if workspace is None:
+        workspace = torch.empty(unfused_workspace_bytes(M, layer.N, layer.K, layer.rank),
+                                dtype=torch.uint8, device=X.device)
+    dt = FP32 if out.dtype == torch.float32 else BF16
+    _check(_lib.svdq_linear_forward_unfused(ctypes.byref(layer._w), X.data_ptr(), M, out.data_ptr(), dt,
+                                            EPILOGUE_GELU_TANH if gelu else EPILOGUE_NONE,
+                                            workspace.data_ptr(), workspace.numel(), _stream(X.device)),
+           "svdq_linear_forward_unfused")
     return out
 
 

@@ -1340,6 +1340,165 @@ __global__ __launch_bounds__(256) void k3_awq_w4a16_wide(const uint8_t *__restri
   }
 }
 
+// ========================================================= unfused branch
+// The low-rank branch as two plain bf16 GEMMs of its own, for the ablation
+// of the fusion the pages credit to the original engine (Korean edition,
+// "SVDQuant 및 Nunchaku 엔진": the down-projection rides with the
+// quantiser and the up-projection with the 4-bit GEMM, so the 16-bit branch
+// adds no memory pass).  Unfused, the branch reads X a second time, writes
+// D, and the 4-bit GEMM's fp32 result makes a round trip through HBM before
+// the up-projection adds D L2.
+
+// D = X L1s.  One workgroup (4 wavefronts) per (tile of 32 token rows, K
+// split), the quantiser's grid; wavefront w takes groups w, w + 4, ... of
+// the split.  Per group a lane loads its row's 4 x 8 bf16 (the A operand of
+// four 32x32x16 bf16 products, lane l: row l % 32, channels 16 j + 8 (l /
+// 32) + [0, 8)) straight from X and L1s in its fragment order (the B
+// operand).  The wavefronts' partials meet in LDS and go out as this
+// split's partial of D, in the quantiser's layout [S][Mp][rp].
+template <int TB>
+__global__ __launch_bounds__(256) void lr_down_kernel(const uint16_t *__restrict__ X, int M, int K, int Mp,
+                                                      int S, const uint16_t *__restrict__ l1t,
+                                                      float *__restrict__ dpart) {
+  const int t = blockIdx.x, s = blockIdx.y;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
+  const int G = K / kGroup, Gs = G / S;
+  const int64_t row = min(t * kTile + (lane & 31), M - 1);   // padding rows repeat row M - 1
+  v16f acc[TB];
+#pragma unroll
+  for (int b = 0; b < TB; ++b) acc[b] = v16f{};
+  for (int gi = w; gi < Gs; gi += 4) {
+    const int g = s * Gs + gi;
+    uint4 xr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      xr[j] = *reinterpret_cast<const uint4 *>(X + row * K + (int64_t)g * kGroup + 16 * j + 8 * h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        const uint4 lf = *reinterpret_cast<const uint4 *>(l1t + ((((int64_t)g * TB + b) * 4 + j) * 64 + lane) * 8);
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8bf(xr[j]), as_v8bf(lf), acc[b], 0, 0, 0);
+      }
+  }
+  __shared__ float red[4][16][64];
+  constexpr int RP = TB * 32;
+  for (int b = 0; b < TB; ++b) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[w][e][lane] = acc[b][e];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * w + i;
+      const float v = red[0][e][lane] + red[1][e][lane] + red[2][e][lane] + red[3][e][lane];
+      const int r = t * kTile + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      dpart[((int64_t)s * Mp + r) * RP + b * 32 + (lane & 31)] = v;
+    }
+    __syncthreads();
+  }
+}
+
+// Y = epilogue(Ym + D L2) where Ym is the 4-bit GEMM's fp32 result (bias
+// included) and D the down-projection's S partials.  Workgroup tile 64 x
+// 256, wavefront tile 32 x 128 (four 32 x 32 products per 16-rank step,
+// D entered as a bf16 high part plus a bf16 remainder as in the fused
+// GEMM).  The products go through the wavefront's own LDS so that Ym is
+// read, and Y written, as whole 16-byte vectors along rows.
+template <int EPI, bool OUT_F32>
+__global__ __launch_bounds__(256) void lr_up_kernel(const float *__restrict__ Ym, const float *__restrict__ dpart,
+                                                    int S, int M, int N, int Mp, int rp,
+                                                    const uint16_t *__restrict__ l2t, void *__restrict__ Y) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, ln = lane & 31;
+  const int m0 = blockIdx.x * 64 + 32 * (w >> 1), n0 = blockIdx.y * 256 + 128 * (w & 1);
+  // the wavefront's 32 x 128 block of Ym, requested first so that its
+  // latency passes under the products: lane l takes 16 float4, row-major
+  // (q * 64 + l) / 32, columns 4 ((q * 64 + l) % 32) + [0, 4)
+  const bool vec = (N % 4) == 0;
+  float4 ymv[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int idx = q * 64 + lane, m = m0 + (idx >> 5), n = n0 + (idx & 31) * 4;
+    ymv[q] = (vec && m < M && n < N) ? *reinterpret_cast<const float4 *>(Ym + (int64_t)m * N + n)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  v16f acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = v16f{};
+  const int64_t drow = m0 + ln;                               // < Mp: partials cover the padding
+  for (int c = 0; c < rp / 16; ++c) {
+    float d[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = 0.0f;
+    for (int sp = 0; sp < S; ++sp) {
+      const float4 *q = reinterpret_cast<const float4 *>(dpart + ((int64_t)sp * Mp + drow) * rp + 16 * c + 8 * h);
+      const float4 a = q[0], b = q[1];
+      d[0] += a.x; d[1] += a.y; d[2] += a.z; d[3] += a.w;
+      d[4] += b.x; d[5] += b.y; d[6] += b.z; d[7] += b.w;
+    }
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t h0 = f32_to_bf16_rne(d[2 * e]), h1 = f32_to_bf16_rne(d[2 * e + 1]);
+      hw[e] = h0 | (h1 << 16);
+      lw[e] = f32_to_bf16_rne(d[2 * e] - __uint_as_float(h0 << 16)) |
+              (f32_to_bf16_rne(d[2 * e + 1] - __uint_as_float(h1 << 16)) << 16);
+    }
+    const v8bf ah = as_v8bf(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    const v8bf al = as_v8bf(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 bw = *reinterpret_cast<const uint4 *>(l2t + (int64_t)(n0 + 32 * j + ln) * rp + 16 * c + 8 * h);
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, as_v8bf(bw), acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, as_v8bf(bw), acc[j], 0, 0, 0);
+    }
+  }
+  constexpr int LD = 132;                                       // padded row, floats
+  __shared__ float stage[4][32 * LD];
+  float *st = stage[w];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) st[(8 * (e >> 2) + 4 * h + (e & 3)) * LD + 32 * j + ln] = acc[j][e];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int idx = q * 64 + lane, r = idx >> 5, c = (idx & 31) * 4;
+    const int m = m0 + r, n = n0 + c;
+    if (m >= M || n >= N) continue;
+    const float4 a = *reinterpret_cast<const float4 *>(st + r * LD + c);
+    const float av[4] = {a.x, a.y, a.z, a.w};
+    float y[4];
+    if (vec) {
+      const float4 bq = ymv[q];
+      y[0] = bq.x + av[0]; y[1] = bq.y + av[1]; y[2] = bq.z + av[2]; y[3] = bq.w + av[3];
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) y[t] = n + t < N ? Ym[(int64_t)m * N + n + t] + av[t] : 0.0f;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if constexpr (EPI == SVDQ_EPILOGUE_GELU_TANH) y[t] = gelu_tanh_f32(y[t]);
+    if (vec) {
+      if constexpr (OUT_F32) {
+        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(Y) + (int64_t)m * N + n) = make_float4(y[0], y[1], y[2], y[3]);
+      } else {
+        const uint32_t lo = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
+        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(Y) + (int64_t)m * N + n) = make_uint2(lo, hi);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (n + t < N) {
+          if constexpr (OUT_F32) reinterpret_cast<float *>(Y)[(int64_t)m * N + n + t] = y[t];
+          else reinterpret_cast<uint16_t *>(Y)[(int64_t)m * N + n + t] = (uint16_t)f32_to_bf16_rne(y[t]);
+        }
+    }
+  }
+}
+
 // ==================================================================== GELU
 __global__ __launch_bounds__(256) void gelu_tanh_bf16_kernel(const uint16_t *__restrict__ in,
                                                              uint16_t *__restrict__ out,
@@ -1524,7 +1683,7 @@ svdq_status_t validate_weights(const svdq_weights_t *w, const char *who) {
 template <bool MX = false, class WL, class KL>
 svdq_status_t launch_k1(const WL &L, const KL &Wl, const svdq_weights_t *w,
                         const void *X, int M, uint8_t *ws, hipStream_t st,
-                        int64_t *dzero = nullptr, int rpz = 0) {
+                        int64_t *dzero = nullptr, int rpz = 0, bool with_down = true) {
   const uint8_t *blob = static_cast<const uint8_t *>(w->blob);
   const dim3 grid((unsigned)(Wl.Mp / kTile), (unsigned)Wl.S);
   const uint16_t *x = static_cast<const uint16_t *>(X);
@@ -1535,7 +1694,7 @@ svdq_status_t launch_k1(const WL &L, const KL &Wl, const svdq_weights_t *w,
   float *dp = reinterpret_cast<float *>(ws + Wl.d);
   const int K = w->K, Mp = (int)Wl.Mp, S = (int)Wl.S;
   const size_t lds = 0;
-  switch (L.rp / 32) {
+  switch (with_down ? L.rp / 32 : 0) {
 #define K1_CASE(TB)                                                                       \
   case TB:                                                                                \
     hipLaunchKernelGGL((k1_quantize_lowrank_down<TB, MX>), grid, dim3(256), lds, st, x, M, K, Mp, \
@@ -1609,10 +1768,11 @@ enum K2In { K2_D_PARTIALS = 0, K2_D_FIXED = 1 };
 static svdq_status_t launch_k2(const svdq_weights_t *w, int M, void *Y, svdq_dtype_t y_dtype,
                                svdq_epilogue_t epilogue, const void *workspace, hipStream_t stream,
                                K2In din = K2_D_PARTIALS, const svdq_weights_t *w2 = nullptr,
-                               void *ws2 = nullptr, size_t ws_bytes = 0) {
+                               void *ws2 = nullptr, size_t ws_bytes = 0, bool with_up = true) {
   const WeightLayout L(w->N, w->K, w->rank);
   const WorkLayout Wl(M, w->K, w->rank);
   K2Args a = make_k2_args(L, Wl, w, M, static_cast<const uint8_t *>(workspace));
+  if (!with_up) a.rp = 0;                      // the low-rank term is left out
   a.Y = Y;
   a.TM = (M + k2c::BM - 1) / k2c::BM;
   a.TN = (w->N + k2c::BN - 1) / k2c::BN;
@@ -1718,6 +1878,79 @@ svdq_status_t svdq_linear_forward(const svdq_weights_t *w, const void *X, int M,
     return st;
   return launch_k2(w, M, Y, y_dtype, epilogue, workspace, stream, K2_D_PARTIALS, nullptr, nullptr,
                    ws_bytes);
+}
+
+// ------------------------------------------------ unfused branch (ablation)
+// Workspace: the forward's, then the K-split partials (if the GEMM splits),
+// then the 4-bit GEMM's fp32 result [M][N].
+static int64_t unfused_ym_offset(int M, int N, int K, int rank) {
+  const WorkLayout Wl(M, K, rank);
+  return round_up(Wl.total + k2_split_bytes(M, N, K), kAlign);
+}
+
+size_t svdq_unfused_workspace_bytes(int M, int N, int K, int rank) {
+  if (M < 1 || N < 1 || K < 1 || K % kGroup != 0 || rank < 0 || rank > SVDQ_MAX_RANK) return 0;
+  return (size_t)(unfused_ym_offset(M, N, K, rank) + round_up((int64_t)M * N * 4, kAlign));
+}
+
+svdq_status_t svdq_linear_forward_unfused(const svdq_weights_t *w, const void *X, int M, void *Y,
+                                          svdq_dtype_t y_dtype, svdq_epilogue_t epilogue,
+                                          void *workspace, size_t ws_bytes, void *hip_stream) {
+  static const char *who = "svdq_linear_forward_unfused";
+  svdq_status_t st = validate_forward(w, M, ws_bytes, workspace, who);
+  if (st != SVDQ_OK) return st;
+  if (!X) return fail(SVDQ_ERR_INVALID_ARGUMENT, "%s: NULL X", who);
+  if (!aligned16(X)) return fail(SVDQ_ERR_INVALID_ARGUMENT, "%s: misaligned X", who);
+  if ((st = validate_output(Y, y_dtype, epilogue, who)) != SVDQ_OK) return st;
+  if ((int64_t)M * w->N > ((int64_t)1 << 31))
+    return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "%s: M*N too large", who);
+  const size_t need = svdq_unfused_workspace_bytes(M, w->N, w->K, w->rank);
+  if (ws_bytes < need)
+    return fail(SVDQ_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes, got %zu", who, need, ws_bytes);
+  if ((st = check_device()) != SVDQ_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const WeightLayout L(w->N, w->K, w->rank);
+  const WorkLayout Wl(M, w->K, w->rank);
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  const uint8_t *blob = static_cast<const uint8_t *>(w->blob);
+  float *dp = reinterpret_cast<float *>(ws + Wl.d);
+  float *ym = reinterpret_cast<float *>(ws + unfused_ym_offset(M, w->N, w->K, w->rank));
+  // (1) the quantiser without the down-projection
+  if ((st = launch_k1(L, Wl, w, X, M, ws, stream, nullptr, 0, false)) != SVDQ_OK) return st;
+  // (2) D = X L1s on its own
+  if (L.rp > 0) {
+    const dim3 grid((unsigned)(Wl.Mp / kTile), (unsigned)Wl.S);
+    const uint16_t *x = static_cast<const uint16_t *>(X);
+    const uint16_t *l1t = reinterpret_cast<const uint16_t *>(blob + L.l1t);
+    switch (L.rp / 32) {
+#define LRD_CASE(TB)                                                                                 \
+  case TB:                                                                                           \
+    hipLaunchKernelGGL((lr_down_kernel<TB>), grid, dim3(256), 0, stream, x, M, w->K, (int)Wl.Mp,     \
+                       (int)Wl.S, l1t, dp);                                                          \
+    break;
+      LRD_CASE(1) LRD_CASE(2) LRD_CASE(3) LRD_CASE(4) LRD_CASE(5) LRD_CASE(6) LRD_CASE(7) LRD_CASE(8)
+#undef LRD_CASE
+      default: return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "%s: rank too large", who);
+    }
+    if ((st = launch_status("down-projection launch")) != SVDQ_OK) return st;
+  }
+  // (3) the 4-bit GEMM without the up-projection: fp32 result with bias
+  if ((st = launch_k2(w, M, ym, SVDQ_FP32, SVDQ_EPILOGUE_NONE, ws, stream, K2_D_PARTIALS, nullptr,
+                      nullptr, (size_t)(Wl.total + k2_split_bytes(M, w->N, w->K)), false)) != SVDQ_OK)
+    return st;
+  // (4) Y = epilogue(Ym + D L2)
+  const dim3 ugrid((unsigned)((M + 63) / 64), (unsigned)(L.Np / 256));
+  const uint16_t *l2t = reinterpret_cast<const uint16_t *>(blob + L.l2t);
+  const bool f32 = y_dtype == SVDQ_FP32, gelu = epilogue == SVDQ_EPILOGUE_GELU_TANH;
+  constexpr int NONE = SVDQ_EPILOGUE_NONE, GELU = SVDQ_EPILOGUE_GELU_TANH;
+#define LRU_GO(E, F) hipLaunchKernelGGL((lr_up_kernel<E, F>), ugrid, dim3(256), 0, stream, ym, dp, (int)Wl.S, M, \
+                                        w->N, (int)Wl.Mp, (int)L.rp, l2t, Y)
+  if (!gelu && f32) LRU_GO(NONE, true);
+  else if (!gelu) LRU_GO(NONE, false);
+  else if (f32) LRU_GO(GELU, true);
+  else LRU_GO(GELU, false);
+#undef LRU_GO
+  return launch_status("up-projection launch");
 }
 
 // ------------------------------------------------ allocation-free forward
