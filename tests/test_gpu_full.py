@@ -200,12 +200,12 @@ def test_awq_full(S, awq, M):
 
 @pytest.mark.parametrize("M,N,K", [(5, 100, 192), (16, 250, 1600), (4, 100, 1600), (9, 48, 768),
                                    (7, 17, 832), (1, 33, 64), (12, 4100, 3072), (10, 40, 64),
-                                   (13, 272, 4160)])
+                                   (13, 272, 4160), (8, 64, 3200), (16, 96, 12288)])
 def test_awq_ragged_with_bias(S, M, N, K):
-    """Both AWQ kernels (one private activation copy per wavefront up to 9
-    rows, copies shared by two wavefronts from 10): ragged column tiles,
-    spare wavefronts, odd group counts, one chunk, several chunks, a last
-    chunk past the groups, a half with no groups of its own."""
+    """Both chunk sizes of the AWQ kernel (12 groups up to 8 rows, 4 groups
+    from 9): ragged column tiles, spare wavefronts, odd group counts, one
+    chunk, several chunks, a last chunk past a wavefront's groups, a
+    wavefront with no groups of its own."""
     announce(f"awq ragged M={M} N={N} K={K}")
     a = synth.awq_case(m_max=M, N=N, K=K, seed=44 + M)
     q, s, z = OA.quantize(a.W)

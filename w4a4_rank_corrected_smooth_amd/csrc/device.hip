@@ -1079,7 +1079,7 @@ __global__ __launch_bounds__(256) void k2_split_sum(const float *__restrict__ pa
 // AWQ W4A16.  A workgroup of 4 wavefronts owns a tile of 16 output channels;
 // wavefront w takes a contiguous quarter of the groups of 64 input channels
 // (rounded up to a multiple of 4, so its range starts on a pair of code
-// blocks and on a 16-byte quad of scale words), kAwqChunk groups at a time.
+// blocks and on a 16-byte quad of scale words), CH groups at a time.
 // Per chunk it first copies the chunk's activations (M rows, a few kilobytes
 // shared by every workgroup, so cache hits) into its own LDS with the
 // global->LDS path, then issues its code loads (16 bytes per lane: two
@@ -1087,7 +1087,7 @@ __global__ __launch_bounds__(256) void k2_split_sum(const float *__restrict__ pa
 // only for the copies; each group's compute then waits for its own loads
 // alone, in issue order.  Every load is unconditional (indices clamped;
 // groups past the range weigh 0, and every value they touch is finite: the
-// copies fill whole rows of kAwqChunk groups, repeating the last group of
+// copies fill whole rows of CH groups, repeating the last group of
 // the range, and the blob's padding words are zero), so the completion
 // counts are exact.  For each group, lane l (channel l % 16, quarter
 // q = l / 16) turns its 16 codes into fp16 (q - z) with the 1024-offset
@@ -1096,7 +1096,20 @@ __global__ __launch_bounds__(256) void k2_split_sum(const float *__restrict__ pa
 // two v_mfma_f32_16x16x32_f16 give the group's inner sums; acc += s * sum in
 // fp32.  Rows m >= M repeat row M - 1 and are never stored.  The four
 // partial sums meet in LDS, in a fixed order.
-constexpr int kAwqChunk = 12;                          // a multiple of 4
+// Groups per chunk: a wavefront copies M rows x CH groups of activations
+// into its own LDS.  Up to kAwqLongChunkRows rows the whole quarter of K
+// (12 groups at K = 3072) goes in one chunk; with more rows a wavefront's
+// copy would leave room for one workgroup per CU (24 KB at 16 rows), so the
+// chunks shrink to 4 groups.  Measured at N = 18432, K = 3072 (back to back,
+// MI355X): chunks of 12 take 8.7 / 11.3 / 13.3 us at M = 1 / 8 / 9; chunks of
+// 4 take 9.1 / 11.7 / 12.0 / 13.1 / 14.9 us at M = 1 / 8 / 9 / 12 / 16;
+// chunks of 8 lose at every M (13.6 us at M = 8).  A two-tile kernel whose
+// wavefronts shared one copy took 17.0 / 17.9 us at M = 12 / 16, and loading
+// the activations straight into registers with every other load up front
+// (no LDS) 10.6 / 19.5 us at M = 1 / 16.
+constexpr int kAwqChunk = 12;
+constexpr int kAwqShortChunk = 4;
+constexpr int kAwqLongChunkRows = 8;
 
 // One group of 64 input channels for a wavefront's 16 x 16 output block:
 // xg points at the lane's activations in LDS (row lane % 16, channels
@@ -1104,10 +1117,8 @@ constexpr int kAwqChunk = 12;                          // a multiple of 4
 // the same channels; even channels in the low half-words), szv the column's
 // fp16 scale | zero << 16.  acc += s * sum over the group (weight 0 when the
 // group is not valid; every input is finite either way).
-__device__ __forceinline__ void awq_group(const uint16_t *xg, uint32_t w0, uint32_t w1, uint32_t szv,
-                                          bool valid, v4f &acc) {
-  const uint4 xa0 = *reinterpret_cast<const uint4 *>(xg);
-  const uint4 xa1 = *reinterpret_cast<const uint4 *>(xg + 8);
+__device__ __forceinline__ void awq_group_regs(uint4 xa0, uint4 xa1, uint32_t w0, uint32_t w1, uint32_t szv,
+                                               bool valid, v4f &acc) {
   const _Float16 zf = __builtin_bit_cast(_Float16, (uint16_t)(szv >> 16));
   const float sf = valid ? (float)__builtin_bit_cast(_Float16, (uint16_t)(szv & 0xFFFF)) : 0.0f;
   const _Float16 off = -((_Float16)1024.0f + zf);
@@ -1133,6 +1144,12 @@ __device__ __forceinline__ void awq_group(const uint16_t *xg, uint32_t w0, uint3
 #pragma unroll
   for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(part[e], sf, acc[e]);
 }
+__device__ __forceinline__ void awq_group(const uint16_t *xg, uint32_t w0, uint32_t w1, uint32_t szv,
+                                          bool valid, v4f &acc) {
+  awq_group_regs(*reinterpret_cast<const uint4 *>(xg), *reinterpret_cast<const uint4 *>(xg + 8), w0, w1, szv,
+                 valid, acc);
+}
+template <int CH>
 __global__ __launch_bounds__(256) void k3_awq_w4a16(const uint8_t *__restrict__ qd,
                                                      const uint32_t *__restrict__ sz,
                                                      const uint16_t *__restrict__ x, int M,
@@ -1151,18 +1168,18 @@ __global__ __launch_bounds__(256) void k3_awq_w4a16(const uint8_t *__restrict__ 
   extern __shared__ __attribute__((aligned(16))) uint8_t awq_lds[];
   v4f acc = v4f{};
   // this wavefront's copy of the chunk's activations: rows 0..M-1 of
-  // kAwqChunk groups each, one 16-byte piece per lane and copy
-  constexpr int npr = kAwqChunk * (kGroup / 8);         // pieces per row
+  // CH groups each, one 16-byte piece per lane and copy
+  constexpr int npr = CH * (kGroup / 8);         // pieces per row
   const int npc = M * npr;
   const int xw_bytes = (npc + 63) / 64 * 1024;
   const uint32_t xl_u32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)awq_lds +
                           (uint32_t)(__builtin_amdgcn_readfirstlane(w) * xw_bytes);
   const uint16_t *xl = reinterpret_cast<const uint16_t *>(awq_lds + w * xw_bytes);
   const uint16_t *xm = xl + min(m, M - 1) * (npr * 8) + 16 * qtr;
-  for (int gc = g0; gc < g1; gc += kAwqChunk) {
+  for (int gc = g0; gc < g1; gc += CH) {
     // activations first (cache hits), then the code and scale stream; every
     // load after the copies is unconditional, so the copies are complete
-    // once at most kAwqChunk / 2 + kAwqChunk / 4 loads remain
+    // once at most CH / 2 + CH / 4 loads remain
     for (int c0 = 0; c0 < npc; c0 += 64) {
       const int pc = min(c0 + lane, npc - 1);
       const int mr = pc / npr, o = pc - mr * npr;
@@ -1176,21 +1193,21 @@ __global__ __launch_bounds__(256) void k3_awq_w4a16(const uint8_t *__restrict__ 
     asm volatile("" : "+s"(zero));
     const uint8_t *qb = qbase + zero;
     const uint32_t *szb = sz + (int64_t)n * G4 + zero;
-    uint4 cw[kAwqChunk / 2];
-    uint4 szw[kAwqChunk / 4];
+    uint4 cw[CH / 2];
+    uint4 szw[CH / 4];
 #pragma unroll
-    for (int j = 0; j < kAwqChunk / 2; ++j) {
+    for (int j = 0; j < CH / 2; ++j) {
       const int pr = min(gc / 2 + j, (g1 - 1) / 2);
       cw[j] = *reinterpret_cast<const uint4 *>(qb + (int64_t)pr * kAwqBlockBytes);
     }
 #pragma unroll
-    for (int j = 0; j < kAwqChunk / 4; ++j) {
+    for (int j = 0; j < CH / 4; ++j) {
       const int qd4 = min(gc / 4 + j, (g1 - 1) / 4);
       szw[j] = *reinterpret_cast<const uint4 *>(szb + 4 * qd4);
     }
-    vmcnt_wait<kAwqChunk / 2 + kAwqChunk / 4>();
+    vmcnt_wait<CH / 2 + CH / 4>();
 #pragma unroll
-    for (int i = 0; i < kAwqChunk; ++i) {
+    for (int i = 0; i < CH; ++i) {
       const uint4 q4 = szw[i / 4];
       const uint32_t szv = (i % 4 == 0) ? q4.x : (i % 4 == 1) ? q4.y : (i % 4 == 2) ? q4.z : q4.w;
       const uint4 c = cw[i / 2];
@@ -1214,128 +1231,6 @@ __global__ __launch_bounds__(256) void k3_awq_w4a16(const uint8_t *__restrict__ 
         const float v = ((r0[e] + r1[e]) + (r2[e] + r3[e])) + b;
         y[(int64_t)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
       }
-    }
-  }
-}
-
-// AWQ W4A16 for more rows (M = 5..16).  With 16 rows, a private copy of a
-// 12-group chunk's activations per wavefront (24 KB) would leave one
-// workgroup per CU.  Here a workgroup covers two column tiles (32 output
-// channels) and splits the groups in two halves: wavefront w takes tile
-// w % 2 and half w / 2, so the two wavefronts of a half share one copy of
-// its activations.  Chunks are kAwqWideChunk groups, double-buffered in LDS
-// per half; each wavefront issues the code and scale loads of up to
-// kAwqWideChunks chunks at once (the HBM stream, all in flight together),
-// then the copy of its half's first chunk.  Chunk k then runs as: a barrier
-// (chunk k - 1 is done with the buffer the next copy overwrites), the copy
-// of chunk k + 1, a wait for everything older (chunk k's copy and, at
-// k = 0, every code load), a barrier (both wavefronts' copies of chunk k
-// are in), and chunk k's groups.  Both halves run the same number of chunks
-// (surplus ones load clamped data and weigh 0), so every barrier is met by
-// all four wavefronts; the halves' sums meet in LDS in a fixed order.
-constexpr int kAwqWideChunk = 4;                       // groups per chunk (one scale quad)
-constexpr int kAwqWideChunks = 8;                      // chunks whose codes are in flight together
-// M from which this kernel runs: measured on MI355X at N = 18432, K = 3072
-// against the one above, 16.0 vs 12.4 us at M = 8 and 18.7 vs 24.4 us at
-// M = 16 (the one above then holds 24 KB of activations per wavefront, one
-// workgroup per CU).  Here each chunk waits on a copy issued one chunk
-// earlier, which bounds it at smaller M.
-constexpr int kAwqWideMinRows = 10;
-__global__ __launch_bounds__(256) void k3_awq_w4a16_wide(const uint8_t *__restrict__ qd,
-                                                          const uint32_t *__restrict__ sz,
-                                                          const uint16_t *__restrict__ x, int M,
-                                                          int N, int K,
-                                                          const uint16_t *__restrict__ bias,
-                                                          uint16_t *__restrict__ y) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-  const int tl = wu & 1, h = wu >> 1;                  // tile within the workgroup, group half
-  const int G = K / kGroup, G4 = (G + 3) & ~3, P = (G + 1) / 2;
-  const int Gh = (((G + 1) / 2) + kAwqWideChunk - 1) / kAwqWideChunk * kAwqWideChunk;
-  const int g0 = h * Gh;                               // this half: groups [g0, g0 + Gh) within [0, G)
-  const int nch = Gh / kAwqWideChunk;
-  const int ntiles = (N + kAwqTile - 1) / kAwqTile;
-  const int tile_raw = blockIdx.x * 2 + tl;
-  const int tile = min(tile_raw, ntiles - 1);
-  const int m = lane & 15, qtr = lane >> 4;
-  const int n = tile * kAwqTile + (lane & 15);
-  const uint8_t *qbase = qd + (int64_t)tile * P * kAwqBlockBytes + lane * 16;
-  const uint32_t *szrow = sz + (int64_t)n * G4;
-  extern __shared__ __attribute__((aligned(16))) uint8_t awq_lds[];
-  constexpr int npr = kAwqWideChunk * (kGroup / 8);    // 16-byte pieces per row of a chunk
-  const int npc = M * npr;
-  const int rounds = (npc + 127) / 128;                // copies per thread per chunk (two wavefronts)
-  const int buf_bytes = rounds * 2048;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)awq_lds;
-  v4f acc = v4f{};
-  // chunk c of this half (groups g0 + 4c + [0, 4), the layer's last group
-  // repeated past G) into the half's buffer `buf`
-  auto copy_x = [&](int c, int buf) {
-    const int gc = g0 + c * kAwqWideChunk;
-    const uint32_t base = lds0 + (uint32_t)((2 * h + buf) * buf_bytes);
-    for (int r = 0; r < rounds; ++r) {
-      const int p0 = 128 * r + 64 * tl;                // this wavefront's 64 pieces
-      const int pc = min(p0 + lane, npc - 1);
-      const int mr = pc / npr, o = pc - mr * npr;
-      const int gi = min(gc + o / 8, G - 1);
-      lds_dma16(x + (int64_t)mr * K + gi * kGroup + (o % 8) * 8, base + (uint32_t)(p0 * 16));
-    }
-  };
-  for (int sc = 0; sc < nch; sc += kAwqWideChunks) {
-    const int nc = min(kAwqWideChunks, nch - sc);
-    __syncthreads();                                   // the previous super-chunk is done with the LDS
-    uint4 cw[kAwqWideChunks][kAwqWideChunk / 2], szw[kAwqWideChunks];
-#pragma unroll
-    for (int k = 0; k < kAwqWideChunks; ++k) {
-      const int gc = min(g0 + min(sc + k, nch - 1) * kAwqWideChunk, G - 1) & ~3;
-#pragma unroll
-      for (int j = 0; j < kAwqWideChunk / 2; ++j)
-        cw[k][j] = *reinterpret_cast<const uint4 *>(qbase + (int64_t)min(gc / 2 + j, P - 1) * kAwqBlockBytes);
-      szw[k] = *reinterpret_cast<const uint4 *>(szrow + gc);
-    }
-    // the copies follow the code loads in issue order (the waits below
-    // count on it): their LDS buffer index takes an offset from an empty
-    // asm placed after the loads
-    int zero = 0;
-    asm volatile("" : "+s"(zero) :: "memory");
-    copy_x(sc, zero);
-#pragma unroll
-    for (int k = 0; k < kAwqWideChunks; ++k) {
-      if (k >= nc) break;
-      if (k > 0) __syncthreads();                      // chunk k - 1 is done with buffer (k + 1) % 2
-      if (k + 1 < nc) {
-        copy_x(sc + k + 1, (k + 1) & 1);
-        vmcnt_wait_dyn(rounds);
-      } else {
-        vmcnt_wait0_known();
-      }
-      __syncthreads();                                 // both wavefronts' copies of chunk k are in
-      const int gc = g0 + (sc + k) * kAwqWideChunk;
-      const uint16_t *xm = reinterpret_cast<const uint16_t *>(awq_lds + (2 * h + (k & 1)) * buf_bytes) +
-                           min(m, M - 1) * (npr * 8) + 16 * qtr;
-#pragma unroll
-      for (int i = 0; i < kAwqWideChunk; ++i) {
-        const uint4 q4 = szw[k];
-        const uint32_t szv = (i == 0) ? q4.x : (i == 1) ? q4.y : (i == 2) ? q4.z : q4.w;
-        const uint4 cc = cw[k][i / 2];
-        awq_group(xm + i * kGroup, i % 2 == 0 ? cc.x : cc.z, i % 2 == 0 ? cc.y : cc.w, szv,
-                  gc + i < G && gc + i < g0 + Gh, acc);
-      }
-    }
-  }
-  __syncthreads();                                     // the buffers are free for the reduction
-  v4f *red = reinterpret_cast<v4f *>(awq_lds);
-  if (h == 1) red[tl * 64 + lane] = acc;
-  __syncthreads();
-  if (h == 1) return;
-  const v4f other = red[tl * 64 + lane];
-  const int col = tile_raw * kAwqTile + (lane & 15);
-  if (tile_raw < ntiles && col < N) {
-    const float b = bias ? (float)__builtin_bit_cast(_Float16, bias[col]) : 0.0f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 4 * (lane >> 4) + e;
-      if (row < M) y[(int64_t)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)((acc[e] + other[e]) + b));
     }
   }
 }
@@ -2293,25 +2188,15 @@ svdq_status_t awq_w4a16_forward(const void *blob, int N, int K, const void *x, i
   if (st != SVDQ_OK) return st;
   const AwqLayout L(N, K);
   const uint8_t *b = static_cast<const uint8_t *>(blob);
-  const int pieces = M * kAwqChunk * (kGroup / 8);     // 16-byte copies of a chunk's activations
-  if (M <= kAwqWideMinRows - 1) {
-    // per wavefront: M rows of a chunk, in whole 1 KB copies
-    const size_t lds = (size_t)4 * ((pieces + 63) / 64 * 1024);
-    hipLaunchKernelGGL(k3_awq_w4a16, dim3((unsigned)(L.Np / kAwqTile)), dim3(256), lds,
-                       static_cast<hipStream_t>(hip_stream), b + L.q,
-                       reinterpret_cast<const uint32_t *>(b + L.sz), static_cast<const uint16_t *>(x), M,
-                       N, K, static_cast<const uint16_t *>(bias), static_cast<uint16_t *>(y));
-  } else {
-    // per workgroup: two halves x two buffers of a 4-group chunk's
-    // activations, in whole 2 KB rounds (also holds the reduction's 2 KB)
-    const int wpieces = M * kAwqWideChunk * (kGroup / 8);
-    const size_t lds = (size_t)4 * ((wpieces + 127) / 128 * 2048);
-    const int64_t tiles = L.Np / kAwqTile;
-    hipLaunchKernelGGL(k3_awq_w4a16_wide, dim3((unsigned)((tiles + 1) / 2)),
-                       dim3(256), lds, static_cast<hipStream_t>(hip_stream), b + L.q,
-                       reinterpret_cast<const uint32_t *>(b + L.sz), static_cast<const uint16_t *>(x), M,
-                       N, K, static_cast<const uint16_t *>(bias), static_cast<uint16_t *>(y));
-  }
+  const int ch = M <= kAwqLongChunkRows ? kAwqChunk : kAwqShortChunk;
+  // per wavefront: M rows of a chunk, in whole 1 KB copies
+  const size_t lds = (size_t)4 * ((M * ch * (kGroup / 8) + 63) / 64 * 1024);
+#define K3_GO(C) hipLaunchKernelGGL((k3_awq_w4a16<C>), dim3((unsigned)(L.Np / kAwqTile)), dim3(256), lds, \
+                                    static_cast<hipStream_t>(hip_stream), b + L.q,                      \
+                                    reinterpret_cast<const uint32_t *>(b + L.sz), static_cast<const uint16_t *>(x), \
+                                    M, N, K, static_cast<const uint16_t *>(bias), static_cast<uint16_t *>(y))
+  if (ch == kAwqChunk) K3_GO(kAwqChunk); else K3_GO(kAwqShortChunk);
+#undef K3_GO
   return launch_status("AWQ kernel launch");
 }
 
