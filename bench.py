@@ -708,6 +708,71 @@ def branch_fusion(S, dev, stream, layers):
     return out
 
 
+def cpu_configs(args):
+    """bench.py --cpu-configs: the oracle's forward (activation quantisation,
+    low-rank down, float64 group-scaled GEMM, low-rank up, bias; AWQ: the
+    dequantised GEMV) timed on the host cores for every configuration, with
+    all threads and, for the tiny and the low-res configurations, one
+    thread.  The layers are prepared by the library's host code (the timed
+    part is the oracle's forward alone).  One JSON line per run."""
+    import numpy as np
+    import synth
+    import w4a4_rank_corrected_smooth_amd as S
+    from oracle import awq as OA
+    from oracle import glue as OG
+    from oracle import svdquant as O
+    from threadpoolctl import threadpool_limits, threadpool_info
+    all_threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) or 1
+
+    def ref_of(hw):
+        return dict(N=hw.N, K=hw.K, rank=hw.rank, iota=hw.inv_lambda.astype(np.float32),
+                    L1s=O.bf16_values(hw.l1s), L2b=O.bf16_values(hw.l2), qW=O.unpack_int4(hw.qweight),
+                    sW=hw.wscales.astype(np.float32), bias=hw.bias.astype(np.float64))
+
+    def timed(fn, min_s=1.0, max_runs=20):
+        fn()
+        runs, t = 0, 0.0
+        while runs < max_runs and (runs == 0 or t < min_s):
+            t0 = time.perf_counter()
+            fn()
+            t += time.perf_counter() - t0
+            runs += 1
+        return t / runs
+
+    def report(name, ops, fn, threads):
+        with threadpool_limits(limits=threads):
+            sec = timed(fn)
+        print(json.dumps({"cpu_oracle": name, "threads": threads, "seconds": round(sec, 4),
+                          "gops": round(ops / sec / 1e9, 2)}), flush=True)
+
+    c = synth.tiny_case()
+    ref = ref_of(S.prepare_weights(c.W, c.calib_absmax(), c.bias, 16))
+    for th in (all_threads, 1):
+        report("tiny_256x512x512_r16", 2.0 * c.M * c.N * c.K, lambda: O.forward(ref, c.X), th)
+    c = synth.qkv_case()
+    ref = ref_of(S.prepare_weights(c.W, c.calib_absmax(), c.bias, 32))
+    report("qkv_4608x3072x9216_r32", 2.0 * c.M * c.N * c.K, lambda: O.forward(ref, c.X), all_threads)
+    del ref
+    fc1, W2, b2 = synth.mlp_cases()
+    ref1 = ref_of(S.prepare_weights(fc1.W, fc1.calib_absmax(), fc1.bias, 32))
+    report("mlp_fc1_4608x3072x12288_r32", 2.0 * fc1.M * fc1.N * fc1.K, lambda: O.forward(ref1, fc1.X), all_threads)
+    rng = np.random.default_rng(12)
+    X2 = O.bf16_bits_of(OG.gelu_tanh_bf16(O.bf16_values(
+        synth.f32_to_bf16_bits(rng.standard_normal((fc1.M, fc1.N), dtype=np.float32)))))
+    del ref1
+    ref2 = ref_of(S.prepare_weights(W2, O.calibration_absmax(O.bf16_values(X2[:64])), b2, 32))
+    report("mlp_fc2_4608x12288x3072_r32", 2.0 * fc1.M * fc1.N * fc1.K, lambda: O.forward(ref2, X2), all_threads)
+    del ref2, X2
+    c = synth.lowres_case()
+    ref = ref_of(S.prepare_weights(c.W, c.calib_absmax(), c.bias, 128))
+    for th in (all_threads, 1):
+        report("lowres_1024x3072x3072_r128", 2.0 * c.M * c.N * c.K, lambda: O.forward(ref, c.X), th)
+    a = synth.awq_case()
+    q, sc, z = OA.quantize(a.W)
+    for M in (1, 16):
+        report(f"awq_m{M}_{M}x3072x18432", 2.0 * M * a.N * a.K, lambda: OA.forward(a.x[:M], q, sc, z), all_threads)
+
+
 def branch_ablation_mode(args):
     """bench.py --branch-ablation: only the fused-against-unfused branch
     timings (QKV, fc1 + GELU, fc2, low-res rank 128), one JSON line; under a
@@ -801,6 +866,8 @@ def main():
                     help="CPU only: summarise a rocprofv3 --pmc pass of the shader counters into profiles/")
     ap.add_argument("--block", action="store_true",
                     help="launch study of one transformer block's calls, eager and as a HIP graph")
+    ap.add_argument("--cpu-configs", action="store_true",
+                    help="CPU only: the oracle's forward timed per configuration (all threads; 1 thread for tiny and low-res)")
     ap.add_argument("--branch-ablation", action="store_true",
                     help="fused against unfused low-rank branch at QKV, fc1, fc2 and low-res (one JSON line)")
     ap.add_argument("--hbm-floor", action="store_true",
@@ -825,6 +892,9 @@ def main():
                "fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d {fe} -- {base}",
                "write": f"rocprofv3 --pmc WRITE_SIZE -f csv -d {wr} -- {base}"}
         summarize_profiles(t, fe, wr, os.path.join(ROOT, "profiles"), cmd, args.profiled_log)
+        return
+    if args.cpu_configs:
+        cpu_configs(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this library runs the layer on a single MI355X and "
