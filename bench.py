@@ -201,6 +201,76 @@ SQ_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU",
                "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU")
 
 
+def summarize_trace(trace_dir, out_path, title, command, json_path=None, note=""):
+    """CPU only: a rocprofv3 --kernel-trace --stats run as a text summary
+    (per-kernel calls and durations), with the command that made it and, if
+    given, the JSON lines the traced run printed."""
+    lines = [f"# {title}", ""]
+    if note:
+        lines += [note, ""]
+    lines += ["Command:", "", "```", command, "```", ""]
+    if trace_dir:
+        stats = _read_csv(_find(trace_dir, "kernel_stats.csv"))
+        lines += ["| kernel | calls | average us | min us | max us | share |", "|---|---:|---:|---:|---:|---:|"]
+        for r in stats:
+            lines.append(f"| `{_short(r['Name'])[:80]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                         f"{float(r['Percentage']):.1f}% |")
+        lines.append("")
+    if json_path:
+        js = [ln.strip() for ln in open(json_path) if ln.startswith("{")]
+        if js:
+            lines += ["The run's own output:", "", "```"] + js + ["```"]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_floor(trace_dir, jsonl, out_path, command):
+    """CPU only: the streaming read and copy kernels of ``--hbm-floor`` from a
+    rocprofv3 kernel trace, by case and grid: each back-to-back series is a
+    run of launches with one grid size, in the order the mode issues them;
+    the mean of a series' last 150 launches (the five timed batches of 30)
+    gives the kernel's own duration and rate, free of launch gaps."""
+    import numpy as np
+    cases = [json.loads(l) for l in open(jsonl) if l.startswith("{")]
+    rows = sorted(_read_csv(_find(trace_dir, "kernel_trace.csv")), key=lambda r: int(r["Start_Timestamp"]))
+    runs = []
+    for r in rows:
+        if "stream_probe" not in r["Kernel_Name"]:
+            continue
+        g = int(r["Grid_Size_X"]) // 256
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if runs and runs[-1][0] == g:
+            runs[-1][1].append(d)
+        else:
+            runs.append((g, [d]))
+    lines = ["# Practical HBM floor at the bandwidth-bound kernels' sizes", "",
+             "A plain streaming read (16 loads of 16 bytes in flight per lane, nontemporal) and a plain copy of "
+             "the quantiser's input (4608 x 3072 and 4608 x 12288 bf16) and of the W4A16 blob (18432 x 3072), "
+             "over rotating buffers larger than the 256 MB Infinity Cache.  Durations are the kernel trace's own "
+             "(mean of each series' last 150 launches), so launch gaps are excluded.", "",
+             "Command:", "", "```", command, "```", "",
+             "| case | bytes | grid | read us | read GB/s | fraction of 8 TB/s |", "|---|---:|---:|---:|---:|---:|"]
+    i = 0
+    for c in cases:
+        grids = sorted(int(k) for k in c["read_gbs_by_grid"])
+        for g in grids + ["copy"]:
+            if i >= len(runs):
+                break
+            gg, ds = runs[i]
+            i += 1
+            us = float(np.mean(ds[-150:]))
+            nb = c["bytes"] * (2 if g == "copy" else 1)
+            label = f"{c['kernel_grid']} (copy)" if g == "copy" else str(g)
+            mark = " (kernel's grid)" if g == c["kernel_grid"] else ""
+            lines.append(f"| {c['hbm_floor']} | {c['bytes']} | {label}{mark} | {us:.2f} | {nb / us / 1e3:.0f} | "
+                         f"{nb / us / 1e3 / PEAK_HBM_GBS:.1%} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_counters(pmc_dir, out_path, command):
     """Per-kernel shader counters (one rocprofv3 --pmc pass of the default
     profile command), averaged over each kernel's dispatches, with the clock
@@ -283,6 +353,9 @@ def summarize_configs(trace_dir, sweep_jsonl, out_path, command):
              "kernel). Rates use the algorithmic work of each "
              "kernel (K2: 2MNK int ops; K1: X + 1/lambda + L1s + codes + scales + D bytes; "
              "K3: codes + scales/zeros + x + y bytes).", "",
+             "K2's fraction is of its own instruction's peak (fp6 for INT4 codes, fp4 for MXFP4: 10.1 "
+             "POP/s each), with the int8 peak (5.0 POP/s) of the metric beside the rate; K1 and K3 are "
+             "against 8 TB/s.", "",
              "| configuration | kernel | median us | p10 us | p90 us | rate | fraction of peak |",
              "|---|---|---:|---:|---:|---:|---:|"]
     si = 0
@@ -303,7 +376,8 @@ def summarize_configs(trace_dir, sweep_jsonl, out_path, command):
             M, N, K = c["M"], c["N"], c["K"]
             if label == "K2":
                 rate = 2.0 * M * N * K / med / 1e6
-                txt, frac = f"{rate:.0f} TOPS", rate / PEAK_INT8_TOPS
+                pk = PEAK_FP4_TOPS if c.get("format") == "mxfp4" else PEAK_FP6_TOPS
+                txt, frac = f"{rate:.0f} TOPS ({rate / PEAK_INT8_TOPS:.1%} of int8)", rate / pk
             elif label == "K1":
                 r = c["rank"]
                 b = 2 * M * K + 4 * K + 2 * K * r + M * K // 2 + 4 * M * (K // 64) + 4 * M * r
@@ -872,9 +946,25 @@ def main():
                     help="fused against unfused low-rank branch at QKV, fc1, fc2 and low-res (one JSON line)")
     ap.add_argument("--hbm-floor", action="store_true",
                     help="streaming read/copy rates at the quantiser's and W4A16 kernel's sizes and grids")
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "OUT_NAME", "TITLE", "COMMAND"),
+                    help="CPU only: summarise a rocprofv3 trace (TRACE_DIR may be '-') into profiles/OUT_NAME")
+    ap.add_argument("--summarize-floor", nargs=2, metavar=("TRACE_DIR", "JSONL"),
+                    help="CPU only: summarise a rocprofv3 trace of --hbm-floor into profiles/hbm_floor.md")
+    ap.add_argument("--json", default=None, help="with --summarize-trace: the traced run's stdout")
+    ap.add_argument("--note", default="", help="with --summarize-trace: a paragraph under the title")
     ap.add_argument("--summarize-configs", nargs=2, metavar=("TRACE_DIR", "SWEEP_JSONL"),
                     help="CPU only: summarise a rocprofv3 trace of --configs into profiles/ and exit")
     args = ap.parse_args()
+    if args.summarize_floor:
+        t, j = args.summarize_floor
+        summarize_floor(t, j, os.path.join(ROOT, "profiles", "hbm_floor.md"),
+                        "rocprofv3 --kernel-trace --stats -f csv -d <dir> -- python3 bench.py --hbm-floor")
+        return
+    if args.summarize_trace:
+        t, name, title, cmd = args.summarize_trace
+        summarize_trace(None if t == "-" else t, os.path.join(ROOT, "profiles", name), title, cmd,
+                        args.json, args.note)
+        return
     if args.summarize_configs:
         t, j = args.summarize_configs
         summarize_configs(t, j, os.path.join(ROOT, "profiles", "kernels_all_configs.md"),
