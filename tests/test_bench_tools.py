@@ -53,7 +53,8 @@ def test_config_summary_series_and_k_split(tmp_path):
     assert cells[1][3] == "100.00"                # big K2
     assert cells[3][3] == "45.00"                 # small K2: GEMM + partial sum, one launch
     tops = 2.0 * 1024 * 3072 * 3072 / 45.0 / 1e6
-    assert cells[3][6] == f"{tops:.0f} TOPS"
+    assert cells[3][6] == f"{tops:.0f} TOPS ({tops / bench.PEAK_INT8_TOPS:.1%} of int8)"
+    assert cells[3][7] == f"{tops / bench.PEAK_FP6_TOPS:.1%}"     # INT4 codes run as fp6
 
 
 def test_counter_summary(tmp_path):
