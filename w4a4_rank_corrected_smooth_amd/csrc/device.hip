@@ -33,6 +33,7 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef unsigned v6u __attribute__((ext_vector_type(6)));
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));   // four bf16 bit patterns
 
 // ------------------------------------------------------------ small helpers
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -456,11 +457,8 @@ constexpr int I4_SA_OFF = I4_SW_OFF + BN * kScaleOpBytes;       // 22528
 constexpr int I4_STAGE = I4_SA_OFF + BM * kScaleOpBytes;        // 24576
 constexpr int I4_LOADS = I4_STAGE / 1024, I4_LOADS_W = I4_LOADS / NWAVES;   // 24, 6
 constexpr int I4_NBUF = 3;
-// after the stages: the low-rank staging of the prologue (8 KB), which the
-// main loop then uses as a zero area (lanes 32..63 of the weight-scale
-// operand read zeros there)
+// after the stages: the low-rank staging of the prologue (8 KB)
 constexpr int I4_AUX_OFF = I4_NBUF * I4_STAGE;                  // 73728
-constexpr int I4_ZERO_BYTES = 2048;
 // MXFP4 stage: one K-step's codes and E8M0 scales (13 KB) in 20 KB slots;
 // four rotate, the fourth holding the prologue's low-rank staging at first.
 constexpr int MX_STAGE = 20480, MX_NBUF = 4;
@@ -749,40 +747,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // INT4 main loop.  Per group and 32 x 32 tile (i, j) of the wavefront:
     //   P  = fp6 matrix instruction on the codes (unit block scales): the
     //        exact integer group sums
-    //   S  = bf16 matrix instruction on the scale operands: sA[m] sW[n]
-    //        from the exact bf16 pieces of both scales
+    //   S  = 32x32x8 bf16 matrix instruction on the scale operands:
+    //        sA[m] sW[n] from the exact bf16 pieces of both scales
     //   acc = fma(P, S, acc)            (one vector instruction per element)
     // The scale product runs on the matrix core, which the codes alone leave
     // mostly idle, so the vector ALU does one instruction per element and
     // group instead of two.  Each operand of group g + 1 is read from LDS
     // right after the last matrix instruction of group g that uses it; the
     // SIMD's other wavefront covers the wait for each tile's products.
-    // Lanes 32..63 of the weight-scale operand (K slots 8..15) read the zero
-    // area after the stages, so those slots contribute nothing.  One barrier
+    // Each lane reads the 8-byte half of a scale operand that its lane half
+    // holds (4 KB per wavefront and group, no padding slots).  One barrier
     // per group: every wavefront waits for its copies of stage g + 1 and for
     // its own LDS reads of stage g, meets the others, and requests stage
     // g + 3 into stage g's buffer.  After the last group the reads of "group
     // G" run on a stale but in-bounds buffer and are never used.
     v8i fa[WTM], fb[WTN];
-    v8bf xa[WTM], xb[WTN];
-    if constexpr (MODE == MODE_FWD) {
-      // the zero area (the prologue's staging until now)
-      reinterpret_cast<uint2 *>(smem + I4_AUX_OFF)[tid] = make_uint2(0u, 0u);
-      static_assert(THREADS * 8 == I4_ZERO_BYTES && 3 * 512 + 16 <= I4_ZERO_BYTES, "zero area");
-    }
-    const bool lo_half = lane < 32;
+    v4s xa[WTM], xb[WTN];
     auto ld_a = [&](int g, int i) {
       const uint8_t *st = stage_i4(g);
       fa[i] = k2_frag(st + (WTM * wmi + i) * kBlockBytes, lane);
       if constexpr (MODE == MODE_FWD)
-        xa[i] = as_v8bf(*reinterpret_cast<const uint4 *>(st + I4_SA_OFF + (WROWS * wmi + 32 * i + ln) * kScaleOpBytes));
+        xa[i] = __builtin_bit_cast(v4s, *reinterpret_cast<const uint2 *>(
+            st + I4_SA_OFF + (WROWS * wmi + 32 * i + ln) * kScaleOpBytes + 8 * hl));
     };
     auto ld_b = [&](int g, int j) {
       const uint8_t *st = stage_i4(g);
       fb[j] = k2_frag(st + A_BYTES + (WTN * wni + j) * kBlockBytes, lane);
       if constexpr (MODE == MODE_FWD) {
-        const uint8_t *xp = lo_half ? st + I4_SW_OFF + (WCOLS * wni + ln) * kScaleOpBytes : smem + I4_AUX_OFF;
-        xb[j] = as_v8bf(*reinterpret_cast<const uint4 *>(xp + 32 * kScaleOpBytes * j));
+        xb[j] = __builtin_bit_cast(v4s, *reinterpret_cast<const uint2 *>(
+            st + I4_SW_OFF + (WCOLS * wni + 32 * j + ln) * kScaleOpBytes + 8 * hl));
       }
     };
     auto sums_store = [&](int g, int i, int j, const v16f &P) {
@@ -808,7 +801,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       LOADS;                                                                                  \
       sums_store(g, i, j, P[(i * WTN + j) & 1]);                                              \
     } else {                                                                                  \
-      const v16f Sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], v16f{}, 0, 0, 0); \
+      const v16f Sx = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(xa[i], xb[j], v16f{}, 0, 0, 0); \
       P[(i2 * WTN + j2) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                \
           fa[i2], fb[j2], v16f{}, 2, 2, 0, 127, 0, 127);                                      \
       LOADS;                                                                                  \

@@ -66,12 +66,14 @@ constexpr int int_of_e2m3(uint32_t v) {
 // exactly into three bf16 pieces, s = s1 + s2 + s3: s1 = s with the low 16
 // bits of its encoding cleared, s2 the same of s - s1, s3 = s - s1 - s2
 // (each subtraction exact; s3 has at most 8 significant bits).  The GEMM
-// forms sA sW for a 32 x 32 tile with one bf16 matrix instruction whose
-// eight K slots (lanes 0..31) hold
-//     activation row m:   a1 a1 a1 a2 a2 a2 a3 a3
-//     weight column n:    b1 b2 b3 b1 b2 b3 b1 b2
-// so the sum of the eight exact products is sA sW - a3 b3 (a3 b3 < 2^-32
-// sA sW).  Each row or column takes 16 bytes: the bf16 values in that order.
+// forms sA sW for a 32 x 32 tile with one 32x32x8 bf16 matrix instruction
+// whose eight K slots hold
+//     activation row m:   a1 a1 a1 a2 | a2 a2 a3 a3
+//     weight column n:    b1 b2 b3 b1 | b2 b3 b1 b2
+// (slots 0..3 in lanes 0..31, slots 4..7 in lanes 32..63), so the sum of
+// the eight exact products is sA sW - a3 b3 (a3 b3 < 2^-32 sA sW).  Each row
+// or column takes 16 bytes, the bf16 values in that order: a lane reads the
+// 8-byte half of its lane half.
 constexpr int kScaleOpBytes = 16;
 
 // The down-projection factor L1s [K][rp] is stored in the order in which the
