@@ -371,6 +371,18 @@ svdq_status_t svdq_debug_group_sums(const svdq_weights_t *w, int M, int m0,
                                     const void *workspace, size_t ws_bytes,
                                     void *hip_stream);
 
+/* The same group sums for caller-supplied activation codes: qact is device
+ * [M, K/2] canonical packed INT4 codes (two's complement nibbles, low nibble
+ * = even k), the form svdq_quantize_activations exports.  A first kernel
+ * packs them into the fp6 code blocks of `workspace` (overwriting the codes
+ * a previous forward left there; the rest of the workspace is untouched),
+ * then the GEMM kernel sums them as above.  Codes are -7..7; a nibble 0x8
+ * (-8, outside the code set) is entered as 0.  Errors and window limits as
+ * svdq_debug_group_sums; M * K <= 2^31. */
+svdq_status_t svdq_debug_group_sums_codes(const svdq_weights_t *w, const uint8_t *qact, int M,
+                                          int m0, int mcount, int n0, int ncount, int32_t *P,
+                                          void *workspace, size_t ws_bytes, void *hip_stream);
+
 /* ============================================================== AWQ W4A16
  * "Bringing Nunchaku 4-bit diffusion inference to Diffusers" (Russian
  * edition, technical-details section; Korean edition, "Diffusers 내

@@ -78,6 +78,57 @@ def test_group_sums_bit_exact(S):
         assert np.array_equal(P, Pref)
 
 
+def _layer_with_codes(S, qW, rank=8, seed=0):
+    """A layer whose residual weight codes are exactly qW [N, K] (the other
+    arrays are arbitrary: the group sums do not read them)."""
+    from oracle.svdquant import pack_int4
+    N, K = qW.shape
+    rng = np.random.default_rng(seed)
+    bf = lambda a: (a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    hw = S.PreparedHost(N, K, rank, np.ones(K, np.float32), bf(rng.standard_normal((K, rank)) * 0.02),
+                        bf(rng.standard_normal((rank, N)) * 0.02), pack_int4(qW),
+                        np.full((N, K // 64), 0.01, np.float32), np.zeros(N, np.float32))
+    return S.Linear(hw, "cuda")
+
+
+@pytest.mark.parametrize("pattern", ["uniform", "extremes", "minus8"])
+def test_group_sums_of_given_codes(S, pattern):
+    """Caller-supplied canonical activation codes through the GEMM's own
+    sums path (svdq_debug_group_sums_codes), against the oracle's integer
+    group sums: codes uniform in -7..7; codes of magnitude 7 only, with weight
+    rows that repeat activation rows' signs, so P reaches +-3136 = 64 * 49,
+    the largest group sum; and canonical nibbles 0x8 (-8, outside the code
+    set), which enter as 0."""
+    M, N, K = 300, 330, 320
+    rng = np.random.default_rng({"uniform": 7, "extremes": 8, "minus8": 9}[pattern])
+    if pattern == "extremes":
+        qA = np.where(rng.random((M, K)) < 0.5, -7, 7).astype(np.int8)
+        qW = np.where(rng.random((N, K)) < 0.5, -7, 7).astype(np.int8)
+        qW[:40] = qA[:40]            # P = +3136 on the diagonal of the first 40 rows
+        qW[40:80] = -qA[40:80]       # and -3136 on the next 40
+    else:
+        qA = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+        qW = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    packed = O.pack_int4(qA)
+    qA_eff = qA
+    if pattern == "minus8":
+        hole = rng.random((M, K // 2)) < 0.1          # some low nibbles become 0x8
+        packed = np.where(hole, (packed & 0xF0) | 0x08, packed).astype(np.uint8)
+        qA_eff = qA.copy()
+        qA_eff[:, 0::2][hole] = 0
+    layer = _layer_with_codes(S, qW)
+    qact = torch.from_numpy(packed).to("cuda")
+    ws = layer.new_workspace(M)
+    for (m0, mc, n0, nc) in [(0, 256, 0, 256), (44, 256, 74, 256), (299, 1, 329, 1), (0, 80, 0, 80)]:
+        announce(f"given codes {pattern}: window m0={m0} mc={mc} n0={n0} nc={nc}")
+        P = S.debug_group_sums_codes(layer, qact, m0, mc, n0, nc, workspace=ws).cpu().numpy()
+        Pref = O.group_sums(qA_eff[m0:m0 + mc], qW[n0:n0 + nc])
+        assert np.array_equal(P, Pref)
+        if pattern == "extremes" and m0 == 0 and mc == 80:
+            d = np.arange(40)
+            assert np.all(P[d, d] == 3136) and np.all(P[40 + d, 40 + d] == -3136)
+
+
 def test_rank0_without_smoothing(S):
     c = synth.linear_case("r0", 302, 160, 192, 256, 0, x_outlier_n=3, x_outlier_scale=30.0)
     ref, f, layer, X, ws, Y = run_case(S, c, smooth=False)

@@ -466,6 +466,10 @@ def test_forward_validation_errors():
     assert lib.awq_w4a16_forward(None, 64, 128, FAKE, 1, None, FAKE, None) == INV
     assert lib.svdq_debug_group_sums(ctypes.byref(w), 64, 0, 300, 0, 8, FAKE, FAKE, ws, None) == SHAPE
     assert lib.svdq_debug_group_sums(ctypes.byref(w), 64, 60, 8, 0, 8, FAKE, FAKE, ws, None) == SHAPE
+    assert lib.svdq_debug_group_sums_codes(ctypes.byref(w), FAKE, 64, 0, 300, 0, 8, FAKE, FAKE, ws,
+                                           None) == SHAPE
+    assert lib.svdq_debug_group_sums_codes(ctypes.byref(w), None, 64, 0, 8, 0, 8, FAKE, FAKE, ws,
+                                           None) == INV
     assert lib.svdq_gelu_tanh_bf16(FAKE + 2, FAKE, 16, None) == INV
     assert S._lib.svdq_workspace_bytes(0, 128, 128, 4) == 0
     assert S._lib.svdq_device_weights_bytes(128, 100, 4) == 0

@@ -44,7 +44,7 @@ EXPORTS = [
     "svdq_unfused_workspace_bytes", "svdq_linear_forward_unfused", "svdq_linear_gemm", "svdq_mlp_forward",
     "svdq_mlp_quantize", "svdq_mlp_gemm1", "svdq_mlp_gemm2", "svdq_gelu_tanh_bf16",
     "svdq_quantize_activations",
-    "svdq_debug_group_sums", "awq_quantize_weights", "awq_device_weights_bytes",
+    "svdq_debug_group_sums", "svdq_debug_group_sums_codes", "awq_quantize_weights", "awq_device_weights_bytes",
     "awq_pack_device_weights", "awq_w4a16_forward",
     "svdq_mx_host_weights_sizes", "svdq_mx_prepare_weights", "svdq_mx_device_weights_bytes",
     "svdq_mx_pack_device_weights", "svdq_mx_workspace_bytes", "svdq_mx_linear_forward",
@@ -102,6 +102,8 @@ _sig("svdq_quantize_activations", _i, [ctypes.POINTER(DeviceWeights), _vp, _i, _
                                        _vp, _sz, _vp])
 _sig("svdq_debug_group_sums", _i, [ctypes.POINTER(DeviceWeights), _i, _i, _i, _i, _i, _vp, _vp,
                                    _sz, _vp])
+_sig("svdq_debug_group_sums_codes", _i, [ctypes.POINTER(DeviceWeights), _vp, _i, _i, _i, _i, _i,
+                                         _vp, _vp, _sz, _vp])
 _sig("awq_quantize_weights", _i, [_vp, _i, _i, _i, _vp, _vp, _vp])
 _sig("awq_device_weights_bytes", _sz, [_i, _i])
 _sig("awq_pack_device_weights", _i, [_vp, _vp, _vp, _i, _i, _vp, _sz])
@@ -460,6 +462,23 @@ def debug_group_sums(layer: Linear, M: int, m0: int, mcount: int, n0: int, ncoun
     _check(_lib.svdq_debug_group_sums(ctypes.byref(layer._w), M, m0, mcount, n0, ncount,
                                       P.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                       _stream(workspace.device)), "svdq_debug_group_sums")
+    return P
+
+
+def debug_group_sums_codes(layer: Linear, qact: torch.Tensor, m0: int, mcount: int, n0: int,
+                           ncount: int, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Exact group sums of caller-supplied canonical activation codes qact
+    (uint8 [M, K/2] on the device) against the layer's weight codes."""
+    assert qact.dtype == torch.uint8 and qact.is_contiguous() and qact.dim() == 2
+    assert qact.shape[1] == layer.K // 2 and qact.device.type == "cuda"
+    M = qact.shape[0]
+    if workspace is None:
+        workspace = layer.new_workspace(M)
+    P = torch.empty((mcount, ncount, layer.K // 64), dtype=torch.int32, device=qact.device)
+    _check(_lib.svdq_debug_group_sums_codes(ctypes.byref(layer._w), qact.data_ptr(), M, m0, mcount,
+                                            n0, ncount, P.data_ptr(), workspace.data_ptr(),
+                                            workspace.numel(), _stream(qact.device)),
+           "svdq_debug_group_sums_codes")
     return P
 
 

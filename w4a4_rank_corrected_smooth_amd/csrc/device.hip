@@ -1477,6 +1477,39 @@ __global__ void canon_codes_kernel(const uint8_t *__restrict__ qa, int M, int K,
   out[idx] = (uint8_t)(((uint32_t)code[0] & 0x0Fu) | (((uint32_t)code[1] & 0x0Fu) << 4));
 }
 
+// Canonical packed activation codes [M, K/2] (two's complement nibbles, low
+// nibble = even k) -> the workspace's fp6 blocks, the inverse of
+// canon_codes_kernel.  One thread per (group, row tile, lane) writes the
+// lane's three 8-byte words; rows >= M get code 0.  A nibble of 0x8 (-8) is
+// outside the INT4 code set -7..7 and is entered as 0.
+__global__ void pack_codes_kernel(const uint8_t *__restrict__ qact, int M, int K, int T,
+                                  uint8_t *__restrict__ qa) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)(K / kGroup) * T * 64) return;
+  const int lane = (int)(idx % 64);
+  const int64_t t = (idx / 64) % T, g = idx / 64 / T;
+  const int64_t row = t * kTile + lane % 32;
+  const int h = lane / 32;
+  uint64_t wv[3] = {0, 0, 0};
+  if (row < M) {
+    const uint8_t *src = qact + row * (K / 2) + g * (kGroup / 2);
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      const int k = lane_code_k(h, c);
+      int q = (src[k / 2] >> (4 * (k & 1))) & 15;
+      q = q >= 8 ? q - 16 : q;
+      if (q == -8) q = 0;
+      const uint64_t v = e2m3_of_int(q);
+      const int bit = 6 * c, j = bit / 64, sh = bit % 64;
+      wv[j] |= v << sh;
+      if (sh > 58) wv[j + 1] |= v >> (64 - sh);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    *reinterpret_cast<uint64_t *>(qa + pair_offset(g, t, T, lane, j)) = wv[j];
+}
+
 // fp32 scale of (m, g) from its operand form: a1 + a2 + a3, exact
 __global__ void canon_scales_kernel(const uint4 *__restrict__ sa, int M, int Mp, int G,
                                     float *__restrict__ out) {
@@ -2016,20 +2049,26 @@ svdq_status_t svdq_quantize_activations(const svdq_weights_t *w, const void *X, 
   return launch_status("inspection kernels");
 }
 
-svdq_status_t svdq_debug_group_sums(const svdq_weights_t *w, int M, int m0, int mcount, int n0,
-                                    int ncount, int32_t *P, const void *workspace,
-                                    size_t ws_bytes, void *hip_stream) {
-  svdq_status_t st = validate_weights(w, "svdq_debug_group_sums");
+static svdq_status_t validate_group_sums(const svdq_weights_t *w, int M, int m0, int mcount,
+                                         int n0, int ncount, const int32_t *P,
+                                         const void *workspace, size_t ws_bytes, const char *who) {
+  svdq_status_t st = validate_weights(w, who);
   if (st != SVDQ_OK) return st;
-  if (!P || !workspace) return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_debug_group_sums: NULL pointer");
-  if (M < 1 || mcount < 1 || ncount < 1 || mcount > 256 || ncount > 256 || m0 < 0 || n0 < 0 ||
-      m0 + mcount > M || n0 + ncount > w->N)
-    return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "svdq_debug_group_sums: bad window");
-  const WeightLayout L(w->N, w->K, w->rank);
+  if (!P || !workspace) return fail(SVDQ_ERR_INVALID_ARGUMENT, "%s: NULL pointer", who);
+  if (M < 1 || (int64_t)M * w->K > ((int64_t)1 << 31) || mcount < 1 || ncount < 1 ||
+      mcount > 256 || ncount > 256 || m0 < 0 || n0 < 0 || m0 + mcount > M || n0 + ncount > w->N)
+    return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "%s: bad window", who);
   const WorkLayout Wl(M, w->K, w->rank);
   if ((int64_t)ws_bytes < Wl.total)
-    return fail(SVDQ_ERR_WORKSPACE_TOO_SMALL, "workspace needs %lld bytes", (long long)Wl.total);
-  if ((st = check_device()) != SVDQ_OK) return st;
+    return fail(SVDQ_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %lld bytes", who, (long long)Wl.total);
+  return check_device();
+}
+
+static svdq_status_t launch_group_sums(const svdq_weights_t *w, int M, int m0, int mcount, int n0,
+                                       int ncount, int32_t *P, const void *workspace,
+                                       hipStream_t stream) {
+  const WeightLayout L(w->N, w->K, w->rank);
+  const WorkLayout Wl(M, w->K, w->rank);
   K2Args a = make_k2_args(L, Wl, w, M, static_cast<const uint8_t *>(workspace));
   a.P = P;
   a.m0 = m0; a.mcount = mcount; a.n0 = n0; a.ncount = ncount;
@@ -2039,8 +2078,36 @@ svdq_status_t svdq_debug_group_sums(const svdq_weights_t *w, int M, int m0, int 
   a.TN = (n0 + ncount - a.tile_n0 + k2c::BN - 1) / k2c::BN;
   const dim3 grid((unsigned)round_up((int64_t)a.TM * a.TN, 8));
   hipLaunchKernelGGL((k2_w4a4_gemm<MODE_SUMS, SVDQ_EPILOGUE_NONE, true>), grid, dim3(k2c::THREADS), 0,
-                     static_cast<hipStream_t>(hip_stream), a);
+                     stream, a);
   return launch_status("group-sum kernel launch");
+}
+
+svdq_status_t svdq_debug_group_sums(const svdq_weights_t *w, int M, int m0, int mcount, int n0,
+                                    int ncount, int32_t *P, const void *workspace,
+                                    size_t ws_bytes, void *hip_stream) {
+  const svdq_status_t st = validate_group_sums(w, M, m0, mcount, n0, ncount, P, workspace, ws_bytes,
+                                               "svdq_debug_group_sums");
+  if (st != SVDQ_OK) return st;
+  return launch_group_sums(w, M, m0, mcount, n0, ncount, P, workspace,
+                           static_cast<hipStream_t>(hip_stream));
+}
+
+svdq_status_t svdq_debug_group_sums_codes(const svdq_weights_t *w, const uint8_t *qact, int M,
+                                          int m0, int mcount, int n0, int ncount, int32_t *P,
+                                          void *workspace, size_t ws_bytes, void *hip_stream) {
+  if (!qact) return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_debug_group_sums_codes: NULL qact");
+  const svdq_status_t st = validate_group_sums(w, M, m0, mcount, n0, ncount, P, workspace, ws_bytes,
+                                               "svdq_debug_group_sums_codes");
+  if (st != SVDQ_OK) return st;
+  const WorkLayout Wl(M, w->K, w->rank);
+  const int T = (int)(Wl.Mp / kTile);
+  const int64_t threads = (int64_t)(w->K / kGroup) * T * 64;
+  const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipLaunchKernelGGL(pack_codes_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                     qact, M, w->K, T, static_cast<uint8_t *>(workspace) + Wl.qa);
+  const svdq_status_t ls = launch_status("code packing kernel launch");
+  if (ls != SVDQ_OK) return ls;
+  return launch_group_sums(w, M, m0, mcount, n0, ncount, P, workspace, stream);
 }
 
 // ------------------------------------------------------------- MXFP4
