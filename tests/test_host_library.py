@@ -620,19 +620,20 @@ def test_workspace_includes_k_split_partials():
     def base(M, K, r):
         Mp, G, rp = up(M), K // 64, -(-r // 32) * 32 if r else 0
         T = Mp // 32
+        gmin = 12 if r > 0 and G >= 12 else 4   # quantiser splits: with a branch, >= 12 groups each
         Ssp = 1
         for s_ in range(1, G + 1):
             if G % s_:
                 continue
-            if s_ == 1 or G // s_ >= 4:
+            if s_ == 1 or G // s_ >= gmin:
                 Ssp = s_
-            if G // s_ >= 4 and T * s_ >= 384:
+            if G // s_ >= gmin and T * s_ >= 384:
                 break
         # fp6 codes, 16-byte scale operands, fp32 partials of D
         return up(Mp * K * 3 // 4) + up(G * Mp * 16) + up(max(Ssp, 2) * Mp * rp * 4)
     for M, N, K, r, ks in [(4608, 12288, 3072, 32, 1), (1024, 3072, 3072, 128, 5), (100, 200, 1024, 8, 2),
                            (1, 3072, 12288, 32, 8), (64, 512, 448, 4, 1), (4608, 3072, 12288, 32, 1),
-                           (512, 9216, 3072, 32, 1), (512, 3072, 3072, 32, 6)]:
+                           (512, 9216, 3072, 32, 1), (512, 3072, 3072, 32, 6), (1024, 3072, 3072, 0, 5)]:
         want = base(M, K, r) + (ks * up(M) * up(N) * 4 if ks > 1 else 0)
         assert lib.svdq_workspace_bytes(M, N, K, r) == want, (M, N, K, r)
 

@@ -844,16 +844,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if constexpr (SPLIT) {
     // K-split: the fp32 partial tile, padded rows and columns included (the
     // partial buffer is [Mp][Np]); bias and the epilogue come in the sum.
+    // Each 32-row half of the wavefront's tile goes out through its own LDS
+    // so the stores are whole 16-byte vectors along rows.
+    __syncthreads();                    // every wavefront is done with the stages
     float *pp = p.part + (int64_t)split * p.Mp * p.Np;
+    float *wbuf = reinterpret_cast<float *>(smem + w * EPI_WAVE_BYTES);
 #pragma unroll
-    for (int i = 0; i < WTM; ++i)
+    for (int i = 0; i < WTM; ++i) {
 #pragma unroll
       for (int j = 0; j < WTN; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = wm + 32 * i + 8 * (e >> 2) + 4 * hl + (e & 3), n = wn + 32 * j + ln;
-          pp[(int64_t)m * p.Np + n] = acc[i][j][e];
-        }
+        for (int e = 0; e < 16; ++e)
+          wbuf[(8 * (e >> 2) + 4 * hl + (e & 3)) * WCOLS + 32 * j + ln] = acc[i][j][e];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      constexpr int LPR = WCOLS / 4;             // lanes per row: 4 floats each
+#pragma unroll
+      for (int q = 0; q < 32 * LPR / 64; ++q) {
+        const int r = q * (64 / LPR) + lane / LPR, c = (lane % LPR) * 4;
+        *reinterpret_cast<float4 *>(pp + (int64_t)(wm + 32 * i + r) * p.Np + wn + c) =
+            *reinterpret_cast<const float4 *>(wbuf + r * WCOLS + c);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
   } else if constexpr (MODE == MODE_FWD && QNEXT) {
     // MLP pair: this layer's output never goes to memory.  Bias (+ GELU),
     // rounded to bf16 (exactly the values the unfused path stores), then the
@@ -1043,28 +1059,54 @@ template <int EPI, bool OUT_F32>
 __global__ __launch_bounds__(256) void k2_split_sum(const float *__restrict__ part, int ksplit, int M,
                                                     int N, int Mp, int Np, const float *__restrict__ bias,
                                                     void *__restrict__ Y) {
+  // eight consecutive columns per thread; every range's partial is loaded
+  // before any is added, and the adds run in range order
+  constexpr int kMaxSplit = 8;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int nq = Np / 4;
+  const int nq = Np / 8;
   const int64_t m = idx / nq;
-  const int n0 = (int)(idx - m * nq) * 4;
+  const int n0 = (int)(idx - m * nq) * 8;
   if (m >= M || n0 >= N) return;
   const float *src = part + m * Np + n0;
-  float4 acc = *reinterpret_cast<const float4 *>(src);
-  for (int k = 1; k < ksplit; ++k) {
-    const float4 v = *reinterpret_cast<const float4 *>(src + (int64_t)k * Mp * Np);
-    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-  }
-  const float a4[4] = {acc.x, acc.y, acc.z, acc.w};
+  float4 v[kMaxSplit][2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int n = n0 + t;
-    if (n >= N) break;
-    float y = a4[t] + bias[n];
-    if constexpr (EPI == SVDQ_EPILOGUE_GELU_TANH) y = gelu_tanh_f32(y);
-    if constexpr (OUT_F32)
-      reinterpret_cast<float *>(Y)[m * N + n] = y;
-    else
-      reinterpret_cast<__bf16 *>(Y)[m * N + n] = (__bf16)y;
+  for (int k = 0; k < kMaxSplit; ++k)
+    if (k < ksplit) {
+      v[k][0] = *reinterpret_cast<const float4 *>(src + (int64_t)k * Mp * Np);
+      v[k][1] = *reinterpret_cast<const float4 *>(src + (int64_t)k * Mp * Np + 4);
+    }
+  float y[8] = {v[0][0].x, v[0][0].y, v[0][0].z, v[0][0].w, v[0][1].x, v[0][1].y, v[0][1].z, v[0][1].w};
+#pragma unroll
+  for (int k = 1; k < kMaxSplit; ++k)
+    if (k < ksplit) {
+      y[0] += v[k][0].x; y[1] += v[k][0].y; y[2] += v[k][0].z; y[3] += v[k][0].w;
+      y[4] += v[k][1].x; y[5] += v[k][1].y; y[6] += v[k][1].z; y[7] += v[k][1].w;
+    }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    y[t] += bias[n0 + t];          // bias is padded to Np
+    if constexpr (EPI == SVDQ_EPILOGUE_GELU_TANH) y[t] = gelu_tanh_f32(y[t]);
+  }
+  if (N % 8 == 0) {                // whole 16-byte vectors (n0 + 8 <= N)
+    if constexpr (OUT_F32) {
+      float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(Y) + m * N + n0);
+      dst[0] = make_float4(y[0], y[1], y[2], y[3]);
+      dst[1] = make_float4(y[4], y[5], y[6], y[7]);
+    } else {
+      uint32_t h[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        h[t] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y[2 * t]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y[2 * t + 1]) << 16);
+      *reinterpret_cast<uint4 *>(reinterpret_cast<__bf16 *>(Y) + m * N + n0) = make_uint4(h[0], h[1], h[2], h[3]);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if (n0 + t < N) {
+        if constexpr (OUT_F32) reinterpret_cast<float *>(Y)[m * N + n0 + t] = y[t];
+        else reinterpret_cast<__bf16 *>(Y)[m * N + n0 + t] = (__bf16)y[t];
+      }
   }
 }
 
@@ -1728,7 +1770,7 @@ static svdq_status_t launch_k2(const svdq_weights_t *w, int M, void *Y, svdq_dty
       hipLaunchKernelGGL((k2_w4a4_gemm<MODE_FWD, NONE, true, false, false, true>), sgrid, block, 0, stream, a);
     svdq_status_t st = launch_status("GEMM kernel launch");
     if (st != SVDQ_OK) return st;
-    const int64_t threads = (int64_t)M * (L.Np / 4);
+    const int64_t threads = (int64_t)M * (L.Np / 8);
     const dim3 rgrid((unsigned)((threads + 255) / 256));
 #define K2_SUM(E, F) hipLaunchKernelGGL((k2_split_sum<E, F>), rgrid, dim3(256), 0, stream, a.part, ks, M, \
                                         w->N, (int)Wl.Mp, (int)L.Np, a.bias, Y)

@@ -108,15 +108,23 @@ struct WeightLayout {
 // Groups of 64 handled by one quantiser workgroup: the K range is split S
 // ways so that enough workgroups exist to keep every CU streaming (about 384:
 // more, shorter splits lose more to each workgroup's start-up than they gain),
-// with, where possible, at least 4 groups per split (one per wavefront).
-// Every split adds a partial low-rank product the GEMM has to sum.
-constexpr int64_t k1_splits(int64_t Mp, int64_t G) {
+// with at least 4 groups per split (one per wavefront).  With a low-rank
+// branch, splits hold at least 12 groups where K has them (three chunks of
+// four, the depth of the quantiser's copy pipeline): every split adds a
+// partial low-rank product that each GEMM workgroup holding a rank chunk has
+// to sum.  At 1024 x 3072, r = 128, twelve splits of 4 groups took 10.4 +
+// 48.0 us (quantiser + GEMM, back to back) against 9.6 + 40.5 us for four
+// splits of 12 (6 splits: 8.5 + 45.2 us; 3 splits: 11.0 + 40.3 us); at
+// rank 0 the twelve splits are faster (4.2 against 5.6 us for the quantiser
+// alone).  The 4608-token shapes get 3 splits either way.
+constexpr int64_t k1_splits(int64_t Mp, int64_t G, int64_t rank) {
   const int64_t T = Mp / kTile;
+  const int64_t gmin = rank > 0 && G >= 12 ? 12 : 4;
   int64_t best = 1;
   for (int64_t s = 1; s <= G; ++s) {
     if (G % s != 0) continue;
-    if (s == 1 || G / s >= 4) best = s;
-    if (G / s >= 4 && T * s >= 384) return s;
+    if (s == 1 || G / s >= gmin) best = s;
+    if (G / s >= gmin && T * s >= 384) return s;
   }
   return best;
 }
@@ -127,7 +135,7 @@ struct WorkLayout {
   int64_t qa = 0, sa = 0, d = 0, total = 0;
   constexpr WorkLayout(int64_t M_, int64_t K_, int64_t rank_)
       : M(M_), Mp(round_up(M_, kPad)), K(K_), G(K_ / kGroup), rp(rank_pad((int)rank_)),
-        S(k1_splits(round_up(M_, kPad), K_ / kGroup)) {
+        S(k1_splits(round_up(M_, kPad), K_ / kGroup, rank_)) {
     int64_t o = 0;
     qa = o; o = round_up(o + Mp * K * 3 / 4, kAlign);    // fp6 codes, tiled
     sa = o; o = round_up(o + G * Mp * kScaleOpBytes, kAlign);   // scale operands [G][Mp]
@@ -204,7 +212,7 @@ struct MxWorkLayout {
   int64_t qa = 0, sa = 0, d = 0, total = 0;
   constexpr MxWorkLayout(int64_t M_, int64_t K_, int64_t rank_)
       : M(M_), Mp(round_up(M_, kPad)), K(K_), G(K_ / kGroup), rp(rank_pad((int)rank_)),
-        S(k1_splits(round_up(M_, kPad), K_ / kGroup)) {
+        S(k1_splits(round_up(M_, kPad), K_ / kGroup, rank_)) {
     int64_t o = 0;
     qa = o; o = round_up(o + Mp * K / 2, kAlign);          // E2M1 codes, tiled
     sa = o; o = round_up(o + Mp * (K / kMxBlock), kAlign); // E8M0 scales, tiled
