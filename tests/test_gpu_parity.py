@@ -226,7 +226,10 @@ def ksplit_of(M, N, K):
                                                  (300, 600, 2048, 16, torch.float32, False),
                                                  (129, 257, 4096, 32, torch.float32, False),
                                                  (64, 512, 1600, 5, torch.bfloat16, True),
-                                                 (1, 3072, 12288, 32, torch.bfloat16, False)])
+                                                 (1, 3072, 12288, 32, torch.bfloat16, False),
+                                                 # N not a multiple of 8: the partial sum's per-element tail
+                                                 (70, 300, 1024, 8, torch.bfloat16, False),
+                                                 (33, 130, 2048, 4, torch.float32, True)])
 def test_k_split_gemm(S, M, N, K, rank, out, gelu):
     ks = ksplit_of(M, N, K)
     assert ks >= 2
