@@ -602,8 +602,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // each range's partial carries some of them and no range waits on all):
     // acc = D L2 on bf16 matrix cores, D entered as a bf16 high part plus a
     // bf16 remainder.  D of the workgroup's 128 rows is assembled once, in
-    // the fourth stage buffer (free until the main loop starts), 32 ranks at
-    // a time: wavefront w sums the K1 splits' partials of rows 32 w .. 32 w
+    // an LDS staging area (below) that is free until the main loop starts:
+    // wavefront w sums the K1 splits' partials of rows 32 w .. 32 w
     // + 31 in split order (lane l: row l / 2, ranks 16 (l % 2) + [0, 16);
     // loads issued four splits at a time, indices clamped, surplus ones not
     // added) and stores the two bf16 parts; every wavefront then reads its
