@@ -199,6 +199,9 @@ CALIBRATION_BYTES = 256 << 20
 
 SQ_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
                "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU")
+# a second pass: where the wavefronts' cycles go (waits, issue, LDS)
+SQ_COUNTERS_MEM = ("GRBM_GUI_ACTIVE", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+                   "SQ_ACTIVE_INST_ANY", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT")
 
 
 def summarize_trace(trace_dir, out_path, title, command, json_path=None, note=""):
@@ -271,10 +274,9 @@ def summarize_floor(trace_dir, jsonl, out_path, command):
     print("\n".join(lines))
 
 
-def summarize_counters(pmc_dir, out_path, command):
-    """Per-kernel shader counters (one rocprofv3 --pmc pass of the default
-    profile command), averaged over each kernel's dispatches, with the clock
-    and the vector-ALU and matrix-pipe occupancy they imply."""
+def _counter_means(pmc_dir, counters):
+    """Per-kernel means of a rocprofv3 --pmc pass (the library's kernels
+    only) and each kernel's dispatch durations (us)."""
     import csv
     import glob
     from collections import defaultdict
@@ -288,6 +290,18 @@ def summarize_counters(pmc_dir, out_path, command):
             continue
         vals[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
         durs[name][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    out = {}
+    for name in sorted(vals):
+        v = {c: float(np.mean(vals[name][c])) for c in counters if vals[name][c]}
+        if len(v) == len(counters):
+            out[name] = (v, len(durs[name]), float(np.mean(list(durs[name].values()))))
+    return out
+
+
+def summarize_counters(pmc_dir, out_path, command):
+    """Per-kernel shader counters (one rocprofv3 --pmc pass of the default
+    profile command), averaged over each kernel's dispatches, with the clock
+    and the vector-ALU and matrix-pipe occupancy they imply."""
     simds, xcds = 1024, 8
     lines = ["# Shader counters per kernel, Flux MLP pair 4608x3072x12288 r32 + AWQ 1x3072x18432", "",
              "Command:", "", "```", command, "```", "",
@@ -299,16 +313,42 @@ def summarize_counters(pmc_dir, out_path, command):
              "which runs slower than a plain trace.", "",
              "| kernel | dispatches | us | cycles | " + " | ".join(SQ_COUNTERS[1:]) + " | VALU busy | matrix busy |",
              "|---|---:|---:|---:|" + "---:|" * (len(SQ_COUNTERS) - 1) + "---:|---:|"]
-    for name in sorted(vals):
-        v = {c: float(np.mean(vals[name][c])) for c in SQ_COUNTERS if vals[name][c]}
-        if len(v) < len(SQ_COUNTERS):
-            continue
-        d = float(np.mean(list(durs[name].values())))
+    for name, (v, n, d) in _counter_means(pmc_dir, SQ_COUNTERS).items():
         cyc = v["GRBM_GUI_ACTIVE"] / xcds
         valu = (v["SQ_INSTS_VALU"] - v["SQ_INSTS_MFMA"]) * 4 / (simds * cyc)
         mfma = v["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * cyc)
-        lines.append(f"| `{name}` | {len(durs[name])} | {d:.1f} | {cyc:.4g} | " +
+        lines.append(f"| `{name}` | {n} | {d:.1f} | {cyc:.4g} | " +
                      " | ".join(f"{v[c]:.4g}" for c in SQ_COUNTERS[1:]) + f" | {valu:.0%} | {mfma:.0%} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_counters_mem(pmc_dir, out_path, command):
+    """The second counter pass: the share of the wavefronts' cycles spent
+    waiting on s_waitcnt (SQ_WAIT_ANY), waiting for an instruction to issue
+    (SQ_WAIT_INST_ANY) and issuing (SQ_ACTIVE_INST_ANY), all against
+    SQ_WAVE_CYCLES, and the LDS instruction and bank-conflict counts."""
+    xcds = 8
+    lines = ["# Where the wavefronts' cycles go, Flux MLP pair 4608x3072x12288 r32 + AWQ 1x3072x18432", "",
+             "Command:", "", "```", command, "```", "",
+             "Means over each kernel's dispatches.  The three shares are of SQ_WAVE_CYCLES (the cycles "
+             "summed over resident wavefronts): SQ_WAIT_ANY counts cycles a wavefront waits on a counter "
+             "(s_waitcnt: memory, LDS), SQ_WAIT_INST_ANY cycles it waits for its next instruction to "
+             "issue (a dependency, a busy pipe, the barrier), SQ_ACTIVE_INST_ANY cycles it issues; the "
+             "LDS wait share is SQ_WAIT_INST_LDS of the same.  Conflicts per LDS instruction = "
+             "SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS.  Durations come from the counter pass.", "",
+             "| kernel | dispatches | us | cycles | " + " | ".join(SQ_COUNTERS_MEM[1:]) +
+             " | waiting on counters | waiting to issue | issuing | LDS wait share | conflicts per LDS instr |",
+             "|---|---:|---:|---:|" + "---:|" * (len(SQ_COUNTERS_MEM) - 1) + "---:|---:|---:|---:|---:|"]
+    for name, (v, n, d) in _counter_means(pmc_dir, SQ_COUNTERS_MEM).items():
+        cyc = v["GRBM_GUI_ACTIVE"] / xcds
+        wc = max(v["SQ_WAVE_CYCLES"], 1.0)
+        lines.append(f"| `{name}` | {n} | {d:.1f} | {cyc:.4g} | " +
+                     " | ".join(f"{v[c]:.4g}" for c in SQ_COUNTERS_MEM[1:]) +
+                     f" | {v['SQ_WAIT_ANY'] / wc:.0%} | {v['SQ_WAIT_INST_ANY'] / wc:.0%} |"
+                     f" {v['SQ_ACTIVE_INST_ANY'] / wc:.0%} | {v['SQ_WAIT_INST_LDS'] / wc:.1%} |"
+                     f" {v['SQ_LDS_BANK_CONFLICT'] / max(v['SQ_INSTS_LDS'], 1.0):.3f} |")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -938,6 +978,8 @@ def main():
                     help="per-configuration kernel timings (one JSON line each) instead of the step")
     ap.add_argument("--summarize-counters", metavar="PMC_DIR",
                     help="CPU only: summarise a rocprofv3 --pmc pass of the shader counters into profiles/")
+    ap.add_argument("--summarize-counters-mem", metavar="PMC_DIR",
+                    help="CPU only: summarise the second --pmc pass (waits, issue, LDS) into profiles/")
     ap.add_argument("--block", action="store_true",
                     help="launch study of one transformer block's calls, eager and as a HIP graph")
     ap.add_argument("--cpu-configs", action="store_true",
@@ -969,6 +1011,13 @@ def main():
         t, j = args.summarize_configs
         summarize_configs(t, j, os.path.join(ROOT, "profiles", "kernels_all_configs.md"),
                           f"rocprofv3 --kernel-trace --stats -f csv -d {t} -- python3 bench.py --configs")
+        return
+    if args.summarize_counters_mem:
+        base = "python3 bench.py --no-cpu-baseline --calibration-copy --skip-unfused --skip-mx"
+        summarize_counters_mem(args.summarize_counters_mem,
+                               os.path.join(ROOT, "profiles", "shader_counters_mem_flux_mlp_pair.md"),
+                               f"rocprofv3 --pmc {' '.join(SQ_COUNTERS_MEM)} -f csv -d "
+                               f"{args.summarize_counters_mem} -- {base}")
         return
     if args.summarize_counters:
         base = "python3 bench.py --no-cpu-baseline --calibration-copy --skip-unfused --skip-mx"

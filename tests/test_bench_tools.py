@@ -76,3 +76,25 @@ def test_counter_summary(tmp_path):
     assert cells[2] == "2" and cells[3] == "5.0" and cells[4] == "1000"
     assert cells[-3] == "40%"                    # 1024 * 100 vector instructions x 4 / (1024 x 1000)
     assert cells[-2] == "25%"                    # 1024 * 250 matrix cycles / (1024 x 1000)
+
+
+def test_counter_summary_of_waits_and_lds(tmp_path):
+    d = tmp_path / "pmc" / "x"
+    d.mkdir(parents=True)
+    vals = {"GRBM_GUI_ACTIVE": 8 * 1000.0, "SQ_WAVE_CYCLES": 4000.0, "SQ_WAIT_ANY": 1000.0,
+            "SQ_WAIT_INST_ANY": 2000.0, "SQ_ACTIVE_INST_ANY": 800.0, "SQ_INSTS_LDS": 500.0,
+            "SQ_WAIT_INST_LDS": 40.0, "SQ_LDS_BANK_CONFLICT": 25.0}
+    with open(d / "1_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
+                    "End_Timestamp"])
+        for c, v in vals.items():
+            w.writerow([1, "void k2_w4a4_gemm<0, 0, false, true, false, false>(K2Args)", c, v, 0, 3000])
+            w.writerow([1, "void some_other_kernel(int)", c, v, 0, 3000])
+    out = tmp_path / "m.md"
+    bench.summarize_counters_mem(str(tmp_path / "pmc"), str(out), "cmd")
+    rows = [l for l in out.read_text().splitlines() if l.startswith("| `")]
+    assert len(rows) == 1                        # the library's kernels only
+    cells = [c.strip() for c in rows[0].split("|")]
+    assert cells[3] == "3.0" and cells[4] == "1000"
+    assert cells[-6:-1] == ["25%", "50%", "20%", "1.0%", "0.050"]
