@@ -1,6 +1,10 @@
 // Offline float64 linear algebra: Gram matrix and a top-r symmetric
 // eigensolver (Householder tridiagonalisation + bisection + inverse
-// iteration), used for the top-r SVD of the smoothed weight.
+// iteration), used for the top-r SVD of the smoothed weight.  The methods
+// are the textbook ones for the symmetric eigenproblem (G. H. Golub and
+// C. F. Van Loan, "Matrix Computations", the chapter on the symmetric
+// eigenvalue problem: Householder tridiagonalisation, Sturm-sequence
+// bisection, inverse iteration), written here from their mathematics.
 #include "host_linalg.h"
 
 #include <algorithm>
