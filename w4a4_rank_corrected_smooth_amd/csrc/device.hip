@@ -224,19 +224,24 @@ __device__ __forceinline__ uint32_t quantize_lane_mx(const uint4 (&xm)[4], const
 // stored as fp6 E2M3 (exact for these integers).  The raw bf16 values also
 // feed a 32x32x16 bf16 MFMA against L1s for the low-rank down-projection;
 // the four wavefronts' partial products are summed through LDS and written
-// as this split's partial D.
+// as this split's partial D.  With two or more 32-rank blocks the blocks go
+// to workgroups of their own (grid z, one block each; the first also
+// quantises and stores the codes), so the workgroup keeps the registers of
+// the one-block form and the grid grows with the rank: at 1024 x 3072,
+// r = 128, 7.5-7.7 us against 9.5 us with all four blocks in one workgroup
+// (back to back), at 4608 x 3072, 20.3 against 24.5 us.
 constexpr int kK1Chunk = 4;                        // groups per chunk = wavefronts
 constexpr int kK1RowBytes = kK1Chunk * kGroup * 2;  // 512
 constexpr int kK1XBytes = kTile * kK1RowBytes;     // 16 KB of X per chunk
 constexpr int kK1BufBytes = kK1XBytes + kK1Chunk * kGroup * 4;   // + 1 KB of 1/lambda
 constexpr int kK1Bufs = 3;
 constexpr int kK1LdsBytes = kK1Bufs * kK1BufBytes;
-template <int TB, bool MX = false>   // rank_pad / 32; MXFP4 instead of INT4 codes
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3 : 1))) void k1_quantize_lowrank_down(
+template <int TB, bool MX = false>   // 32-rank blocks per workgroup (0 or 1); MXFP4 instead of INT4 codes
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k1_quantize_lowrank_down(
     const uint16_t *__restrict__ X, int M, int K, int Mp, int S,
     const float *__restrict__ iota, const uint16_t *__restrict__ l1t,
     uint8_t *__restrict__ qa, float *__restrict__ sa, float *__restrict__ dpart,
-    int64_t *__restrict__ dzero, int rpz) {
+    int64_t *__restrict__ dzero, int rpz, int tbt) {
   __shared__ __attribute__((aligned(16))) uint8_t k1_lds[kK1LdsBytes];
   const uint32_t lds_u32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)k1_lds;
   const int t = blockIdx.x, s = blockIdx.y;
@@ -245,6 +250,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
   const int G = K / kGroup, Gs = G / S, T = Mp / kTile;
   const int rr = lane & 31, h = lane >> 5;
   const int row = t * kTile + rr;
+  // rank blocks rb0 .. rb0 + TB - 1 of the layer's tbt; with the rank split
+  // across workgroups (grid z), only the first quantises and stores codes
+  const int rb0 = (int)blockIdx.z * TB;
+  const bool wq = rb0 == 0;
   const int nch = (Gs + kK1Chunk - 1) / kK1Chunk;
   constexpr int NB = TB > 0 ? TB : 1;
   constexpr int L1N = 4 * TB;                      // L1s loads per wave and chunk
@@ -286,7 +295,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
 #pragma unroll
         for (int b = 0; b < TB; ++b)
           d[j * NB + b] = *reinterpret_cast<const uint4 *>(
-              l1t + ((((int64_t)g * TB + b) * 4 + j) * 64 + lane) * 8);
+              l1t + ((((int64_t)g * tbt + rb0 + b) * 4 + j) * 64 + lane) * 8);
     }
   };
   v16f dacc[NB];
@@ -310,7 +319,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
     const int c = c0 + u;
     if (c >= nch) break;
     constexpr int kStores = MX ? 2 : 4;
-    const int later = kStores * min(c, kK1Bufs - 1) + (ncopy + L1N) * (min(nch - 1, c + kK1Bufs - 1) - c);
+    const int later = (wq ? kStores : 0) * min(c, kK1Bufs - 1) + (ncopy + L1N) * (min(nch - 1, c + kK1Bufs - 1) - c);
     vmcnt_wait_dyn(later);
     __syncthreads();
     const uint8_t *buf = k1_lds + u * kK1BufBytes;
@@ -331,7 +340,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
       io[2 * j] = iota_c[4 * j + 2 * h];
       io[2 * j + 1] = iota_c[4 * j + 2 * h + 1];
     }
-    if constexpr (MX) {
+    if (!wq) {
+      // another workgroup of this row tile and split quantises
+    } else if constexpr (MX) {
       // the lane's MX block: channels 32 h + [0, 32) of its group
       uint4 xm[4];
 #pragma unroll
@@ -372,7 +383,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
     // the copy buffers are free now: the four wavefronts' partial products
     // meet there (4 x 16 x 64 floats = 16 KB)
     float (*red)[16][64] = reinterpret_cast<float (*)[16][64]>(k1_lds);
-    constexpr int RP = TB * 32;
+    const int RP = tbt * 32;
     for (int b = 0; b < TB; ++b) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) red[w][e][lane] = dacc[b][e];
@@ -382,14 +393,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
         const int e = 4 * w + i;
         const float v = red[0][e][lane] + red[1][e][lane] + red[2][e][lane] + red[3][e][lane];
         const int r = t * kTile + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        dpart[((int64_t)s * Mp + r) * RP + b * 32 + (lane & 31)] = v;
+        dpart[((int64_t)s * Mp + r) * RP + (rb0 + b) * 32 + (lane & 31)] = v;
       }
       __syncthreads();
     }
   }
   // For a fused MLP pair: clear this row tile's rows of the next layer's
   // fixed-point D, which the GEMM that follows accumulates into.
-  if (dzero != nullptr && s == 0) {
+  if (dzero != nullptr && s == 0 && wq) {
     int64_t *dz = dzero + (int64_t)t * kTile * rpz;
     for (int i = threadIdx.x; i < kTile * rpz / 2; i += 256)
       reinterpret_cast<int4 *>(dz)[i] = make_int4(0, 0, 0, 0);
@@ -402,9 +413,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB <= 1 ? 3
 // Workgroup: 4 wavefronts (2 x 2), output tile 128 x 256; wavefront tile
 // 64 x 128 (2 x 4 MFMA tiles of 32 x 32).  Two workgroups share a CU, so
 // each SIMD runs wavefronts of two independent workgroups.  One pipeline
-// stage holds one group of 64 input channels in LDS (A codes, B codes, their
-// fp32 scales), copied global -> LDS by the load unit; four stages rotate.
-// Per group a workgroup copies 20 KB for 32768 outputs.
+// stage holds one group of 64 input channels in LDS (A codes, B codes and
+// both sides' scale operands), copied global -> LDS by the load unit; three
+// stages rotate (the MXFP4 form: four).  Per group a workgroup copies 24 KB
+// for 32768 outputs.
 //
 // Per 32 x 32 tile and group:
 //   P  = v_mfma_scale_f32_32x32x64_f8f6f4 on fp6 codes (unit block scales):
@@ -1648,7 +1660,10 @@ svdq_status_t launch_k1(const WL &L, const KL &Wl, const svdq_weights_t *w,
                         const void *X, int M, uint8_t *ws, hipStream_t st,
                         int64_t *dzero = nullptr, int rpz = 0, bool with_down = true) {
   const uint8_t *blob = static_cast<const uint8_t *>(w->blob);
-  const dim3 grid((unsigned)(Wl.Mp / kTile), (unsigned)Wl.S);
+  const int tbt = with_down ? (int)(L.rp / 32) : 0;
+  // two or more rank blocks: one workgroup per block (grid z), one block each
+  const int rsplit = tbt >= 2 ? tbt : 1;
+  const dim3 grid((unsigned)(Wl.Mp / kTile), (unsigned)Wl.S, (unsigned)rsplit);
   const uint16_t *x = static_cast<const uint16_t *>(X);
   const float *iota = reinterpret_cast<const float *>(blob + L.iota);
   const uint16_t *l1t = reinterpret_cast<const uint16_t *>(blob + L.l1t);
@@ -1657,14 +1672,13 @@ svdq_status_t launch_k1(const WL &L, const KL &Wl, const svdq_weights_t *w,
   float *dp = reinterpret_cast<float *>(ws + Wl.d);
   const int K = w->K, Mp = (int)Wl.Mp, S = (int)Wl.S;
   const size_t lds = 0;
-  switch (with_down ? L.rp / 32 : 0) {
+  switch (tbt / rsplit) {
 #define K1_CASE(TB)                                                                       \
   case TB:                                                                                \
     hipLaunchKernelGGL((k1_quantize_lowrank_down<TB, MX>), grid, dim3(256), lds, st, x, M, K, Mp, \
-                       S, iota, l1t, qa, sa, dp, dzero, rpz);                             \
+                       S, iota, l1t, qa, sa, dp, dzero, rpz, tbt);                        \
     break;
-    K1_CASE(0) K1_CASE(1) K1_CASE(2) K1_CASE(3) K1_CASE(4) K1_CASE(5) K1_CASE(6) K1_CASE(7)
-    K1_CASE(8)
+    K1_CASE(0) K1_CASE(1)
 #undef K1_CASE
     default: return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "rank too large");
   }
