@@ -395,7 +395,7 @@ def summarize_configs(trace_dir, sweep_jsonl, out_path, command):
              "K3: codes + scales/zeros + x + y bytes).", "",
              "K2's fraction is of its own instruction's peak (fp6 for INT4 codes, fp4 for MXFP4: 10.1 "
              "POP/s each), with the int8 peak (5.0 POP/s) of the metric beside the rate; K1 and K3 are "
-             "against 8 TB/s.", "",
+             "against 8 TB/s.  A layer row gives 2MNK over the sum of its K1 and K2 medians.", "",
              "| configuration | kernel | median us | p10 us | p90 us | rate | fraction of peak |",
              "|---|---|---:|---:|---:|---:|---:|"]
     si = 0
@@ -404,6 +404,7 @@ def summarize_configs(trace_dir, sweep_jsonl, out_path, command):
             kinds = [("K3", "k3_awq")]
         else:
             kinds = [("K1", "k1_quantize"), ("K2", "k2_w4a4")]
+        meds = {}
         for label, key in kinds:
             while si < len(series) and key not in series[si][0]:
                 si += 1
@@ -413,6 +414,7 @@ def summarize_configs(trace_dir, sweep_jsonl, out_path, command):
             si += 1
             b2b = np.array(ds[-120:])
             med = float(np.median(b2b))
+            meds[label] = med
             M, N, K = c["M"], c["N"], c["K"]
             if label == "K2":
                 rate = 2.0 * M * N * K / med / 1e6
@@ -429,6 +431,14 @@ def summarize_configs(trace_dir, sweep_jsonl, out_path, command):
                 txt, frac = f"{rate:.0f} GB/s", rate / PEAK_HBM_GBS
             lines.append(f"| {c['config']} ({M}x{K}->{N}) | `{name}` | {med:.2f} | "
                          f"{np.percentile(b2b, 10):.2f} | {np.percentile(b2b, 90):.2f} | {txt} | {frac:.1%} |")
+        if "K1" in meds and "K2" in meds:
+            # the layer: 2MNK over the two kernels' median durations together
+            M, N, K = c["M"], c["N"], c["K"]
+            t = meds["K1"] + meds["K2"]
+            rate = 2.0 * M * N * K / t / 1e6
+            pk = PEAK_FP4_TOPS if c.get("format") == "mxfp4" else PEAK_FP6_TOPS
+            lines.append(f"| {c['config']} ({M}x{K}->{N}) | layer (K1 + K2) | {t:.2f} | | | "
+                         f"{rate:.0f} TOPS ({rate / PEAK_INT8_TOPS:.1%} of int8) | {rate / pk:.1%} |")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))

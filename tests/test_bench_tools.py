@@ -47,8 +47,12 @@ def test_config_summary_series_and_k_split(tmp_path):
         {"config": "small", "M": 1024, "N": 3072, "K": 3072, "rank": 128}]) + "\n")
     out = tmp_path / "summary.md"
     bench.summarize_configs(str(tmp_path / "trace"), str(cfg), str(out), "cmd")
-    rows = [l for l in out.read_text().splitlines() if l.startswith("| big") or l.startswith("| small")]
-    assert len(rows) == 4
+    all_rows = [l for l in out.read_text().splitlines() if l.startswith("| big") or l.startswith("| small")]
+    rows = [l for l in all_rows if "layer (K1 + K2)" not in l]
+    layers = [[c.strip() for c in l.split("|")] for l in all_rows if "layer (K1 + K2)" in l]
+    assert len(rows) == 4 and len(layers) == 2
+    assert layers[0][3] == "110.00"               # big: 10 + 100 us
+    assert layers[1][3] == "56.00"                # small: 11 + 45 us
     cells = [[c.strip() for c in r.split("|")] for r in rows]
     assert cells[1][3] == "100.00"                # big K2
     assert cells[3][3] == "45.00"                 # small K2: GEMM + partial sum, one launch
