@@ -37,6 +37,7 @@ PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 256 CU x 2.4 GHz x 8192 op
 PEAK_HBM_GBS = 8000.0
 PEAK_FP4_TOPS = 10100.0     # MI355X dense FP4 MFMA
 PEAK_FP6_TOPS = 10100.0     # MI355X dense FP6 MFMA (the instruction the INT4 GEMM runs on)
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 
 
 def log(msg):
@@ -224,6 +225,27 @@ def summarize_trace(trace_dir, out_path, title, command, json_path=None, note=""
         js = [ln.strip() for ln in open(json_path) if ln.startswith("{")]
         if js:
             lines += ["The run's own output:", "", "```"] + js + ["```"]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_mfma(jsonl, out_path, command):
+    """CPU only: the --mfma-peak lines as a table (rate against the published
+    dense peak of each instruction)."""
+    rows = [json.loads(l) for l in open(jsonl) if l.startswith("{")]
+    lines = ["# Achievable matrix-instruction rates (registers only)", "",
+             "svdq_measure_mfma: 512 workgroups of 256 threads (two per CU, two wavefronts per SIMD), every "
+             "wavefront four independent accumulation chains of `iters` instructions of one kind; one launch "
+             "timed with events after three warm-up launches, median of five.  Rate = instructions x "
+             "operations per instruction / time.  The shader clock read after a launch this short is not "
+             "reliable, so no cycle count is derived from it.", "",
+             "Command:", "", "```", command, "```", "",
+             "| instruction | ms per launch | rate (T ops/s) | published dense peak | fraction |",
+             "|---|---:|---:|---:|---:|"]
+    for r in rows:
+        lines.append(f"| {r['mfma']} | {r['ms']:.3f} | {r['rate_tops']:.0f} | {r['peak_tops']:.0f} | "
+                     f"{r['frac_of_peak']:.1%} |")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -929,6 +951,45 @@ def branch_ablation_mode(args):
     print(json.dumps({"study": "branch_fusion", "layers": res}), flush=True)
 
 
+def mfma_peak(args):
+    """Achievable issue rate of each matrix instruction the path uses, in
+    registers (svdq_measure_mfma): 512 workgroups (two per CU, so two
+    wavefronts per SIMD), each wavefront four independent chains; the
+    launch is timed with events after a warm-up, median of 5.  One JSON line
+    per instruction: the rate, its published dense peak, and the time one
+    SIMD spends per instruction (the shader clock read after a launch this
+    short is not reliable, so no cycle count is derived)."""
+    import numpy as np
+    import torch
+    import w4a4_rank_corrected_smooth_amd as S
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    S.device_check()
+    stream = torch.cuda.current_stream(dev)
+    grid, iters = 512, 60000
+    sink = torch.zeros(grid, dtype=torch.int32, device=dev)
+    peaks = {0: PEAK_FP6_TOPS, 1: PEAK_FP4_TOPS, 2: PEAK_BF16_TFLOPS, 3: PEAK_BF16_TFLOPS, 4: PEAK_INT8_TOPS}
+    for kind, (label, ops) in S.MFMA_KINDS.items():
+        for _ in range(3):
+            S.measure_mfma(kind, iters, grid, sink)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            S.measure_mfma(kind, iters, grid, sink)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        t = float(np.median(ts))
+        n_instr = grid * 4 * 4 * iters
+        rate = n_instr * ops / t / 1e12
+        out = {"mfma": label, "grid": grid, "iters": iters, "ms": round(t * 1e3, 3),
+               "rate_tops": round(rate, 1), "peak_tops": peaks[kind], "frac_of_peak": round(rate / peaks[kind], 4),
+               "ns_per_instruction_per_simd": round(t * 1e9 * 1024 / n_instr, 2)}
+        print(json.dumps(out), flush=True)
+
+
 def hbm_floor(args):
     """The practical HBM rate at the bandwidth-bound kernels' own sizes and
     grids: a plain streaming read (and copy) of the quantiser's input (4608 x
@@ -996,10 +1057,14 @@ def main():
                     help="CPU only: the oracle's forward timed per configuration (all threads; 1 thread for tiny and low-res)")
     ap.add_argument("--branch-ablation", action="store_true",
                     help="fused against unfused low-rank branch at QKV, fc1, fc2 and low-res (one JSON line)")
+    ap.add_argument("--mfma-peak", action="store_true",
+                    help="achievable issue rate of each matrix instruction the path uses (registers only)")
     ap.add_argument("--hbm-floor", action="store_true",
                     help="streaming read/copy rates at the quantiser's and W4A16 kernel's sizes and grids")
     ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "OUT_NAME", "TITLE", "COMMAND"),
                     help="CPU only: summarise a rocprofv3 trace (TRACE_DIR may be '-') into profiles/OUT_NAME")
+    ap.add_argument("--summarize-mfma", metavar="JSONL",
+                    help="CPU only: the --mfma-peak output as profiles/mfma_peak.md")
     ap.add_argument("--summarize-floor", nargs=2, metavar=("TRACE_DIR", "JSONL"),
                     help="CPU only: summarise a rocprofv3 trace of --hbm-floor into profiles/hbm_floor.md")
     ap.add_argument("--json", default=None, help="with --summarize-trace: the traced run's stdout")
@@ -1007,6 +1072,10 @@ def main():
     ap.add_argument("--summarize-configs", nargs=2, metavar=("TRACE_DIR", "SWEEP_JSONL"),
                     help="CPU only: summarise a rocprofv3 trace of --configs into profiles/ and exit")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, os.path.join(ROOT, "profiles", "mfma_peak.md"),
+                       "python3 bench.py --mfma-peak")
+        return
     if args.summarize_floor:
         t, j = args.summarize_floor
         summarize_floor(t, j, os.path.join(ROOT, "profiles", "hbm_floor.md"),
@@ -1058,6 +1127,9 @@ def main():
         return
     if args.hbm_floor:
         hbm_floor(args)
+        return
+    if args.mfma_peak:
+        mfma_peak(args)
         return
     if args.branch_ablation:
         branch_ablation_mode(args)

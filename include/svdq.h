@@ -424,6 +424,18 @@ svdq_status_t awq_w4a16_forward(const void *blob, int N, int K, const void *x_fp
 svdq_status_t svdq_measure_stream(const void *src, void *dst, size_t bytes, int grid, int mode,
                                   uint32_t *sink, void *hip_stream);
 
+/* Not part of the layer: the issue rate of the matrix instructions the path
+ * uses, operands in registers.  Launches `grid` workgroups of 256 threads;
+ * every wavefront runs four independent chains of `iters` instructions of
+ * one kind: 0 fp6 32x32x64 block-scaled (K2's group sums), 1 fp4 32x32x64
+ * (the MXFP4 form), 2 bf16 32x32x16, 3 bf16 32x32x8 (K2's scale product),
+ * 4 int8 32x32x32.  Each workgroup writes one word to device `sink` [grid]
+ * (so no work is optimised away).  The caller times the launch:
+ * instructions = grid * 4 wavefronts * 4 chains * iters.  Errors:
+ * SVDQ_ERR_INVALID_ARGUMENT (kind, NULL sink), SVDQ_ERR_UNSUPPORTED_SHAPE
+ * (iters outside 1..2^24, grid outside 1..2^20).  Asynchronous. */
+svdq_status_t svdq_measure_mfma(int kind, int iters, int grid, uint32_t *sink, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

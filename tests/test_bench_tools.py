@@ -102,3 +102,14 @@ def test_counter_summary_of_waits_and_lds(tmp_path):
     cells = [c.strip() for c in rows[0].split("|")]
     assert cells[3] == "3.0" and cells[4] == "1000"
     assert cells[-6:-1] == ["25%", "50%", "20%", "1.0%", "0.050"]
+
+
+def test_mfma_summary(tmp_path):
+    j = tmp_path / "m.jsonl"
+    j.write_text(json.dumps({"mfma": "fp6 32x32x64", "grid": 512, "iters": 10, "ms": 7.0, "rate_tops": 9065.8,
+                             "peak_tops": 10100.0, "frac_of_peak": 0.8976, "sclk_mhz": None,
+                             "simd_cycles_per_instruction": None}) + "\n")
+    out = tmp_path / "p.md"
+    bench.summarize_mfma(str(j), str(out), "cmd")
+    row = [l for l in out.read_text().splitlines() if l.startswith("| fp6")][0]
+    assert [c.strip() for c in row.split("|")][2:6] == ["7.000", "9066", "10100", "89.8%"]

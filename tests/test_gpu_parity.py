@@ -250,3 +250,15 @@ def test_k_split_gemm(S, M, N, K, rank, out, gelu):
     err1 = np.max(np.abs(Y1 - Yref)) / np.max(np.abs(f["Y"]))
     assert err1 <= (1.13 * TOL_F32 + 2.0 ** -8 if gelu else tol)
     assert np.max(np.abs(Y1 - Y)) / np.max(np.abs(f["Y"])) <= 2 * tol
+
+
+def test_matrix_probe_runs_and_is_deterministic(S):
+    """The matrix-instruction probe behind the achievable-peak figures (not
+    part of the layer): every kind runs, and two runs fold to the same words."""
+    sink = torch.zeros(8, dtype=torch.int32, device="cuda")
+    for kind in S.MFMA_KINDS:
+        S.measure_mfma(kind, 16, 8, sink)
+        a = sink.clone()
+        S.measure_mfma(kind, 16, 8, sink)
+        torch.cuda.synchronize()
+        assert torch.equal(a, sink), S.MFMA_KINDS[kind][0]

@@ -471,6 +471,14 @@ def test_forward_validation_errors():
     assert lib.svdq_debug_group_sums_codes(ctypes.byref(w), None, 64, 0, 8, 0, 8, FAKE, FAKE, ws,
                                            None) == INV
     assert lib.svdq_gelu_tanh_bf16(FAKE + 2, FAKE, 16, None) == INV
+    # measurement probes: argument checks come before any device work
+    assert lib.svdq_measure_mfma(5, 10, 8, FAKE, None) == INV
+    assert lib.svdq_measure_mfma(0, 10, 8, None, None) == INV
+    assert lib.svdq_measure_mfma(0, 0, 8, FAKE, None) == SHAPE
+    assert lib.svdq_measure_mfma(0, 10, 0, FAKE, None) == SHAPE
+    assert lib.svdq_measure_stream(FAKE, None, 4096, 8, 0, None, None) == INV     # a read needs a sink
+    assert lib.svdq_measure_stream(FAKE, FAKE, 4100, 8, 1, None, None) == INV     # 16-byte multiples
+    assert lib.svdq_measure_stream(FAKE, FAKE, 4096, 0, 1, None, None) == SHAPE
     assert S._lib.svdq_workspace_bytes(0, 128, 128, 4) == 0
     assert S._lib.svdq_device_weights_bytes(128, 100, 4) == 0
 

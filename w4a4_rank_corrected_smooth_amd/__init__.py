@@ -49,7 +49,7 @@ EXPORTS = [
     "svdq_mx_host_weights_sizes", "svdq_mx_prepare_weights", "svdq_mx_device_weights_bytes",
     "svdq_mx_pack_device_weights", "svdq_mx_workspace_bytes", "svdq_mx_linear_forward",
     "svdq_mx_linear_quantize", "svdq_mx_linear_gemm", "svdq_mx_quantize_activations",
-    "svdq_merge_lora", "svdq_mx_merge_lora", "svdq_measure_stream",
+    "svdq_merge_lora", "svdq_mx_merge_lora", "svdq_measure_stream", "svdq_measure_mfma",
 ]
 
 
@@ -118,6 +118,7 @@ _sig("svdq_mx_linear_quantize", _i, [_W, _vp, _i, _vp, _sz, _vp])
 _sig("svdq_mx_linear_gemm", _i, [_W, _i, _vp, _i, _i, _vp, _sz, _vp])
 _sig("svdq_mx_quantize_activations", _i, [_W, _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp])
 _sig("svdq_measure_stream", _i, [_vp, _vp, _sz, _i, _i, _vp, _vp])
+_sig("svdq_measure_mfma", _i, [_i, _i, _i, _vp, _vp])
 _sig("svdq_merge_lora", _i, [ctypes.POINTER(HostWeights), _vp, _vp, _i, ctypes.c_float,
                              ctypes.POINTER(HostWeights)])
 _sig("svdq_mx_merge_lora", _i, [ctypes.POINTER(MxHostWeights), _vp, _vp, _i, ctypes.c_float,
@@ -668,6 +669,20 @@ def awq_forward(layer: AwqLinear, x: torch.Tensor, bias: Optional[torch.Tensor] 
 
 
 # ------------------------------------------------------------ measurement
+MFMA_KINDS = {0: ("fp6 32x32x64", 2 * 32 * 32 * 64), 1: ("fp4 32x32x64", 2 * 32 * 32 * 64),
+              2: ("bf16 32x32x16", 2 * 32 * 32 * 16), 3: ("bf16 32x32x8", 2 * 32 * 32 * 8),
+              4: ("int8 32x32x32", 2 * 32 * 32 * 32)}
+
+
+def measure_mfma(kind: int, iters: int, grid: int, sink: torch.Tensor) -> None:
+    """svdq_measure_mfma: `grid` workgroups, each wavefront four chains of
+    `iters` matrix instructions of `kind` (MFMA_KINDS); the caller times it."""
+    if sink.dtype != torch.int32 or sink.numel() < grid or sink.device.type != "cuda":
+        raise ValueError("sink must be an int32 device tensor of at least `grid` elements")
+    _check(_lib.svdq_measure_mfma(kind, iters, grid, sink.data_ptr(), _stream(sink.device)),
+           "svdq_measure_mfma")
+
+
 def measure_stream(src: torch.Tensor, grid: int, dst: Optional[torch.Tensor] = None,
                    sink: Optional[torch.Tensor] = None) -> None:
     """svdq_measure_stream: a plain streaming read of `src` (dst None) or

@@ -1464,6 +1464,69 @@ __global__ __launch_bounds__(256) void gelu_tanh_bf16_kernel(const uint16_t *__r
 }
 
 // ============================================================ measurement
+// Issue rate of the matrix instructions the path uses, operands in
+// registers: every wavefront runs four independent accumulation chains of
+// `iters` instructions of one kind (its operands made opaque to the compiler
+// each iteration, so nothing is hoisted or folded) and the workgroup folds
+// its result into one word of `sink`.  Kinds: 0 fp6 32x32x64 (block-scaled,
+// unit scales: K2's group sums), 1 fp4 32x32x64 (the MXFP4 form), 2 bf16
+// 32x32x16, 3 bf16 32x32x8 (K2's scale product), 4 int8 32x32x32.  The host
+// times the launch; two workgroups per CU put two wavefronts on every SIMD.
+typedef int v4i_m __attribute__((ext_vector_type(4)));
+typedef int v16i_m __attribute__((ext_vector_type(16)));
+template <int KIND>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_probe_kernel(int iters,
+                                                                                            uint32_t *sink) {
+  const int lane = threadIdx.x & 63;
+  v16f acc[4];
+  v16i_m iacc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) { acc[c] = v16f{}; iacc[c] = v16i_m{}; }
+  v8i f8;
+  v8bf b16;
+  v4s b8;
+  v4i_m i8;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    f8[r] = (lane * 7 + r) & 0x0F0F0F0F;                 // small fp6 / fp4 codes
+    b16[r] = (__bf16)(0.001f * (float)(r + lane));
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    b8[r] = (short)(0x3c00 + r + lane);
+    i8[r] = (lane + r) & 0x07070707;
+  }
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (KIND <= 1) asm volatile("" : "+v"(f8));
+    if constexpr (KIND == 2) asm volatile("" : "+v"(b16));
+    if constexpr (KIND == 3) asm volatile("" : "+v"(b8));
+    if constexpr (KIND == 4) asm volatile("" : "+v"(i8));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if constexpr (KIND == 0)
+        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f8, f8, acc[c], 2, 2, 0, 127, 0, 127);
+      if constexpr (KIND == 1)
+        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f8, f8, acc[c], 4, 4, 0, 127, 0, 127);
+      if constexpr (KIND == 2) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b16, b16, acc[c], 0, 0, 0);
+      if constexpr (KIND == 3) acc[c] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(b8, b8, acc[c], 0, 0, 0);
+      if constexpr (KIND == 4) iacc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(i8, i8, iacc[c], 0, 0, 0);
+    }
+  }
+  uint32_t v = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v += __float_as_uint(acc[c][e]) + (uint32_t)iacc[c][e];
+  __shared__ uint32_t fold[256];
+  fold[threadIdx.x] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int i = 0; i < 256; ++i) t += fold[i];
+    sink[blockIdx.x] = t;
+  }
+}
+
 // Plain streaming read (mode 0: every 16-byte word loaded once, 16 loads in
 // flight per lane, folded into one word per workgroup so nothing is
 // optimised away) or copy (mode 1) of `bytes` with a caller-chosen grid:
@@ -2291,6 +2354,25 @@ svdq_status_t svdq_measure_stream(const void *src, void *dst, size_t bytes, int 
   hipLaunchKernelGGL(stream_probe_kernel, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(hip_stream),
                      static_cast<const v4u *>(src), static_cast<v4u *>(dst), (int64_t)(bytes / 16), mode, sink);
   return launch_status("stream probe launch");
+}
+
+svdq_status_t svdq_measure_mfma(int kind, int iters, int grid, uint32_t *sink, void *hip_stream) {
+  if (!sink) return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_measure_mfma: NULL sink");
+  if (kind < 0 || kind > 4) return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_measure_mfma: kind %d", kind);
+  if (iters < 1 || iters > (1 << 24) || grid < 1 || grid > (1 << 20))
+    return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "svdq_measure_mfma: iters %d grid %d", iters, grid);
+  svdq_status_t st = check_device();
+  if (st != SVDQ_OK) return st;
+  const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const dim3 g((unsigned)grid), b(256);
+  switch (kind) {
+    case 0: hipLaunchKernelGGL(mfma_probe_kernel<0>, g, b, 0, stream, iters, sink); break;
+    case 1: hipLaunchKernelGGL(mfma_probe_kernel<1>, g, b, 0, stream, iters, sink); break;
+    case 2: hipLaunchKernelGGL(mfma_probe_kernel<2>, g, b, 0, stream, iters, sink); break;
+    case 3: hipLaunchKernelGGL(mfma_probe_kernel<3>, g, b, 0, stream, iters, sink); break;
+    default: hipLaunchKernelGGL(mfma_probe_kernel<4>, g, b, 0, stream, iters, sink); break;
+  }
+  return launch_status("matrix probe launch");
 }
 
 svdq_status_t awq_w4a16_forward(const void *blob, int N, int K, const void *x, int M,
