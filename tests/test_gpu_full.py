@@ -200,12 +200,15 @@ def test_awq_full(S, awq, M):
 
 @pytest.mark.parametrize("M,N,K", [(5, 100, 192), (16, 250, 1600), (4, 100, 1600), (9, 48, 768),
                                    (7, 17, 832), (1, 33, 64), (12, 4100, 3072), (10, 40, 64),
-                                   (13, 272, 4160), (8, 64, 3200), (16, 96, 12288)])
+                                   (13, 272, 4160), (8, 64, 3200), (16, 96, 12288), (11, 16, 128),
+                                   (14, 9, 640), (16, 33, 3072)])
 def test_awq_ragged_with_bias(S, M, N, K):
-    """Both chunk sizes of the AWQ kernel (12 groups up to 8 rows, 4 groups
-    from 9): ragged column tiles, spare wavefronts, odd group counts, one
-    chunk, several chunks, a last chunk past a wavefront's groups, a
-    wavefront with no groups of its own."""
+    """Both shapes of the AWQ kernel (one tile and chunks of 12 groups up to
+    8 rows; two tiles per workgroup and chunks of 4 groups from 9): ragged
+    column tiles, an odd tile count (the last workgroup's second tile past
+    the end), a single tile, spare wavefronts, odd group counts, one chunk,
+    several chunks, a last chunk past a wavefront's groups, a wavefront with
+    no groups of its own."""
     announce(f"awq ragged M={M} N={N} K={K}")
     a = synth.awq_case(m_max=M, N=N, K=K, seed=44 + M)
     q, s, z = OA.quantize(a.W)

@@ -1123,26 +1123,29 @@ __global__ __launch_bounds__(256) void k2_split_sum(const float *__restrict__ pa
 }
 
 // ======================================================================= K3
-// AWQ W4A16.  A workgroup of 4 wavefronts owns a tile of 16 output channels;
-// wavefront w takes a contiguous quarter of the groups of 64 input channels
-// (rounded up to a multiple of 4, so its range starts on a pair of code
-// blocks and on a 16-byte quad of scale words), CH groups at a time.
+// AWQ W4A16.  A workgroup of 4 wavefronts owns T tiles of 16 output
+// channels (T = 1 up to kAwqLongChunkRows rows, 2 above); wavefront w takes
+// a contiguous quarter of the groups of 64 input channels (rounded up to a
+// multiple of 4, so its range starts on a pair of code blocks and on a
+// 16-byte quad of scale words), CH groups at a time.
 // Per chunk it first copies the chunk's activations (M rows, a few kilobytes
 // shared by every workgroup, so cache hits) into its own LDS with the
-// global->LDS path, then issues its code loads (16 bytes per lane: two
-// groups) and scale loads (16 bytes: four groups), the HBM stream, and waits
-// only for the copies; each group's compute then waits for its own loads
-// alone, in issue order.  Every load is unconditional (indices clamped;
-// groups past the range weigh 0, and every value they touch is finite: the
-// copies fill whole rows of CH groups, repeating the last group of
-// the range, and the blob's padding words are zero), so the completion
-// counts are exact.  For each group, lane l (channel l % 16, quarter
-// q = l / 16) turns its 16 codes into fp16 (q - z) with the 1024-offset
-// trick (0x6400 | code is the fp16 value 1024 + code; subtracting 1024 + z
-// is exact), the activations [16, 64] read from LDS are the A operand, and
-// two v_mfma_f32_16x16x32_f16 give the group's inner sums; acc += s * sum in
-// fp32.  Rows m >= M repeat row M - 1 and are never stored.  The four
-// partial sums meet in LDS, in a fixed order.
+// global->LDS path, then issues its scale loads (16 bytes per lane: four
+// groups) and code loads (16 bytes: two groups), per tile, the HBM stream,
+// and waits only for the copies; each group's compute then waits for its own
+// loads alone, in issue order.  Every load is unconditional (indices
+// clamped; groups past the range weigh 0, tiles past the last are computed
+// and never stored, and every value they touch is finite: the copies fill
+// whole rows of CH groups, repeating the last group of the range, and the
+// blob's padding words are zero), so the completion counts are exact.  For
+// each group, lane l (channel l % 16, quarter q = l / 16) turns its 16 codes
+// into fp16 (q - z) with the 1024-offset trick (0x6400 | code is the fp16
+// value 1024 + code; subtracting 1024 + z is exact), the activations
+// [16, 64] read once from LDS are the A operand of every tile, and two
+// v_mfma_f32_16x16x32_f16 per tile give the group's inner sums;
+// acc += s * sum in fp32.  Rows m >= M repeat row M - 1 and are never
+// stored.  The four partial sums of a tile meet in LDS, in a fixed order, so
+// a tile's result does not depend on T.
 // Groups per chunk: a wavefront copies M rows x CH groups of activations
 // into its own LDS.  Up to kAwqLongChunkRows rows the whole quarter of K
 // (12 groups at K = 3072) goes in one chunk; with more rows a wavefront's
@@ -1154,9 +1157,21 @@ __global__ __launch_bounds__(256) void k2_split_sum(const float *__restrict__ pa
 // wavefronts shared one copy took 17.0 / 17.9 us at M = 12 / 16, and loading
 // the activations straight into registers with every other load up front
 // (no LDS) 10.6 / 19.5 us at M = 1 / 16.
+// Tiles per workgroup: above 8 rows the activation copies (16 rows x 4
+// groups x 128 bytes per wavefront and chunk, every workgroup on the CU
+// repeating them) cost more than the code stream's latency gains from a big
+// grid, so a workgroup takes two tiles and copies once for both: M = 12 / 13
+// / 16 take 12.4 / 12.7 / 13.1 us against 13.1 / 14.7 / 15.1 us with one.
+// At 1 to 8 rows two tiles lose (9.6 against 8.5 us at M = 1: half the
+// workgroups, 2.25 per CU), and so do four or eight tiles above 8 rows
+// (15.2 / 17.6 us at M = 16).  Padding the LDS rows against bank conflicts,
+// the reduction buffer inside the copy area, and the next chunk's code loads
+// issued before the current chunk's compute (or before its copies) all lost
+// or changed nothing.
 constexpr int kAwqChunk = 12;
 constexpr int kAwqShortChunk = 4;
 constexpr int kAwqLongChunkRows = 8;
+constexpr int kAwqWideTiles = 2;
 
 // One group of 64 input channels for a wavefront's 16 x 16 output block:
 // xg points at the lane's activations in LDS (row lane % 16, channels
@@ -1196,7 +1211,7 @@ __device__ __forceinline__ void awq_group(const uint16_t *xg, uint32_t w0, uint3
   awq_group_regs(*reinterpret_cast<const uint4 *>(xg), *reinterpret_cast<const uint4 *>(xg + 8), w0, w1, szv,
                  valid, acc);
 }
-template <int CH>
+template <int CH, int T>
 __global__ __launch_bounds__(256) void k3_awq_w4a16(const uint8_t *__restrict__ qd,
                                                      const uint32_t *__restrict__ sz,
                                                      const uint16_t *__restrict__ x, int M,
@@ -1204,16 +1219,27 @@ __global__ __launch_bounds__(256) void k3_awq_w4a16(const uint8_t *__restrict__ 
                                                      const uint16_t *__restrict__ bias,
                                                      uint16_t *__restrict__ y) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int tile = blockIdx.x;
+  const int ntiles = (N + kAwqTile - 1) / kAwqTile;
+  const int tile0 = blockIdx.x * T;
   const int G = K / kGroup;
   const int G4 = (G + 3) & ~3;
   const int Gq = ((G + 3) / 4 + 3) & ~3;
   const int g0 = min(G, w * Gq), g1 = min(G, g0 + Gq);
   const int m = lane & 15, qtr = lane >> 4;
-  const int n = tile * kAwqTile + (lane & 15);
-  const uint8_t *qbase = qd + (int64_t)tile * ((G + 1) / 2) * kAwqBlockBytes + lane * 16;
+  // the lane's code bytes and scale words in each tile (tiles past the last
+  // read the last one)
+  const uint8_t *qbase[T];
+  const uint32_t *sbase[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int tl = min(tile0 + t, ntiles - 1);
+    qbase[t] = qd + (int64_t)tl * ((G + 1) / 2) * kAwqBlockBytes + lane * 16;
+    sbase[t] = sz + (int64_t)(tl * kAwqTile + (lane & 15)) * G4;
+  }
   extern __shared__ __attribute__((aligned(16))) uint8_t awq_lds[];
-  v4f acc = v4f{};
+  v4f acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = v4f{};
   // this wavefront's copy of the chunk's activations: rows 0..M-1 of
   // CH groups each, one 16-byte piece per lane and copy
   constexpr int npr = CH * (kGroup / 8);         // pieces per row
@@ -1226,7 +1252,7 @@ __global__ __launch_bounds__(256) void k3_awq_w4a16(const uint8_t *__restrict__ 
   for (int gc = g0; gc < g1; gc += CH) {
     // activations first (cache hits), then the code and scale stream; every
     // load after the copies is unconditional, so the copies are complete
-    // once at most CH / 2 + CH / 4 loads remain
+    // once at most T (CH / 2 + CH / 4) loads remain
     for (int c0 = 0; c0 < npc; c0 += 64) {
       const int pc = min(c0 + lane, npc - 1);
       const int mr = pc / npr, o = pc - mr * npr;
@@ -1238,45 +1264,54 @@ __global__ __launch_bounds__(256) void k3_awq_w4a16(const uint8_t *__restrict__ 
     // asm placed after the copies, so the compiler cannot hoist them above.
     int zero = 0;
     asm volatile("" : "+s"(zero));
-    const uint8_t *qb = qbase + zero;
-    const uint32_t *szb = sz + (int64_t)n * G4 + zero;
-    uint4 cw[CH / 2];
-    uint4 szw[CH / 4];
-#pragma unroll
-    for (int j = 0; j < CH / 2; ++j) {
-      const int pr = min(gc / 2 + j, (g1 - 1) / 2);
-      cw[j] = *reinterpret_cast<const uint4 *>(qb + (int64_t)pr * kAwqBlockBytes);
-    }
+    uint4 szw[CH / 4][T];
+    uint4 cw[CH / 2][T];
 #pragma unroll
     for (int j = 0; j < CH / 4; ++j) {
       const int qd4 = min(gc / 4 + j, (g1 - 1) / 4);
-      szw[j] = *reinterpret_cast<const uint4 *>(szb + 4 * qd4);
+#pragma unroll
+      for (int t = 0; t < T; ++t) szw[j][t] = *reinterpret_cast<const uint4 *>(sbase[t] + zero + 4 * qd4);
     }
-    vmcnt_wait<CH / 2 + CH / 4>();
+#pragma unroll
+    for (int j = 0; j < CH / 2; ++j) {
+      const int pr = min(gc / 2 + j, (g1 - 1) / 2);
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        cw[j][t] = *reinterpret_cast<const uint4 *>(qbase[t] + zero + (int64_t)pr * kAwqBlockBytes);
+    }
+    vmcnt_wait<T * (CH / 2 + CH / 4)>();
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const uint4 q4 = szw[i / 4];
-      const uint32_t szv = (i % 4 == 0) ? q4.x : (i % 4 == 1) ? q4.y : (i % 4 == 2) ? q4.z : q4.w;
-      const uint4 c = cw[i / 2];
-      // groups past the wavefront's range weigh 0, so every load above is
-      // used and none is moved below the wait
-      awq_group(xm + i * kGroup, i % 2 == 0 ? c.x : c.z, i % 2 == 0 ? c.y : c.w, szv, gc + i < g1, acc);
+      const uint4 xa0 = *reinterpret_cast<const uint4 *>(xm + i * kGroup);
+      const uint4 xa1 = *reinterpret_cast<const uint4 *>(xm + i * kGroup + 8);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const uint4 q4 = szw[i / 4][t];
+        const uint32_t szv = (i % 4 == 0) ? q4.x : (i % 4 == 1) ? q4.y : (i % 4 == 2) ? q4.z : q4.w;
+        const uint4 c = cw[i / 2][t];
+        // groups past the wavefront's range weigh 0, so every load above is
+        // used and none is moved below the wait
+        awq_group_regs(xa0, xa1, i % 2 == 0 ? c.x : c.z, i % 2 == 0 ? c.y : c.w, szv, gc + i < g1, acc[t]);
+      }
     }
   }
-  __shared__ v4f red[4][64];
-  red[w][lane] = acc;
-  __syncthreads();
-  if (w != 0) return;
-  const v4f r0 = red[0][lane], r1 = red[1][lane], r2 = red[2][lane], r3 = red[3][lane];
-  const int col = tile * kAwqTile + (lane & 15);
-  if (col < N) {
-    const float b = bias ? (float)__builtin_bit_cast(_Float16, bias[col]) : 0.0f;
+  __shared__ v4f red[4][T][64];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 4 * (lane >> 4) + e;
-      if (row < M) {
-        const float v = ((r0[e] + r1[e]) + (r2[e] + r3[e])) + b;
-        y[(int64_t)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
+  for (int t = 0; t < T; ++t) red[w][t][lane] = acc[t];
+  __syncthreads();
+  // wavefront w stores tiles w, w + 4, ...
+  for (int t = w; t < T; t += 4) {
+    const v4f r0 = red[0][t][lane], r1 = red[1][t][lane], r2 = red[2][t][lane], r3 = red[3][t][lane];
+    const int col = (tile0 + t) * kAwqTile + (lane & 15);
+    if (tile0 + t < ntiles && col < N) {
+      const float b = bias ? (float)__builtin_bit_cast(_Float16, bias[col]) : 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 4 * (lane >> 4) + e;
+        if (row < M) {
+          const float v = ((r0[e] + r1[e]) + (r2[e] + r3[e])) + b;
+          y[(int64_t)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
+        }
       }
     }
   }
@@ -2386,14 +2421,18 @@ svdq_status_t awq_w4a16_forward(const void *blob, int N, int K, const void *x, i
   if (st != SVDQ_OK) return st;
   const AwqLayout L(N, K);
   const uint8_t *b = static_cast<const uint8_t *>(blob);
-  const int ch = M <= kAwqLongChunkRows ? kAwqChunk : kAwqShortChunk;
+  const bool wide = M > kAwqLongChunkRows;
+  const int ch = wide ? kAwqShortChunk : kAwqChunk;
+  const int T = wide ? kAwqWideTiles : 1;
   // per wavefront: M rows of a chunk, in whole 1 KB copies
   const size_t lds = (size_t)4 * ((M * ch * (kGroup / 8) + 63) / 64 * 1024);
-#define K3_GO(C) hipLaunchKernelGGL((k3_awq_w4a16<C>), dim3((unsigned)(L.Np / kAwqTile)), dim3(256), lds, \
-                                    static_cast<hipStream_t>(hip_stream), b + L.q,                      \
-                                    reinterpret_cast<const uint32_t *>(b + L.sz), static_cast<const uint16_t *>(x), \
-                                    M, N, K, static_cast<const uint16_t *>(bias), static_cast<uint16_t *>(y))
-  if (ch == kAwqChunk) K3_GO(kAwqChunk); else K3_GO(kAwqShortChunk);
+  const unsigned grid = (unsigned)((L.Np / kAwqTile + T - 1) / T);
+#define K3_GO(C, TT) hipLaunchKernelGGL((k3_awq_w4a16<C, TT>), dim3(grid), dim3(256), lds,                \
+                                        static_cast<hipStream_t>(hip_stream), b + L.q,                  \
+                                        reinterpret_cast<const uint32_t *>(b + L.sz),                  \
+                                        static_cast<const uint16_t *>(x), M, N, K,                     \
+                                        static_cast<const uint16_t *>(bias), static_cast<uint16_t *>(y))
+  if (wide) K3_GO(kAwqShortChunk, kAwqWideTiles); else K3_GO(kAwqChunk, 1);
 #undef K3_GO
   return launch_status("AWQ kernel launch");
 }
