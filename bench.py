@@ -100,11 +100,14 @@ def _read_csv(path):
 
 
 def _find(d, suffix):
-    for root, _, files in os.walk(d):
-        for f in files:
-            if f.endswith(suffix):
-                return os.path.join(root, f)
-    raise FileNotFoundError(f"no *{suffix} under {d}")
+    """The one *suffix file under d; a directory holding the output of more
+    than one profiler run is refused, so runs are never mixed."""
+    hits = sorted(os.path.join(root, f) for root, _, files in os.walk(d) for f in files if f.endswith(suffix))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    if len(hits) > 1:
+        raise RuntimeError(f"{len(hits)} *{suffix} files under {d} (output of several runs): {hits}")
+    return hits[0]
 
 
 def _short(name):

@@ -113,3 +113,17 @@ def test_mfma_summary(tmp_path):
     bench.summarize_mfma(str(j), str(out), "cmd")
     row = [l for l in out.read_text().splitlines() if l.startswith("| fp6")][0]
     assert [c.strip() for c in row.split("|")][2:6] == ["7.000", "9066", "10100", "89.8%"]
+
+
+def test_summaries_refuse_mixed_runs(tmp_path):
+    """A profile directory holding two runs' CSV files is refused rather than
+    summarised from whichever file the walk meets first."""
+    d = tmp_path / "trace" / "vm"
+    write_trace(str(d), [("k2_w4a4_gemm<0>", 10.0)])
+    assert bench._find(str(tmp_path / "trace"), "kernel_trace.csv").endswith("1_kernel_trace.csv")
+    with open(d / "2_kernel_trace.csv", "w") as f:
+        f.write("Kernel_Name,Start_Timestamp,End_Timestamp\n")
+    with pytest.raises(RuntimeError, match="several runs"):
+        bench._find(str(tmp_path / "trace"), "kernel_trace.csv")
+    with pytest.raises(FileNotFoundError):
+        bench._find(str(tmp_path / "trace"), "kernel_stats.csv")
