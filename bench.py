@@ -236,7 +236,9 @@ def summarize_trace(trace_dir, out_path, title, command, json_path=None, note=""
 def summarize_mfma(jsonl, out_path, command):
     """CPU only: the --mfma-peak lines as a table (rate against the published
     dense peak of each instruction)."""
-    rows = [json.loads(l) for l in open(jsonl) if l.startswith("{")]
+    allrows = [json.loads(l) for l in open(jsonl) if l.startswith("{")]
+    rows = [r for r in allrows if "mfma" in r]
+    mixes = {r["kind"]: r for r in allrows if "mix" in r}
     lines = ["# Achievable matrix-instruction rates (registers only)", "",
              "svdq_measure_mfma: 512 workgroups of 256 threads (two per CU, two wavefronts per SIMD), every "
              "wavefront four independent accumulation chains of `iters` instructions of one kind; one launch "
@@ -249,6 +251,35 @@ def summarize_mfma(jsonl, out_path, command):
     for r in rows:
         lines.append(f"| {r['mfma']} | {r['ms']:.3f} | {r['rate_tops']:.0f} | {r['peak_tops']:.0f} | "
                      f"{r['frac_of_peak']:.1%} |")
+    if mixes:
+        fp6 = [r for r in rows if r["mfma"].startswith("fp6")]
+        lines += ["", "## Instruction mixes", "",
+                  "Same launch shape; one slot per chain and iteration.  Time per slot is what one SIMD spends on "
+                  "it with two wavefronts resident.", "",
+                  "| mix | ms per launch | ns per slot per SIMD |", "|---|---:|---:|"]
+        for k in sorted(mixes):
+            lines.append(f"| {mixes[k]['mix']} | {mixes[k]['ms']:.3f} | {mixes[k]['ns_per_slot_per_simd']:.2f} |")
+        if fp6 and 5 in mixes and 6 in mixes:
+            a, b = fp6[0]["ns_per_instruction_per_simd"], mixes[6]["ns_per_slot_per_simd"]
+            c = mixes[5]["ns_per_slot_per_simd"]
+            lines += ["", f"An fp6 instruction alone takes {a:.2f} ns and 16 FMAs alone {b:.2f} ns; together, on "
+                      f"independent registers, {c:.2f} ns, {c / (a + b):.0%} of their sum: on a SIMD the vector "
+                      "ALU runs beside the matrix core for only a small part of the time, so the GEMM's time per "
+                      "group is close to the sum of its matrix and vector instructions."]
+        x8 = [r for r in rows if r["mfma"].startswith("bf16 32x32x8")]
+        if 7 in mixes and fp6 and x8 and 6 in mixes:
+            parts = (x8[0]["ns_per_instruction_per_simd"] + fp6[0]["ns_per_instruction_per_simd"]
+                     + mixes[6]["ns_per_slot_per_simd"])
+            lines += ["", f"The GEMM's step takes {mixes[7]['ns_per_slot_per_simd']:.2f} ns against {parts:.2f} ns "
+                      f"for its three parts alone ({mixes[7]['ns_per_slot_per_simd'] / parts:.0%})."]
+        if 7 in mixes:
+            g = 8 * mixes[7]["ns_per_slot_per_simd"]
+            # fc2 at 4608 x 3072, K = 12288: 36 x 12 tiles of 128 x 256 on 256 CUs x 2 slots; the busiest
+            # CU holds two workgroups, so each of its SIMDs runs 2 x 192 wavefront-groups
+            lines += ["", f"The GEMM's step for one tile: {mixes[7]['ns_per_slot_per_simd']:.2f} ns; a wavefront's "
+                      f"group (8 tiles) {g:.0f} ns of SIMD time.  At fc2 (4608 x 3072, K = 12288: 432 tiles of "
+                      f"128 x 256, at most two workgroups on a CU, 2 x 192 wavefront-groups per SIMD) that is "
+                      f"{384 * g / 1e3:.0f} us for the main loop alone, with no wait, prologue or epilogue."]
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -961,7 +992,9 @@ def mfma_peak(args):
     launch is timed with events after a warm-up, median of 5.  One JSON line
     per instruction: the rate, its published dense peak, and the time one
     SIMD spends per instruction (the shader clock read after a launch this
-    short is not reliable, so no cycle count is derived)."""
+    short is not reliable, so no cycle count is derived).  Then one line per
+    instruction mix (an fp6 instruction with 16 independent FMAs, the FMAs
+    alone, the GEMM's per-tile step): the time one SIMD spends per slot."""
     import numpy as np
     import torch
     import w4a4_rank_corrected_smooth_amd as S
@@ -972,7 +1005,8 @@ def mfma_peak(args):
     grid, iters = 512, 60000
     sink = torch.zeros(grid, dtype=torch.int32, device=dev)
     peaks = {0: PEAK_FP6_TOPS, 1: PEAK_FP4_TOPS, 2: PEAK_BF16_TFLOPS, 3: PEAK_BF16_TFLOPS, 4: PEAK_INT8_TOPS}
-    for kind, (label, ops) in S.MFMA_KINDS.items():
+
+    def timed(kind):
         for _ in range(3):
             S.measure_mfma(kind, iters, grid, sink)
         torch.cuda.synchronize()
@@ -984,13 +1018,22 @@ def mfma_peak(args):
             e1.record(stream)
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1) * 1e-3)
-        t = float(np.median(ts))
+        return float(np.median(ts))
+
+    for kind, (label, ops) in S.MFMA_KINDS.items():
+        t = timed(kind)
         n_instr = grid * 4 * 4 * iters
         rate = n_instr * ops / t / 1e12
         out = {"mfma": label, "grid": grid, "iters": iters, "ms": round(t * 1e3, 3),
                "rate_tops": round(rate, 1), "peak_tops": peaks[kind], "frac_of_peak": round(rate / peaks[kind], 4),
                "ns_per_instruction_per_simd": round(t * 1e9 * 1024 / n_instr, 2)}
         print(json.dumps(out), flush=True)
+    # instruction mixes: time per slot (one chain step) on one SIMD
+    for kind, label in S.MFMA_MIXES.items():
+        t = timed(kind)
+        n_slots = grid * 4 * 4 * iters
+        print(json.dumps({"mix": label, "kind": kind, "grid": grid, "iters": iters, "ms": round(t * 1e3, 3),
+                          "ns_per_slot_per_simd": round(t * 1e9 * 1024 / n_slots, 2)}), flush=True)
 
 
 def hbm_floor(args):

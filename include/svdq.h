@@ -429,9 +429,12 @@ svdq_status_t svdq_measure_stream(const void *src, void *dst, size_t bytes, int 
  * every wavefront runs four independent chains of `iters` instructions of
  * one kind: 0 fp6 32x32x64 block-scaled (K2's group sums), 1 fp4 32x32x64
  * (the MXFP4 form), 2 bf16 32x32x16, 3 bf16 32x32x8 (K2's scale product),
- * 4 int8 32x32x32.  Each workgroup writes one word to device `sink` [grid]
- * (so no work is optimised away).  The caller times the launch:
- * instructions = grid * 4 wavefronts * 4 chains * iters.  Errors:
+ * 4 int8 32x32x32; or one instruction mix per chain and iteration: 5 an
+ * fp6 32x32x64 plus 16 fp32 FMAs on other registers, 6 the 16 FMAs alone,
+ * 7 the GEMM's step for one 32 x 32 tile (bf16 32x32x8 scale product, fp6
+ * group sum, 16 FMAs).  Each workgroup writes one word to device `sink`
+ * [grid] (so no work is optimised away).  The caller times the launch:
+ * slots = grid * 4 wavefronts * 4 chains * iters.  Errors:
  * SVDQ_ERR_INVALID_ARGUMENT (kind, NULL sink), SVDQ_ERR_UNSUPPORTED_SHAPE
  * (iters outside 1..2^24, grid outside 1..2^20).  Asynchronous. */
 svdq_status_t svdq_measure_mfma(int kind, int iters, int grid, uint32_t *sink, void *hip_stream);

@@ -108,11 +108,29 @@ def test_mfma_summary(tmp_path):
     j = tmp_path / "m.jsonl"
     j.write_text(json.dumps({"mfma": "fp6 32x32x64", "grid": 512, "iters": 10, "ms": 7.0, "rate_tops": 9065.8,
                              "peak_tops": 10100.0, "frac_of_peak": 0.8976, "sclk_mhz": None,
-                             "simd_cycles_per_instruction": None}) + "\n")
+                             "ns_per_instruction_per_simd": 14.1}) + "\n")
     out = tmp_path / "p.md"
     bench.summarize_mfma(str(j), str(out), "cmd")
     row = [l for l in out.read_text().splitlines() if l.startswith("| fp6")][0]
     assert [c.strip() for c in row.split("|")][2:6] == ["7.000", "9066", "10100", "89.8%"]
+    # with the instruction mixes: the overlap ratio and the GEMM step's floor
+    with open(j, "a") as f:
+        f.write("\n" + json.dumps({"mix": "a", "kind": 5, "grid": 512, "iters": 10, "ms": 1.0,
+                                    "ns_per_slot_per_simd": 30.0}))
+        f.write("\n" + json.dumps({"mix": "b", "kind": 6, "grid": 512, "iters": 10, "ms": 1.0,
+                                    "ns_per_slot_per_simd": 20.0}))
+        f.write("\n" + json.dumps({"mix": "c", "kind": 7, "grid": 512, "iters": 10, "ms": 1.0,
+                                    "ns_per_slot_per_simd": 50.0}))
+    bench.summarize_mfma(str(j), str(out), "cmd")
+    text = out.read_text()
+    assert "together, on independent registers, 30.00 ns, 88% of their sum" in text   # 30 / (14.1 + 20)
+    assert "three parts" not in text              # no bf16 32x32x8 row yet
+    with open(j, "a") as f:
+        f.write("\n" + json.dumps({"mfma": "bf16 32x32x8", "grid": 512, "iters": 10, "ms": 1.0, "rate_tops": 1.0,
+                                    "peak_tops": 2500.0, "frac_of_peak": 0.5, "ns_per_instruction_per_simd": 10.9}))
+    bench.summarize_mfma(str(j), str(out), "cmd")
+    assert "takes 50.00 ns against 45.00 ns for its three parts alone (111%)" in out.read_text()
+    assert "a wavefront's group (8 tiles) 400 ns" in text and "that is 154 us" in text
 
 
 def test_summaries_refuse_mixed_runs(tmp_path):

@@ -256,9 +256,9 @@ def test_matrix_probe_runs_and_is_deterministic(S):
     """The matrix-instruction probe behind the achievable-peak figures (not
     part of the layer): every kind runs, and two runs fold to the same words."""
     sink = torch.zeros(8, dtype=torch.int32, device="cuda")
-    for kind in S.MFMA_KINDS:
+    for kind in list(S.MFMA_KINDS) + list(S.MFMA_MIXES):
         S.measure_mfma(kind, 16, 8, sink)
         a = sink.clone()
         S.measure_mfma(kind, 16, 8, sink)
         torch.cuda.synchronize()
-        assert torch.equal(a, sink), S.MFMA_KINDS[kind][0]
+        assert torch.equal(a, sink), kind

@@ -472,7 +472,8 @@ def test_forward_validation_errors():
                                            None) == INV
     assert lib.svdq_gelu_tanh_bf16(FAKE + 2, FAKE, 16, None) == INV
     # measurement probes: argument checks come before any device work
-    assert lib.svdq_measure_mfma(5, 10, 8, FAKE, None) == INV
+    assert lib.svdq_measure_mfma(8, 10, 8, FAKE, None) == INV
+    assert lib.svdq_measure_mfma(-1, 10, 8, FAKE, None) == INV
     assert lib.svdq_measure_mfma(0, 10, 8, None, None) == INV
     assert lib.svdq_measure_mfma(0, 0, 8, FAKE, None) == SHAPE
     assert lib.svdq_measure_mfma(0, 10, 0, FAKE, None) == SHAPE

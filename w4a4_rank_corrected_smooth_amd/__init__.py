@@ -672,11 +672,14 @@ def awq_forward(layer: AwqLinear, x: torch.Tensor, bias: Optional[torch.Tensor] 
 MFMA_KINDS = {0: ("fp6 32x32x64", 2 * 32 * 32 * 64), 1: ("fp4 32x32x64", 2 * 32 * 32 * 64),
               2: ("bf16 32x32x16", 2 * 32 * 32 * 16), 3: ("bf16 32x32x8", 2 * 32 * 32 * 8),
               4: ("int8 32x32x32", 2 * 32 * 32 * 32)}
+# instruction mixes (time per slot, no operation count): kind -> label
+MFMA_MIXES = {5: "fp6 32x32x64 + 16 fp32 FMA", 6: "16 fp32 FMA", 7: "GEMM step: bf16 32x32x8 + fp6 32x32x64 + 16 FMA"}
 
 
 def measure_mfma(kind: int, iters: int, grid: int, sink: torch.Tensor) -> None:
     """svdq_measure_mfma: `grid` workgroups, each wavefront four chains of
-    `iters` matrix instructions of `kind` (MFMA_KINDS); the caller times it."""
+    `iters` matrix instructions of `kind` (MFMA_KINDS) or instruction-mix
+    slots (MFMA_MIXES); the caller times it."""
     if sink.dtype != torch.int32 or sink.numel() < grid or sink.device.type != "cuda":
         raise ValueError("sink must be an int32 device tensor of at least `grid` elements")
     _check(_lib.svdq_measure_mfma(kind, iters, grid, sink.data_ptr(), _stream(sink.device)),

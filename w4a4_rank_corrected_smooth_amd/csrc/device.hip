@@ -1505,22 +1505,34 @@ __global__ __launch_bounds__(256) void gelu_tanh_bf16_kernel(const uint16_t *__r
 // each iteration, so nothing is hoisted or folded) and the workgroup folds
 // its result into one word of `sink`.  Kinds: 0 fp6 32x32x64 (block-scaled,
 // unit scales: K2's group sums), 1 fp4 32x32x64 (the MXFP4 form), 2 bf16
-// 32x32x16, 3 bf16 32x32x8 (K2's scale product), 4 int8 32x32x32.  The host
-// times the launch; two workgroups per CU put two wavefronts on every SIMD.
+// 32x32x16, 3 bf16 32x32x8 (K2's scale product), 4 int8 32x32x32.  Kinds 5-7
+// time instruction mixes, one slot per chain and iteration: 5 an fp6
+// instruction plus 16 fp32 FMAs on other registers, 6 the 16 FMAs alone,
+// 7 the GEMM's step for one 32 x 32 tile (a bf16 32x32x8 scale product, an
+// fp6 group sum for the next step, 16 FMAs of the previous sums times the
+// new product).  Comparing 5 with 0 + 6 shows whether the vector ALU runs
+// beside the matrix core.  The host times the launch; two workgroups per CU
+// put two wavefronts on every SIMD.
 typedef int v4i_m __attribute__((ext_vector_type(4)));
 typedef int v16i_m __attribute__((ext_vector_type(16)));
 template <int KIND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_probe_kernel(int iters,
                                                                                             uint32_t *sink) {
   const int lane = threadIdx.x & 63;
-  v16f acc[4];
+  constexpr bool MIX = KIND >= 5;
+  v16f acc[4], vacc[4];
   v16i_m iacc[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) { acc[c] = v16f{}; iacc[c] = v16i_m{}; }
-  v8i f8;
+  for (int c = 0; c < 4; ++c) {
+    acc[c] = v16f{}; iacc[c] = v16i_m{};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) vacc[c][e] = MIX ? 0.001f * (float)(e + lane + c) : 0.0f;
+  }
+  v8i f8, g8[4];
   v8bf b16;
-  v4s b8;
+  v4s b8, h8[4];
   v4i_m i8;
+  float kf = 1.0f + 1e-7f * (float)lane;
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     f8[r] = (lane * 7 + r) & 0x0F0F0F0F;                 // small fp6 / fp4 codes
@@ -1531,27 +1543,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     b8[r] = (short)(0x3c00 + r + lane);
     i8[r] = (lane + r) & 0x07070707;
   }
+  // distinct operands per chain for the step mix, so no product is shared
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) g8[c][r] = (lane * 5 + r + 3 * c) & 0x0F0F0F0F;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) h8[c][r] = (short)(0x3c00 + r + lane + 5 * c);
+  }
   for (int it = 0; it < iters; ++it) {
-    if constexpr (KIND <= 1) asm volatile("" : "+v"(f8));
+    if constexpr (KIND <= 1 || KIND == 5) asm volatile("" : "+v"(f8));
     if constexpr (KIND == 2) asm volatile("" : "+v"(b16));
     if constexpr (KIND == 3) asm volatile("" : "+v"(b8));
     if constexpr (KIND == 4) asm volatile("" : "+v"(i8));
+    if constexpr (MIX) asm volatile("" : "+v"(kf));
+    if constexpr (KIND == 7) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(g8[c]), "+v"(h8[c]));
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      if constexpr (KIND == 0)
+      if constexpr (KIND == 0 || KIND == 5)
         acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f8, f8, acc[c], 2, 2, 0, 127, 0, 127);
       if constexpr (KIND == 1)
         acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f8, f8, acc[c], 4, 4, 0, 127, 0, 127);
       if constexpr (KIND == 2) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b16, b16, acc[c], 0, 0, 0);
       if constexpr (KIND == 3) acc[c] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(b8, b8, acc[c], 0, 0, 0);
       if constexpr (KIND == 4) iacc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(i8, i8, iacc[c], 0, 0, 0);
+      if constexpr (KIND == 5 || KIND == 6) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) vacc[c][e] = __builtin_fmaf(vacc[c][e], kf, vacc[c][e]);
+      }
+      if constexpr (KIND == 7) {
+        // acc holds the previous step's sums; vacc accumulates sums x product
+        const v16f Sx = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(b8, h8[c], v16f{}, 0, 0, 0);
+        const v16f Pn = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f8, g8[c], v16f{}, 2, 2, 0, 127, 0, 127);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) vacc[c][e] = __builtin_fmaf(acc[c][e], Sx[e], vacc[c][e]);
+        acc[c] = Pn;
+      }
     }
   }
   uint32_t v = 0;
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) v += __float_as_uint(acc[c][e]) + (uint32_t)iacc[c][e];
+    for (int e = 0; e < 16; ++e)
+      v += __float_as_uint(acc[c][e]) + (uint32_t)iacc[c][e] + __float_as_uint(vacc[c][e]);
   __shared__ uint32_t fold[256];
   fold[threadIdx.x] = v;
   __syncthreads();
@@ -2393,7 +2431,7 @@ svdq_status_t svdq_measure_stream(const void *src, void *dst, size_t bytes, int 
 
 svdq_status_t svdq_measure_mfma(int kind, int iters, int grid, uint32_t *sink, void *hip_stream) {
   if (!sink) return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_measure_mfma: NULL sink");
-  if (kind < 0 || kind > 4) return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_measure_mfma: kind %d", kind);
+  if (kind < 0 || kind > 7) return fail(SVDQ_ERR_INVALID_ARGUMENT, "svdq_measure_mfma: kind %d", kind);
   if (iters < 1 || iters > (1 << 24) || grid < 1 || grid > (1 << 20))
     return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "svdq_measure_mfma: iters %d grid %d", iters, grid);
   svdq_status_t st = check_device();
@@ -2405,7 +2443,10 @@ svdq_status_t svdq_measure_mfma(int kind, int iters, int grid, uint32_t *sink, v
     case 1: hipLaunchKernelGGL(mfma_probe_kernel<1>, g, b, 0, stream, iters, sink); break;
     case 2: hipLaunchKernelGGL(mfma_probe_kernel<2>, g, b, 0, stream, iters, sink); break;
     case 3: hipLaunchKernelGGL(mfma_probe_kernel<3>, g, b, 0, stream, iters, sink); break;
-    default: hipLaunchKernelGGL(mfma_probe_kernel<4>, g, b, 0, stream, iters, sink); break;
+    case 4: hipLaunchKernelGGL(mfma_probe_kernel<4>, g, b, 0, stream, iters, sink); break;
+    case 5: hipLaunchKernelGGL(mfma_probe_kernel<5>, g, b, 0, stream, iters, sink); break;
+    case 6: hipLaunchKernelGGL(mfma_probe_kernel<6>, g, b, 0, stream, iters, sink); break;
+    default: hipLaunchKernelGGL(mfma_probe_kernel<7>, g, b, 0, stream, iters, sink); break;
   }
   return launch_status("matrix probe launch");
 }
