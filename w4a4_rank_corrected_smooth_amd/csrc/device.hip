@@ -421,7 +421,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 // Per 32 x 32 tile and group:
 //   P  = v_mfma_scale_f32_32x32x64_f8f6f4 on fp6 codes (unit block scales):
 //        the exact int32 group sums, delivered as fp32 (|P| <= 3136)
-//   acc = fma(P, fl32(sA[m] sW[n]), acc)        (two VALU ops per element)
+//   S  = v_mfma_f32_32x32x8_bf16 on the scale operands: sA[m] sW[n] from
+//        the exact bf16 pieces of both scales
+//   acc = fma(P, S, acc)                        (one VALU op per element)
+// On a SIMD the matrix core and the vector ALU barely run at the same time
+// (svdq_measure_mfma's instruction mixes: an fp6 instruction and 16
+// independent FMAs take 89% of their separate times), so a wavefront's
+// group costs about the sum of its 16 matrix and ~140 vector instructions.
 // The accumulators start from the low-rank up-projection D L2 (bf16 MFMA,
 // D split into a bf16 high part and a bf16 remainder), computed while the
 // first stages are copied; the epilogue adds the bias, the optional GELU,
