@@ -814,6 +814,36 @@ def settle(fn, seconds):
             return n
 
 
+def k2_mix_ceiling_us(step_ns, M, N, K, cus=256):
+    """Main-loop floor of one GEMM launch from the measured time of its
+    per-tile step (svdq_measure_mfma kind 7, SIMD time per step with two
+    wavefronts resident): the busiest CU holds ceil(tiles / CUs) workgroup
+    tiles, each putting one wavefront on every SIMD for K / 64 groups of 8
+    steps.  Waits, prologue and epilogue are not in it."""
+    tiles = -(-M // 128) * -(-N // 256)
+    per_cu = -(-tiles // cus)
+    return per_cu * (K // 64) * 8 * step_ns / 1e3
+
+
+def measure_step_ns(S, dev, stream, iters=20000, grid=512):
+    """SIMD time of the GEMM's per-tile step (kind 7), median of 5 launches."""
+    import numpy as np
+    import torch
+    sink = torch.zeros(grid, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        S.measure_mfma(7, iters, grid, sink)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        S.measure_mfma(7, iters, grid, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    return float(np.median(ts)) * 1e9 * 1024 / (grid * 4 * 4 * iters)
+
+
 def back_to_back(fn, stream, n=30, reps=5):
     """Median over `reps` series of the mean duration of `n` launches of
     fn(i) enqueued back to back between two events (us)."""
@@ -1324,6 +1354,9 @@ def main():
     if not args.skip_mx:
         mx = mx_pair(args, S, fc1, W2, b2, ax2, X, R, dev, stream)
 
+    log("the GEMM's per-tile instruction mix, timed alone")
+    step_ns = measure_step_ns(S, dev, stream)
+
     names = ["fc1_quantize", "fc1_gemm_gelu_quantize_fc2", "fc2_gemm", "awq_m1"]
     dur = {n: [] for n in names}
     span = []
@@ -1337,6 +1370,7 @@ def main():
     value = 2 * ops_layer / (ms_per_step * 1e-3) / 1e12
 
     k2_us = 0.5 * (avg["fc1_gemm_gelu_quantize_fc2"] + avg["fc2_gemm"])
+    mix_us = 0.5 * (k2_mix_ceiling_us(step_ns, M, N1, K1) + k2_mix_ceiling_us(step_ns, M, N2, K2))
     achieved = ops_layer / (k2_us * 1e-6) / 1e12
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "k2_traffic.json")
@@ -1373,7 +1407,12 @@ def main():
                      "traffic": traffic, "kernel": "k2_w4a4_gemm",
                      "instruction": "v_mfma_scale_f32_32x32x64_f8f6f4 (fp6 E2M3 operands)",
                      "frac_int8_peak": round(achieved / PEAK_INT8_TOPS, 4), "peak_int8": PEAK_INT8_TOPS,
-                     "ops_per_launch": ops_layer, "avg_launch_us": round(k2_us, 2)},
+                     "ops_per_launch": ops_layer, "avg_launch_us": round(k2_us, 2),
+                     # the main loop's instruction mix alone (matrix and vector
+                     # instructions barely overlap on a SIMD): mean over fc1 and fc2
+                     "mix_step_ns": round(step_ns, 2),
+                     "mix_ceiling_us": round(mix_us, 2),
+                     "frac_of_mix_ceiling": round(mix_us / k2_us, 4)},
         "kernels_us": {n: round(v, 2) for n, v in avg.items()},
         "event_step_us": round(float(np.mean(span)), 2),
         "settle_steps": settle_steps,

@@ -145,3 +145,12 @@ def test_summaries_refuse_mixed_runs(tmp_path):
         bench._find(str(tmp_path / "trace"), "kernel_trace.csv")
     with pytest.raises(FileNotFoundError):
         bench._find(str(tmp_path / "trace"), "kernel_stats.csv")
+
+
+def test_gemm_mix_ceiling():
+    """The busiest CU's share of the GEMM: fc1 (4608 x 12288, K = 3072) has
+    1728 tiles, 7 on the busiest CU, 48 groups each; fc2 (4608 x 3072, K =
+    12288) 432 tiles, 2 on the busiest CU, 192 groups; 8 steps per group."""
+    assert bench.k2_mix_ceiling_us(40.0, 4608, 12288, 3072) == pytest.approx(7 * 48 * 8 * 40.0 / 1e3)
+    assert bench.k2_mix_ceiling_us(40.0, 4608, 3072, 12288) == pytest.approx(2 * 192 * 8 * 40.0 / 1e3)
+    assert bench.k2_mix_ceiling_us(40.0, 1, 256, 64) == pytest.approx(8 * 40.0 / 1e3)   # one tile, one group
