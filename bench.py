@@ -1165,26 +1165,25 @@ def main():
     if args.summarize_configs:
         t, j = args.summarize_configs
         summarize_configs(t, j, os.path.join(ROOT, "profiles", "kernels_all_configs.md"),
-                          f"rocprofv3 --kernel-trace --stats -f csv -d {t} -- python3 bench.py --configs")
+                          "rocprofv3 --kernel-trace --stats -f csv -d <dir> -- python3 bench.py --configs")
         return
     if args.summarize_counters_mem:
         base = "python3 bench.py --no-cpu-baseline --calibration-copy --skip-unfused --skip-mx"
         summarize_counters_mem(args.summarize_counters_mem,
                                os.path.join(ROOT, "profiles", "shader_counters_mem_flux_mlp_pair.md"),
-                               f"rocprofv3 --pmc {' '.join(SQ_COUNTERS_MEM)} -f csv -d "
-                               f"{args.summarize_counters_mem} -- {base}")
+                               f"rocprofv3 --pmc {' '.join(SQ_COUNTERS_MEM)} -f csv -d <dir> -- {base}")
         return
     if args.summarize_counters:
         base = "python3 bench.py --no-cpu-baseline --calibration-copy --skip-unfused --skip-mx"
         summarize_counters(args.summarize_counters, os.path.join(ROOT, "profiles", "shader_counters_flux_mlp_pair.md"),
-                           f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} -f csv -d {args.summarize_counters} -- {base}")
+                           f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} -f csv -d <dir> -- {base}")
         return
     if args.summarize_profile:
         t, fe, wr = args.summarize_profile
         base = "python3 bench.py --no-cpu-baseline --calibration-copy --skip-unfused --skip-mx"
-        cmd = {"trace": f"rocprofv3 --kernel-trace --stats -f csv -d {t} -- {base}",
-               "fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d {fe} -- {base}",
-               "write": f"rocprofv3 --pmc WRITE_SIZE -f csv -d {wr} -- {base}"}
+        cmd = {"trace": f"rocprofv3 --kernel-trace --stats -f csv -d <dir> -- {base}",
+               "fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -- {base}",
+               "write": f"rocprofv3 --pmc WRITE_SIZE -f csv -d <dir> -- {base}"}
         summarize_profiles(t, fe, wr, os.path.join(ROOT, "profiles"), cmd, args.profiled_log)
         return
     if args.cpu_configs:
