@@ -252,6 +252,33 @@ def test_k_split_gemm(S, M, N, K, rank, out, gelu):
     assert np.max(np.abs(Y1 - Y)) / np.max(np.abs(f["Y"])) <= 2 * tol
 
 
+# Narrow tiles: a grid of fewer than 128 tiles of 128 x 256 whose 64 x 128
+# grid holds at least 256 tiles runs the narrow-tile GEMM (no K-split).
+def narrow_of(M, N):
+    wide = -(-M // 128) * -(-N // 256)
+    return wide < 128 and -(-M // 64) * -(-N // 128) >= 256
+
+
+@pytest.mark.parametrize("M,N,K,rank,out,gelu", [(1000, 2000, 640, 16, torch.float32, False),
+                                                 # N not a multiple of 8: the epilogue's scalar tail
+                                                 (777, 4100, 1088, 32, torch.bfloat16, True),
+                                                 (1024, 3072, 3072, 0, torch.float32, False),
+                                                 (1100, 2100, 1024, 100, torch.bfloat16, False)])
+def test_narrow_tile_gemm(S, M, N, K, rank, out, gelu):
+    """The narrow-tile GEMM (64 x 128 workgroup tiles, one row of matrix
+    tiles per wavefront) against the oracle: ragged M and N, rank 0 and
+    ranks of one to four 32-rank chunks, GELU, both output types."""
+    assert narrow_of(M, N)
+    c = synth.linear_case(f"nt{M}x{N}x{K}", 700 + M, M, N, K, rank,
+                          x_outlier_n=max(1, K // 64), x_outlier_scale=40.0)
+    ref, f, layer, X, ws, Y = run_case(S, c, out_dtype=out, gelu=gelu, check_codes=False)
+    Yref = OG.gelu_tanh_bf16(f["Y"]) if gelu else f["Y"]
+    tol = TOL_BF16 if out == torch.bfloat16 else TOL_F32
+    err = np.max(np.abs(Y - Yref)) / np.max(np.abs(f["Y"]))
+    announce(f"narrow tiles max err / max|Y| {err:.3e}")
+    assert err <= (1.13 * TOL_F32 + 2.0 ** -8 if gelu else tol)
+
+
 def test_matrix_probe_runs_and_is_deterministic(S):
     """The matrix-instruction probe behind the achievable-peak figures (not
     part of the layer): every kind runs, and two runs fold to the same words."""

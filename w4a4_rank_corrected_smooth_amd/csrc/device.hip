@@ -513,10 +513,27 @@ __device__ __forceinline__ v8i mx_frag(const uint8_t *blk, int lane) {
   return r;
 }
 
-template <int MODE, int EPI, bool OUT_F32, bool DFIX = false, bool QNEXT = false, bool SPLIT = false>
+template <int MODE, int EPI, bool OUT_F32, bool DFIX = false, bool QNEXT = false, bool SPLIT = false,
+          bool NARROW = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_w4a4_gemm(K2Args p) {
   using namespace k2c;
   static_assert(!SPLIT || (MODE == MODE_FWD && !QNEXT), "K-split: plain INT4 forward only");
+  static_assert(!NARROW || (MODE == MODE_FWD && !QNEXT && !SPLIT), "narrow tiles: plain INT4 forward only");
+  // Tile shape.  The default workgroup tile is 128 x 256 (wavefront tiles of
+  // 2 x 4 matrix tiles); NARROW takes 64 x 128 (1 x 2), four times the
+  // workgroups, for grids that the wide tile leaves mostly idle.
+  constexpr int WTM = NARROW ? 1 : k2c::WTM, WTN = NARROW ? 2 : k2c::WTN;
+  constexpr int WROWS = 32 * WTM, WCOLS = 32 * WTN, BM = 2 * WROWS, BN = 2 * WCOLS;
+  constexpr int A_BYTES = BM / kTile * kBlockBytes, B_BYTES = BN / kTile * kBlockBytes;
+  constexpr int I4_SW_OFF = A_BYTES + B_BYTES;
+  constexpr int I4_SA_OFF = I4_SW_OFF + BN * kScaleOpBytes;
+  constexpr int I4_STAGE = I4_SA_OFF + BM * kScaleOpBytes;
+  constexpr int I4_LOADS_W = I4_STAGE / 1024 / NWAVES;
+  constexpr int I4_AUX_OFF = I4_NBUF * I4_STAGE;
+  constexpr int EPI_WAVE_BYTES = 32 * WCOLS * 4;
+  static_assert(I4_STAGE % (1024 * NWAVES) == 0 && A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0 &&
+                (BN * kScaleOpBytes) % 1024 == 0 && (BM * kScaleOpBytes) % 1024 == 0,
+                "whole 1 KB loads, each from one array, equal per wavefront");
   // ---- tile of this workgroup (XCD-aware, grouped); with a K-split,
   // consecutive workgroups on one XCD take different tiles of one K range
   const int T = p.TM * p.TN;
@@ -637,11 +654,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     static_assert(BM * 16 * 2 * 2 <= SMEM_BYTES - I4_AUX_OFF && BM * 32 * 2 * 2 <= MX_STAGE,
                   "low-rank staging fits");
     const int rloc = 32 * wu + (lane >> 1), k0 = 16 * (lane & 1);
+    const bool drows = !NARROW || 32 * wu < BM;    // the narrow tile has 64 rows: wavefronts 0 and 1
     for (int c2 = split; c2 < p.rp / 32; c2 += SPLIT ? p.ksplit : 1) {
       float d[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) d[e] = 0.f;
-      if constexpr (DFIX) {
+      if (DFIX && drows) {
         // one fixed-point sum: 16 int64 per lane, converted with one rounding
         const int4 *q = reinterpret_cast<const int4 *>(p.dfix + (int64_t)(bm + rloc) * p.rp + 32 * c2 + k0);
 #pragma unroll
@@ -654,7 +672,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
       const float *dp0 = p.dpart + (int64_t)(bm + rloc) * p.rp + 32 * c2 + k0;
-      for (int s0 = 0; s0 < (DFIX ? 0 : p.S); s0 += 4) {
+      for (int s0 = 0; s0 < (DFIX || !drows ? 0 : p.S); s0 += 4) {
         float4 v[4][4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -690,7 +708,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           bw[cc][j] = *reinterpret_cast<const uint4 *>(p.l2t + (int64_t)(wn + 32 * j + ln) * p.rp + 32 * c2 + 16 * cc + 8 * hl);
 #pragma unroll
       for (int pass = 0; pass < (HALF ? 2 : 1); ++pass) {
-        if (!HALF || (lane & 1) == pass) {
+        if (drows && (!HALF || (lane & 1) == pass)) {
           uint4 *hp = reinterpret_cast<uint4 *>(dhi + rloc * RS + (HALF ? 0 : k0));
           uint4 *lp = reinterpret_cast<uint4 *>(dlo + rloc * RS + (HALF ? 0 : k0));
           hp[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]); hp[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
@@ -781,6 +799,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // G" run on a stale but in-bounds buffer and are never used.
     v8i fa[WTM], fb[WTN];
     v4s xa[WTM], xb[WTN];
+    // the narrow tile's schedule reads codes and scale operands separately
+    auto ld_fa = [&](int g, int i) { fa[i] = k2_frag(stage_i4(g) + (WTM * wmi + i) * kBlockBytes, lane); };
+    auto ld_fb = [&](int g, int j) { fb[j] = k2_frag(stage_i4(g) + A_BYTES + (WTN * wni + j) * kBlockBytes, lane); };
+    auto ld_xa = [&](int g, int i) {
+      if constexpr (MODE == MODE_FWD)
+        xa[i] = __builtin_bit_cast(v4s, *reinterpret_cast<const uint2 *>(
+            stage_i4(g) + I4_SA_OFF + (WROWS * wmi + 32 * i + ln) * kScaleOpBytes + 8 * hl));
+    };
+    auto ld_xb = [&](int g, int j) {
+      if constexpr (MODE == MODE_FWD)
+        xb[j] = __builtin_bit_cast(v4s, *reinterpret_cast<const uint2 *>(
+            stage_i4(g) + I4_SW_OFF + (WCOLS * wni + 32 * j + ln) * kScaleOpBytes + 8 * hl));
+    };
     auto ld_a = [&](int g, int i) {
       const uint8_t *st = stage_i4(g);
       fa[i] = k2_frag(st + (WTM * wmi + i) * kBlockBytes, lane);
@@ -834,7 +865,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     v16f P[2];
     if (MODE == MODE_FWD && G > 2) vmcnt_wait<I4_LOADS_W>(); else vmcnt_wait0();
     __syncthreads();
-    ld_a(0, 0); ld_a(0, 1);
+    if constexpr (NARROW) {
+      ld_a(0, 0);
+    } else {
+      ld_a(0, 0); ld_a(0, 1);
+    }
 #pragma unroll
     for (int j = 0; j < WTN; ++j) ld_b(0, j);
     P[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[0], fb[0], v16f{}, 2, 2, 0, 127, 0, 127);
@@ -845,16 +880,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __syncthreads();
         if (g + 3 < G) fetch(g + 3);
       }
-      I4_STEP(0, 0, 0, 1, 0, );
-      I4_STEP(0, 1, 0, 2, 0, );
-      I4_STEP(0, 2, 0, 3, 0, );
-      I4_STEP(0, 3, 1, 0, 4, ld_a(g + 1, 0));              // a0 last read by (0,3)'s sums
-      I4_STEP(1, 0, 1, 1, 4, ld_b(g + 1, 0));              // b0 by (1,0)'s
-      I4_STEP(1, 1, 1, 2, 4, ld_b(g + 1, 1));
-      I4_STEP(1, 2, 1, 3, 4, ld_b(g + 1, 2));
-      // the next group's first sums (after the last group: a stale but
-      // in-bounds buffer, never used)
-      I4_STEP(1, 3, 0, 0, 8, ld_a(g + 1, 1); ld_b(g + 1, 3));
+      if constexpr (NARROW) {
+        // one row tile: a0's codes are read again right after the sums of
+        // (0,1) issue, its scale operand after (0,1)'s scale product
+        I4_STEP(0, 0, 0, 1, 7, ld_fa(g + 1, 0); ld_fb(g + 1, 0); ld_xb(g + 1, 0));
+        I4_STEP(0, 1, 0, 0, 5, ld_xa(g + 1, 0); ld_fb(g + 1, 1); ld_xb(g + 1, 1));
+      } else {
+        I4_STEP(0, 0, 0, 1, 0, );
+        I4_STEP(0, 1, 0, 2, 0, );
+        I4_STEP(0, 2, 0, 3, 0, );
+        I4_STEP(0, 3, 1, 0, 4, ld_a(g + 1, 0));              // a0 last read by (0,3)'s sums
+        I4_STEP(1, 0, 1, 1, 4, ld_b(g + 1, 0));              // b0 by (1,0)'s
+        I4_STEP(1, 1, 1, 2, 4, ld_b(g + 1, 1));
+        I4_STEP(1, 2, 1, 3, 4, ld_b(g + 1, 2));
+        // the next group's first sums (after the last group: a stale but
+        // in-bounds buffer, never used)
+        I4_STEP(1, 3, 0, 0, 8, ld_a(g + 1, 1); ld_b(g + 1, 3));
+      }
     }
 #undef I4_STEP
   }  // INT4 main loop
@@ -1913,6 +1955,22 @@ static svdq_status_t launch_k2(const svdq_weights_t *w, int M, void *Y, svdq_dty
   const bool f32 = y_dtype == SVDQ_FP32;
   const bool gelu = epilogue == SVDQ_EPILOGUE_GELU_TANH;
   constexpr int NONE = SVDQ_EPILOGUE_NONE, GELU = SVDQ_EPILOGUE_GELU_TANH;
+  // Narrow tiles (64 x 128) when the wide grid would leave most CUs idle and
+  // the narrow one fills the chip without splitting K
+  if (!w2 && k2_narrow(M, w->N)) {
+    a.TM = (M + 63) / 64;
+    a.TN = (w->N + 127) / 128;
+    const dim3 ngrid((unsigned)round_up((int64_t)a.TM * a.TN, 8));
+#define K2_NGO(E, F, DF) hipLaunchKernelGGL((k2_w4a4_gemm<MODE_FWD, E, F, DF, false, false, true>), ngrid, block, 0, \
+                                            stream, a)
+    const bool df = din == K2_D_FIXED;
+    if (!gelu && f32) { if (df) K2_NGO(NONE, true, true); else K2_NGO(NONE, true, false); }
+    else if (!gelu) { if (df) K2_NGO(NONE, false, true); else K2_NGO(NONE, false, false); }
+    else if (f32) { if (df) K2_NGO(GELU, true, true); else K2_NGO(GELU, true, false); }
+    else { if (df) K2_NGO(GELU, false, true); else K2_NGO(GELU, false, false); }
+#undef K2_NGO
+    return launch_status("GEMM kernel launch");
+  }
   // K-split when the tile grid leaves the chip idle and the workspace has
   // room for the partials (svdq_workspace_bytes includes it)
   const int ks = (int)k2_ksplit(M, w->N, w->K);

@@ -164,6 +164,17 @@ constexpr int64_t k2_ksplit(int64_t M, int64_t N, int64_t K) {
   if (s > K / kGroup / 8) s = K / kGroup / 8;
   return s >= 2 ? s : 1;
 }
+// Narrow tiles (64 x 128 instead of 128 x 256) for grids of fewer than 128
+// wide tiles whose narrow grid holds at least 256 tiles: no K-split, no
+// partials.
+#ifndef K2_NARROW
+#define K2_NARROW 1
+#endif
+constexpr bool k2_narrow(int64_t M, int64_t N) {
+  const int64_t wide = ((M + kK2TileM - 1) / kK2TileM) * ((N + kK2TileN - 1) / kK2TileN);
+  const int64_t narrow = ((M + 63) / 64) * ((N + 127) / 128);
+  return K2_NARROW && wide < 128 && narrow >= 256;
+}
 // bytes of the K-split partials after the quantiser's part of the workspace
 constexpr int64_t k2_split_bytes(int64_t M, int64_t N, int64_t K) {
   const int64_t s = k2_ksplit(M, N, K);
