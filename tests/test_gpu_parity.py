@@ -263,7 +263,11 @@ def narrow_of(M, N):
                                                  # N not a multiple of 8: the epilogue's scalar tail
                                                  (777, 4100, 1088, 32, torch.bfloat16, True),
                                                  (1024, 3072, 3072, 0, torch.float32, False),
-                                                 (1100, 2100, 1024, 100, torch.bfloat16, False)])
+                                                 (1100, 2100, 1024, 100, torch.bfloat16, False),
+                                                 # fewer groups than the four stages in flight
+                                                 (1024, 2048, 64, 0, torch.bfloat16, False),
+                                                 (1024, 2048, 128, 8, torch.float32, False),
+                                                 (1024, 3072, 192, 16, torch.float32, True)])
 def test_narrow_tile_gemm(S, M, N, K, rank, out, gelu):
     """The narrow-tile GEMM (64 x 128 workgroup tiles, one row of matrix
     tiles per wavefront) against the oracle: ragged M and N, rank 0 and

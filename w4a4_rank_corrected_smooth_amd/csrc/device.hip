@@ -529,8 +529,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int I4_SA_OFF = I4_SW_OFF + BN * kScaleOpBytes;
   constexpr int I4_STAGE = I4_SA_OFF + BM * kScaleOpBytes;
   constexpr int I4_LOADS_W = I4_STAGE / 1024 / NWAVES;
-  constexpr int I4_AUX_OFF = I4_NBUF * I4_STAGE;
+  // Stages in flight: three for the wide tile (72 KB); four for the narrow
+  // one, whose stage is half the size (low-res 1024 x 3072 -> 3072 at rank
+  // 128: 29.1 us against 32.5 with three; five or six stages took 33.5 /
+  // 33.8 us)
+  constexpr int NBUF = NARROW ? 4 : I4_NBUF;
+  constexpr int I4_AUX_OFF = NBUF * I4_STAGE;
   constexpr int EPI_WAVE_BYTES = 32 * WCOLS * 4;
+  static_assert(I4_AUX_OFF + BM * 16 * 2 * 2 <= SMEM_BYTES, "stages and low-rank staging fit");
   static_assert(I4_STAGE % (1024 * NWAVES) == 0 && A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0 &&
                 (BN * kScaleOpBytes) % 1024 == 0 && (BM * kScaleOpBytes) % 1024 == 0,
                 "whole 1 KB loads, each from one array, equal per wavefront");
@@ -597,7 +603,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   const uint32_t voff = 16u * lane;
   auto fetch = [&](int g) {
-    const uint32_t buf = smem_lds + (uint32_t)((g % I4_NBUF) * I4_STAGE) + (uint32_t)(wu * 1024);
+    const uint32_t buf = smem_lds + (uint32_t)((g % NBUF) * I4_STAGE) + (uint32_t)(wu * 1024);
 #pragma unroll
     for (int r = 0; r < I4_LOADS_W; ++r)
       lds_dma16_s(sbase[r] + g * sstride[r], voff, buf + (uint32_t)(r * NWAVES * 1024));
@@ -626,9 +632,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   auto stage_of = [&](int g) { return smem + (g % MX_NBUF) * MX_STAGE; };
-  auto stage_i4 = [&](int g) { return smem + (g % I4_NBUF) * I4_STAGE; };
+  auto stage_i4 = [&](int g) { return smem + (g % NBUF) * I4_STAGE; };
 
-  for (int g = 0; g < 3 && g < G; ++g) {
+  for (int g = 0; g < (MODE == MODE_MX ? 3 : NBUF) && g < G; ++g) {
     if constexpr (MODE == MODE_MX) fetch_mx(g); else fetch(g);
   }
   if constexpr (MODE == MODE_FWD || MODE == MODE_MX) {
@@ -795,7 +801,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // holds (4 KB per wavefront and group, no padding slots).  One barrier
     // per group: every wavefront waits for its copies of stage g + 1 and for
     // its own LDS reads of stage g, meets the others, and requests stage
-    // g + 3 into stage g's buffer.  After the last group the reads of "group
+    // g + NBUF into stage g's buffer.  After the last group the reads of "group
     // G" run on a stale but in-bounds buffer and are never used.
     v8i fa[WTM], fb[WTN];
     v4s xa[WTM], xb[WTN];
@@ -863,7 +869,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __builtin_amdgcn_sched_barrier(0);                                                        \
   }
     v16f P[2];
-    if (MODE == MODE_FWD && G > 2) vmcnt_wait<I4_LOADS_W>(); else vmcnt_wait0();
+    // stages 0 and 1 complete; later ones may still be in flight
+    if (MODE == MODE_FWD && G >= NBUF) vmcnt_wait<I4_LOADS_W * (NBUF - 2)>();
+    else if (MODE == MODE_FWD && NBUF > 3) vmcnt_wait_dyn(I4_LOADS_W * max(G - 2, 0));
+    else vmcnt_wait0();
     __syncthreads();
     if constexpr (NARROW) {
       ld_a(0, 0);
@@ -876,9 +885,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int g = 0; g < G; ++g) {
       if (g + 1 < G) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wavefront is done reading stage g
-        if (MODE == MODE_FWD && g + 2 < G) vmcnt_wait<I4_LOADS_W>(); else vmcnt_wait0();
+        // stage g + 1 complete, stages g + 2 .. g + NBUF - 1 may be in flight
+        if (MODE == MODE_FWD && g + NBUF - 1 < G) vmcnt_wait<I4_LOADS_W * (NBUF - 2)>();
+        else if (MODE == MODE_FWD && NBUF > 3) vmcnt_wait_dyn(I4_LOADS_W * max(G - 2 - g, 0));
+        else vmcnt_wait0();
         __syncthreads();
-        if (g + 3 < G) fetch(g + 3);
+        if (g + NBUF < G) fetch(g + NBUF);
       }
       if constexpr (NARROW) {
         // one row tile: a0's codes are read again right after the sums of
