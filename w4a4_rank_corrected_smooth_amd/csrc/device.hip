@@ -31,6 +31,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v6u __attribute__((ext_vector_type(6)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef short v4s __attribute__((ext_vector_type(4)));   // four bf16 bit patterns
@@ -1104,7 +1105,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (m < p.M) {
           uint8_t *dst = reinterpret_cast<uint8_t *>(p.Y) + ((int64_t)m * p.N + n) * ES;
           if (vec_ok && n + VE <= p.N) {
-            *reinterpret_cast<uint4 *>(dst) = v;
+            // streaming store: the output is not read again by this launch
+            // (QKV 4608 x 3072 -> 9216: 172.6 against 175.0 us)
+            __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u *>(dst));
           } else {
             const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -1665,7 +1668,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // optimised away) or copy (mode 1) of `bytes` with a caller-chosen grid:
 // the practical HBM rate at a given size and grid, against which the codec
 // kernels are judged.
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) void stream_probe_kernel(const v4u *__restrict__ src,
                                                            v4u *__restrict__ dst, int64_t n16,
                                                            int mode, uint32_t *__restrict__ sink) {
