@@ -62,7 +62,8 @@ CASES = [("ragged", 130, 256, 320, 200, 8, 5), ("tiles", 256, 512, 576, 384, 16,
          ("one-row", 1, 64, 64, 64, 1, 1), ("rank0-next", 300, 192, 384, 96, 12, 0),
          ("wide-rank", 200, 128, 256, 130, 40, 70),
          ("split-fc2", 200, 256, 1024, 256, 8, 8),        # fc2's GEMM is K-split (2 tiles, 16 groups)
-         ("narrow-fc2", 1024, 256, 512, 2048, 16, 32)]   # fc2's GEMM runs narrow tiles on fixed-point D
+         ("narrow-fc2", 1024, 256, 512, 2048, 16, 32),   # fc2's GEMM runs narrow tiles on fixed-point D
+         ("narrow-fc2-3-groups", 1024, 256, 192, 2048, 16, 8)]   # ... with fewer groups than its stages
 
 
 @pytest.mark.parametrize("name,M,K1,N1,N2,r1,r2", CASES)
