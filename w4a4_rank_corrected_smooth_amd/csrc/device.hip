@@ -857,9 +857,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       LOADS;                                                                                  \
       sums_store(g, i, j, P[(i * WTN + j) & 1]);                                              \
     } else {                                                                                  \
+      if constexpr (MM_PRIO) __builtin_amdgcn_s_setprio(3);                                   \
       const v16f Sx = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(xa[i], xb[j], v16f{}, 0, 0, 0); \
       P[(i2 * WTN + j2) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                \
           fa[i2], fb[j2], v16f{}, 2, 2, 0, 127, 0, 127);                                      \
+      if constexpr (MM_PRIO) __builtin_amdgcn_s_setprio(0);                                   \
       LOADS;                                                                                  \
       _Pragma("unroll") for (int e = 0; e < 16; ++e)                                          \
           acc[i][j][e] = __builtin_fmaf(P[(i * WTN + j) & 1][e], Sx[e], acc[i][j][e]);        \
@@ -870,6 +872,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __builtin_amdgcn_sched_barrier(0);                                                        \
   }
     v16f P[2];
+    // The wavefront raises its issue priority while it issues a step's two
+    // matrix instructions, so of the two wavefronts on a SIMD the one ready
+    // to feed the matrix core goes first.  Measured interleaved: fc2 198.8
+    // against 204.0 us, QKV 165.5 against 169.5; with a GELU epilogue (fc1,
+    // and fc1 with the next layer's quantiser) it lost 1-2%: there the other
+    // workgroup's epilogue, long vector work, is what the priority delays.
+    constexpr bool MM_PRIO = MODE == MODE_FWD && EPI == SVDQ_EPILOGUE_NONE && !QNEXT;
     // stages 0 and 1 complete; later ones may still be in flight
     if (MODE == MODE_FWD && G >= NBUF) vmcnt_wait<I4_LOADS_W * (NBUF - 2)>();
     else if (MODE == MODE_FWD && NBUF > 3) vmcnt_wait_dyn(I4_LOADS_W * max(G - 2, 0));
