@@ -894,6 +894,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     P[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[0], fb[0], v16f{}, 2, 2, 0, 127, 0, 127);
     for (int g = 0; g < G; ++g) {
       if (g + 1 < G) {
+        // the barrier and the next copies go at raised priority too (fc2
+        // 195.1 against 201.3 us); not where the epilogue is long
+        if constexpr (MM_PRIO) __builtin_amdgcn_s_setprio(2);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wavefront is done reading stage g
         // stage g + 1 complete, stages g + 2 .. g + NBUF - 1 may be in flight
         if (MODE == MODE_FWD && g + NBUF - 1 < G) vmcnt_wait<I4_LOADS_W * (NBUF - 2)>();
@@ -901,6 +904,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         else vmcnt_wait0();
         __syncthreads();
         if (g + NBUF < G) fetch(g + NBUF);
+        if constexpr (MM_PRIO) __builtin_amdgcn_s_setprio(0);
       }
       if constexpr (NARROW) {
         // one row tile: a0's codes are read again right after the sums of
